@@ -1,0 +1,274 @@
+"""Edge-level pins of the oracle's Roe fluxes.
+
+The oracle's one-layer flux uses the 2x2 closed form and its two-layer flux
+uses Faddeev-LeVerrier + Durand-Kerner + adjugate eigenvectors + Gaussian
+elimination.  Here both are checked against a generic library eigen-
+decomposition of the Roe matrix A_ij as the IR-Roe paper defines it
+(Sec. 2.2, with the density ratio r in the lower-layer row), against closed
+forms, and against the jump conditions that a path-conservative scheme must
+satisfy: the flux seen from the two sides of an edge differs exactly by the
+non-conservative products B_ij dW + S_ij dH.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+G = 9.81
+
+
+def _roe_avg(hL, qL, hR, qR):
+    sL, sR = math.sqrt(hL), math.sqrt(hR)
+    return (sL * qL / hL + sR * qR / hR) / (sL + sR), 0.5 * (hL + hR)
+
+
+def _pminus(A):
+    lam, K = np.linalg.eig(A)
+    lam = lam.real
+    K = K.real
+    return K @ np.diag(0.5 * (1.0 - np.sign(lam))) @ np.linalg.inv(K), lam
+
+
+def _flip(state, idx):
+    s = np.array(state, dtype=float)
+    s[list(idx)] *= -1.0
+    return s
+
+
+# --------------------------------------------------------------- one layer
+
+def _random_states1(rng, n):
+    hL = rng.uniform(0.2, 10.0, n)
+    hR = rng.uniform(0.2, 10.0, n)
+    qL = rng.uniform(-3, 3, n) * hL
+    qR = rng.uniform(-3, 3, n) * hR
+    tL = rng.uniform(-2, 2, n) * hL
+    tR = rng.uniform(-2, 2, n) * hR
+    cL = rng.uniform(0, 1, n) * hL
+    cR = rng.uniform(0, 1, n) * hR
+    HL = rng.uniform(-1, 1, n)
+    HR = rng.uniform(-1, 1, n)
+    return [(np.array([hL[i], qL[i], tL[i], cL[i], HL[i]]),
+             np.array([hR[i], qR[i], tR[i], cR[i], HR[i]])) for i in range(n)]
+
+
+def test_roe1_matches_library_eigendecomposition():
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for L, R in _random_states1(rng, 4000):
+        phi, sp = oracle.roe1_edge(L, R, G)
+        u, h = _roe_avg(L[0], L[1], R[0], R[1])
+        A = np.array([[0.0, 1.0], [G * h - u * u, 2.0 * u]])
+        P, lam = _pminus(A)
+        F = lambda s: np.array([s[1], s[1] ** 2 / s[0] + 0.5 * G * s[0] ** 2])
+        X = F(R) - F(L) - np.array([0.0, G * h]) * (R[4] - L[4])
+        ref = F(L) + P @ X
+        scale = np.abs(F(L)).max() + np.abs(X).max()
+        worst = max(worst, np.abs(phi[:2] - ref).max() / scale)
+        assert sp == pytest.approx(np.abs(lam).max(), rel=1e-13)
+        up = L if phi[0] > 0 else R
+        assert phi[2] == pytest.approx(phi[0] * up[2] / up[0], rel=1e-13, abs=1e-300)
+        assert phi[3] == pytest.approx(phi[0] * up[3] / up[0], rel=1e-13, abs=1e-300)
+    assert worst < 1e-12
+
+
+def test_roe1_supersonic_is_upwind():
+    # all waves to the right: the flux is the left physical flux, exactly
+    L = np.array([1.0, 8.0, 0.3, 0.5, 0.2])
+    R = np.array([1.3, 9.0, -0.1, 0.1, -0.4])
+    phi, _ = oracle.roe1_edge(L, R, G)
+    assert phi[0] == L[1]
+    assert phi[1] == L[1] ** 2 / L[0] + 0.5 * G * L[0] ** 2
+    # all waves to the left: flux = F(W_R) - S dH
+    L2 = _flip(R, [1, 2])
+    R2 = _flip(L, [1, 2])
+    phi2, _ = oracle.roe1_edge(L2, R2, G)
+    h = 0.5 * (L2[0] + R2[0])
+    F1R = R2[1] ** 2 / R2[0] + 0.5 * G * R2[0] ** 2
+    assert phi2[0] == pytest.approx(R2[1], rel=1e-14)
+    assert phi2[1] == pytest.approx(F1R - G * h * (R2[4] - L2[4]), rel=1e-14)
+
+
+def test_roe1_consistency():
+    # equal states on a flat bed: the numerical flux is the physical flux
+    s = np.array([2.0, 1.5, -0.7, 0.4, 0.3])
+    phi, sp = oracle.roe1_edge(s, s, G)
+    assert phi[0] == s[1]
+    assert phi[1] == pytest.approx(s[1] ** 2 / s[0] + 0.5 * G * s[0] ** 2, rel=1e-15)
+    assert phi[2] == pytest.approx(s[1] * s[2] / s[0], rel=1e-15)
+    assert sp == pytest.approx(abs(s[1] / s[0]) + math.sqrt(G * s[0]), rel=1e-15)
+
+
+def test_roe1_still_water_is_balanced():
+    # lake at rest: h + z equal, no velocity -> only the hydrostatic flux
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        zL, zR = rng.uniform(-2, 2, 2)
+        L = np.array([5.0 - zL, 0.0, 0.0, 0.0, -zL])
+        R = np.array([5.0 - zR, 0.0, 0.0, 0.0, -zR])
+        phi, _ = oracle.roe1_edge(L, R, G)
+        assert abs(phi[0]) < 1e-13
+        assert phi[1] == pytest.approx(0.5 * G * L[0] ** 2, rel=1e-14)
+
+
+def test_roe1_wall_is_the_mirror_problem():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        h = rng.uniform(0.1, 10)
+        q = rng.uniform(-5, 5) * h
+        L = np.array([h, q, rng.uniform(-1, 1), rng.uniform(0, h), 0.2])
+        wall, spw = oracle.roe1_wall(L, G)
+        mirror, spm = oracle.roe1_edge(L, _flip(L, [1]), G)
+        assert wall[0] == 0.0 and wall[2] == 0.0 and wall[3] == 0.0
+        assert abs(mirror[0]) <= 1e-14 * abs(q) + 1e-300
+        assert wall[1] == pytest.approx(mirror[1], rel=1e-14)
+        assert spw == pytest.approx(spm, rel=1e-15)
+
+
+def test_roe1_path_conservative_jump():
+    # flux leaving i minus flux entering j = S_ij (H_j - H_i) in the normal
+    # momentum row only; mass, transverse momentum and pollutant are
+    # conserved (evaluated independently from both sides of the edge)
+    rng = np.random.default_rng(7)
+    for L, R in _random_states1(rng, 2000):
+        phi_ij, _ = oracle.roe1_edge(L, R, G)
+        phi_ji, _ = oracle.roe1_edge(_flip(R, [1, 2]), _flip(L, [1, 2]), G)
+        into_j = np.array([-phi_ji[0], phi_ji[1], phi_ji[2], -phi_ji[3]])
+        h = 0.5 * (L[0] + R[0])
+        scale = abs(phi_ij).max() + 1.0
+        assert abs(into_j[0] - phi_ij[0]) < 1e-13 * scale
+        assert abs(into_j[2] - phi_ij[2]) < 1e-13 * scale
+        assert abs(into_j[3] - phi_ij[3]) < 1e-13 * scale
+        assert abs((into_j[1] - phi_ij[1]) - G * h * (R[4] - L[4])) < 1e-12 * scale
+
+
+# --------------------------------------------------------------- two layers
+
+def _A2(L, R, r):
+    u1, h1 = _roe_avg(L[0], L[1], R[0], R[1])
+    u2, h2 = _roe_avg(L[3], L[4], R[3], R[4])
+    A = np.array([[0, 1, 0, 0],
+                  [G * h1 - u1 * u1, 2 * u1, G * h1, 0],
+                  [0, 0, 0, 1],
+                  [r * G * h2, 0, G * h2 - u2 * u2, 2 * u2]], dtype=float)
+    return A, h1, h2
+
+
+def _random_states2(rng, n):
+    out = []
+    while len(out) < n:
+        h1 = rng.uniform(0.5, 4.0, 2)
+        h2 = rng.uniform(0.5, 4.0, 2)
+        u1 = rng.uniform(-0.6, 0.6, 2)
+        u2 = u1 + rng.uniform(-0.2, 0.2, 2)
+        t = rng.uniform(-0.5, 0.5, 4)
+        H = rng.uniform(-0.5, 0.5, 2)
+        L = np.array([h1[0], u1[0] * h1[0], t[0], h2[0], u2[0] * h2[0], t[1], H[0]])
+        R = np.array([h1[1], u1[1] * h1[1], t[2], h2[1], u2[1] * h2[1], t[3], H[1]])
+        A, _, _ = _A2(L, R, 0.98)
+        if np.all(np.abs(np.linalg.eigvals(A).imag) == 0.0):
+            out.append((L, R))
+    return out
+
+
+def test_roe2_eigenvalues_match_library():
+    rng = np.random.default_rng(21)
+    for L, R in _random_states2(rng, 1500):
+        _, sp, lam = oracle.roe2_edge(L, R, G, 0.98)
+        A, _, _ = _A2(L, R, 0.98)
+        ref = np.sort(np.linalg.eigvals(A).real)
+        assert np.abs(lam - ref).max() < 1e-10 * np.abs(ref).max()
+        assert sp == pytest.approx(np.abs(ref).max(), rel=1e-10)
+
+
+def test_roe2_eigenvalues_closed_form_equal_velocities():
+    # u1 = u2 = u: lambda = u +- sqrt(x), x the roots of
+    # x^2 - (c1^2 + c2^2) x + (1 - r) c1^2 c2^2 = 0
+    for (h1, h2, u, r) in [(2.5, 2.5, 0.0, 0.98), (1.0, 3.0, 0.4, 0.9), (2.0, 0.7, -0.3, 0.5)]:
+        L = np.array([h1, u * h1, 0.0, h2, u * h2, 0.0, 0.0])
+        _, _, lam = oracle.roe2_edge(L, L, G, r)
+        a, b = G * h1, G * h2
+        disc = math.sqrt((a + b) ** 2 - 4 * (1 - r) * a * b)
+        xs = [(a + b + disc) / 2, (a + b - disc) / 2]
+        ref = sorted([u - math.sqrt(xs[0]), u - math.sqrt(xs[1]),
+                      u + math.sqrt(xs[1]), u + math.sqrt(xs[0])])
+        assert np.allclose(lam, ref, rtol=0, atol=1e-12)
+    # the rest state of the two-layer workload: external and internal speeds
+    L = np.array([2.5, 0.0, 0.0, 2.5, 0.0, 0.0, 0.0])
+    _, sp, lam = oracle.roe2_edge(L, L, G, 0.98)
+    assert sp == pytest.approx(6.98595, abs=5e-6)
+    assert lam[2] == pytest.approx(0.49648, abs=5e-6)
+
+
+def test_roe2_flux_matches_library_eigendecomposition():
+    rng = np.random.default_rng(22)
+    worst = 0.0
+    for L, R in _random_states2(rng, 1500):
+        phi, _, _ = oracle.roe2_edge(L, R, G, 0.98)
+        A, h1, h2 = _A2(L, R, 0.98)
+        P, _ = _pminus(A)
+        F = lambda s: np.array([s[1], s[1] ** 2 / s[0] + 0.5 * G * s[0] ** 2,
+                                s[4], s[4] ** 2 / s[3] + 0.5 * G * s[3] ** 2])
+        dh1, dh2, dH = R[0] - L[0], R[3] - L[3], R[6] - L[6]
+        BdW = np.array([0.0, -G * h1 * dh2, 0.0, -0.98 * G * h2 * dh1])
+        SdH = np.array([0.0, G * h1, 0.0, G * h2]) * dH
+        X = F(R) - F(L) - BdW - SdH
+        ref = F(L) + P @ X
+        got = phi[[0, 1, 3, 4]]
+        scale = np.abs(F(L)).max() + np.abs(X).max()
+        worst = max(worst, np.abs(got - ref).max() / scale)
+        up1 = L if phi[0] > 0 else R
+        up2 = L if phi[3] > 0 else R
+        assert phi[2] == pytest.approx(phi[0] * up1[2] / up1[0], rel=1e-13, abs=1e-300)
+        assert phi[5] == pytest.approx(phi[3] * up2[5] / up2[3], rel=1e-13, abs=1e-300)
+    assert worst < 1e-10
+
+
+def test_roe2_total_momentum_identity():
+    # Seen from both sides, layer masses are conserved and the momentum jumps
+    # are the non-conservative products.  On a flat bed the density-weighted
+    # sum rho1 q1 + rho2 q2 jumps by -r g d(h1 h2): the discrete form of the
+    # two-layer system's total momentum balance, which holds only when r
+    # multiplies the lower layer's coupling term.
+    rng = np.random.default_rng(23)
+    for L, R in _random_states2(rng, 800):
+        for flat in (False, True):
+            if flat:
+                R = R.copy()
+                R[6] = L[6]
+            phi_ij, _, _ = oracle.roe2_edge(L, R, G, 0.98)
+            phi_ji, _, _ = oracle.roe2_edge(_flip(R, [1, 2, 4, 5]), _flip(L, [1, 2, 4, 5]), G, 0.98)
+            into_j = np.array([-phi_ji[0], phi_ji[1], phi_ji[2], -phi_ji[3], phi_ji[4], phi_ji[5]])
+            scale = np.abs(phi_ij).max() + 1.0
+            h1 = 0.5 * (L[0] + R[0]); h2 = 0.5 * (L[3] + R[3])
+            dh1, dh2, dH = R[0] - L[0], R[3] - L[3], R[6] - L[6]
+            assert abs(into_j[0] - phi_ij[0]) < 1e-11 * scale
+            assert abs(into_j[3] - phi_ij[3]) < 1e-11 * scale
+            j1 = into_j[1] - phi_ij[1]
+            j2 = into_j[4] - phi_ij[4]
+            assert abs(j1 - (-G * h1 * dh2 + G * h1 * dH)) < 1e-10 * scale
+            assert abs(j2 - (-0.98 * G * h2 * dh1 + G * h2 * dH)) < 1e-10 * scale
+            if flat:
+                d12 = R[0] * R[3] - L[0] * L[3]
+                assert abs(0.98 * j1 + j2 + 0.98 * G * d12) < 1e-10 * scale
+
+
+def test_roe2_wall_zero_mass_flux():
+    L = np.array([2.0, 0.7, 0.1, 3.0, -0.4, 0.2, 0.0])
+    phi, sp = oracle.roe2_wall(L, G, 0.98)
+    assert phi[0] == 0.0 and phi[2] == 0.0 and phi[3] == 0.0 and phi[5] == 0.0
+    full, sp2, _ = oracle.roe2_edge(L, _flip(L, [1, 4]), G, 0.98)
+    assert abs(full[0]) < 1e-12 and abs(full[3]) < 1e-12
+    assert phi[1] == pytest.approx(full[1], rel=1e-13)
+    assert phi[4] == pytest.approx(full[4], rel=1e-13)
+    assert sp == sp2
+
+
+def test_roe2_nonhyperbolic_is_reported():
+    # a large velocity shear between the layers makes the internal roots complex
+    L = np.array([2.0, 2.0 * 1.5, 0.0, 2.0, -2.0 * 1.5, 0.0, 0.0])
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.roe2_edge(L, L, G, 0.98)
+    assert e.value.code == 4

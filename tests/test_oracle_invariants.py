@@ -1,0 +1,296 @@
+"""Whole-run pins of the oracle: properties the pages and the mathematics fix.
+
+* well-balance for water at rest (IR-Roe paper, Sec. 2.2: the scheme is
+  well-balanced for stationary solutions corresponding to water at rest);
+* conservation of water (and pollutant, and each layer's) mass under walls
+  and periodic sides, and of x-momentum on a flat x-periodic channel;
+* the exact (Stoker) solution of the 1D dam break;
+* invariance under rotations (Eq. (2)) and grid reflections;
+* constant-concentration preservation of the passive pollutant;
+* the CFL time step of Eq. (5) on a state with known wave speeds.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.optimize import brentq
+
+import inputs
+import oracle
+
+G = 9.81
+
+
+def _fsum(a):
+    return math.fsum(np.asarray(a, dtype=float).tolist())
+
+
+def _tri_areas(w):
+    p = w.node_xy[w.tri]
+    return 0.5 * ((p[:, 1, 0] - p[:, 0, 0]) * (p[:, 2, 1] - p[:, 0, 1])
+                  - (p[:, 2, 0] - p[:, 0, 0]) * (p[:, 1, 1] - p[:, 0, 1]))
+
+
+# ---------------------------------------------------------------- well-balance
+
+def test_lake_at_rest_cartesian():
+    w = inputs.config2(n=96, nsteps=1000, hump=False, blob=False)
+    st, dts, _ = oracle.run(w)
+    h, qx, qy = st[0], st[1], st[2]
+    assert np.abs(qx / h).max() <= 1e-12
+    assert np.abs(qy / h).max() <= 1e-12
+    assert np.abs(h + w.z - 5.0).max() <= 1e-12
+
+
+def test_lake_at_rest_triangles():
+    w = inputs.config4(nq=24, nsteps=200, still=True)
+    st, _, _ = oracle.run(w)
+    h, qx, qy = st
+    assert np.abs(qx / h).max() <= 1e-12
+    assert np.abs(qy / h).max() <= 1e-12
+    assert np.abs(h + w.z - 5.0).max() <= 1e-12
+
+
+def test_lake_at_rest_two_layers():
+    w = inputs.config5(nq=20, nsteps=200, step=False)
+    st, _, _ = oracle.run(w)
+    h1, q1x, q1y, h2, q2x, q2y = st
+    for q, h in ((q1x, h1), (q1y, h1), (q2x, h2), (q2y, h2)):
+        assert np.abs(q / h).max() <= 1e-12
+    assert np.abs(h2 + w.z - 2.5).max() <= 1e-12          # interface
+    assert np.abs(h1 + h2 + w.z - 5.0).max() <= 1e-12     # free surface
+
+
+# ---------------------------------------------------------------- conservation
+
+@pytest.mark.parametrize("case", ["c1", "c3", "c4", "c4tracer"])
+def test_mass_conservation_one_layer(case):
+    if case == "c1":
+        w = inputs.config1()
+        area = np.full(w.ncells, w.dx * w.dy)
+    elif case == "c3":
+        w = inputs.config3(nx=64, ny=48, nsteps=100)
+        area = np.full(w.ncells, w.dx * w.dy)
+    else:
+        w = inputs.config4(nq=30, nsteps=60)
+        area = _tri_areas(w)
+        if case == "c4tracer":
+            rng = np.random.default_rng(2)
+            w.ntracers = 1
+            w.state.append(w.state[0] * rng.uniform(0, 1, w.ncells))
+    m0 = [_fsum(w.state[v] * area) for v in (0, 3) if v < len(w.state)]
+    st, _, _ = oracle.run(w)
+    m1 = [_fsum(st[v] * area) for v in (0, 3) if v < len(st)]
+    for a, b in zip(m0, m1):
+        assert abs(b - a) <= 1e-12 * abs(a)
+
+
+def test_mass_conservation_two_layers():
+    w = inputs.config5(nq=20, nsteps=150)
+    area = _tri_areas(w)
+    m0 = [_fsum(w.state[v] * area) for v in (0, 3)]
+    st, _, _ = oracle.run(w)
+    m1 = [_fsum(st[v] * area) for v in (0, 3)]
+    for a, b in zip(m0, m1):
+        assert abs(b - a) <= 1e-12 * abs(a)
+
+
+def test_x_momentum_conserved_in_flat_periodic_channel():
+    # walls at y = 0, Ly exert no x-force, the bed is flat, x is periodic
+    w = inputs.config3(nx=64, ny=32, nsteps=100, flat=True)
+    scale = _fsum(np.abs(w.state[1]))
+    p0 = _fsum(w.state[1])
+    st, _, _ = oracle.run(w)
+    assert abs(_fsum(st[1]) - p0) <= 1e-12 * scale
+
+
+# ---------------------------------------------------------------- Stoker
+
+def _stoker(hL, hR, g):
+    cL = math.sqrt(g * hL)
+
+    def f(hm):  # left rarefaction meets right shock
+        um_raref = 2.0 * (cL - math.sqrt(g * hm))
+        um_shock = (hm - hR) * math.sqrt(0.5 * g * (hm + hR) / (hm * hR))
+        return um_raref - um_shock
+
+    hm = brentq(f, hR, hL, xtol=1e-15, rtol=1e-15)
+    um = 2.0 * (cL - math.sqrt(g * hm))
+    sh = hm * um / (hm - hR)
+    return hm, um, sh, cL
+
+
+def _stoker_h(x, t, x0, hL, hR, g):
+    hm, um, sh, cL = _stoker(hL, hR, g)
+    cm = math.sqrt(g * hm)
+    xi = (x - x0) / t
+    h = np.where(xi < -cL, hL, 0.0)
+    fan = (xi >= -cL) & (xi <= um - cm)
+    h = np.where(fan, (2.0 * cL - xi) ** 2 / (9.0 * g), h)
+    h = np.where((xi > um - cm) & (xi <= sh), hm, h)
+    h = np.where(xi > sh, hR, h)
+    return h
+
+
+def test_stoker_constants():
+    hm, um, sh, cL = _stoker(2.0, 1.0, G)
+    assert hm == pytest.approx(1.45384089, abs=1e-8)
+    assert um == pytest.approx(1.30583375, abs=1e-8)
+    assert sh == pytest.approx(4.18312792, abs=1e-8)
+
+
+def _dam_break_error(nx):
+    L = 64.0
+    w = inputs.config1(nx=nx, ny=4)
+    w.dx = w.dy = L / nx
+    st, dts, _ = oracle.run(w, nsteps=10 * nx)
+    t = np.cumsum(dts)
+    n = int(np.searchsorted(t, 6.0)) + 1           # first step with t >= 6 s
+    st, dts, _ = oracle.run(w, nsteps=n)
+    t = dts.sum()
+    assert 6.0 <= t < 7.0
+    h = st[0].reshape(4, nx)
+    assert (h == h[0]).all()
+    # exact cell averages by fine sampling
+    sub = 64
+    xs = (np.arange(nx * sub) + 0.5) * (L / (nx * sub))
+    exact = _stoker_h(xs, t, L / 2, 2.0, 1.0, G).reshape(nx, sub).mean(axis=1)
+    return np.abs(h[0] - exact).mean(), t
+
+
+def test_dam_break_matches_stoker():
+    errs = [_dam_break_error(64 * 2 ** k)[0] for k in range(3)]
+    # first-order scheme: L1 error well inside 0.03 m at 64 cells and
+    # shrinking under refinement
+    assert errs[0] < 0.03
+    assert errs[1] < 0.8 * errs[0]
+    assert errs[2] < 0.8 * errs[1]
+
+
+# ---------------------------------------------------------------- symmetries
+
+def test_config1_rows_identical_and_no_transverse_flow():
+    w = inputs.config1()
+    st, _, _ = oracle.run(w)
+    for a in st:
+        g2 = a.reshape(64, 64)
+        assert (g2 == g2[0]).all()
+    assert (st[2] == 0.0).all()
+
+
+def test_mirror_in_x():
+    w = inputs.config1(nx=50, ny=6)
+    rng = np.random.default_rng(4)
+    w.state[1] = rng.uniform(-0.3, 0.3, w.ncells) * w.state[0]
+    w.state[2] = rng.uniform(-0.3, 0.3, w.ncells) * w.state[0]
+    w.z = rng.uniform(0, 0.2, w.ncells)
+    m = w.copy()
+
+    def flip(a):
+        return a.reshape(w.ny, w.nx)[:, ::-1].ravel().copy()
+
+    m.z = flip(w.z)
+    m.state = [flip(a) for a in w.state]
+    m.state[1] = -m.state[1]
+    sa, da, _ = oracle.run(w, nsteps=60)
+    sb, db, _ = oracle.run(m, nsteps=60)
+    assert np.abs(da - db).max() <= 1e-15 * da.max()
+    back = [flip(a) for a in sb]
+    back[1] = -back[1]
+    for a, b in zip(sa, back):
+        assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max() + 1e-300
+
+
+def test_transpose_xy():
+    w = inputs.config2(n=40, nsteps=50)
+    rng = np.random.default_rng(8)
+    w.state[1] = rng.uniform(-0.2, 0.2, w.ncells) * w.state[0]
+    t = w.copy()
+
+    def tr(a):
+        return a.reshape(w.ny, w.nx).T.ravel().copy()
+
+    t.z = tr(w.z)
+    t.state = [tr(w.state[0]), tr(w.state[2]), tr(w.state[1]), tr(w.state[3])]
+    sa, da, _ = oracle.run(w)
+    sb, db, _ = oracle.run(t)
+    assert np.abs(da - db).max() <= 1e-13 * da.max()
+    back = [tr(sb[0]), tr(sb[2]), tr(sb[1]), tr(sb[3])]
+    for a, b in zip(sa, back):
+        assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+@pytest.mark.parametrize("layers", [1, 2])
+def test_rotation_invariance_triangles(layers):
+    th = 0.3
+    c, s = math.cos(th), math.sin(th)
+    if layers == 1:
+        w = inputs.config4(nq=16, nsteps=60)
+        nv_pairs = [(1, 2)]
+    else:
+        w = inputs.config5(nq=14, nsteps=60)
+        nv_pairs = [(1, 2), (4, 5)]
+    rng = np.random.default_rng(9)
+    for (a, b) in nv_pairs:
+        hh = w.state[a - 1]
+        w.state[a] = rng.uniform(-0.05, 0.05, w.ncells) * hh
+        w.state[b] = rng.uniform(-0.05, 0.05, w.ncells) * hh
+    rw = w.copy()
+    x, y = w.node_xy[:, 0], w.node_xy[:, 1]
+    rw.node_xy = np.stack([c * x - s * y + 3.0, s * x + c * y - 1.0], axis=1)
+    for (a, b) in nv_pairs:
+        qx, qy = w.state[a], w.state[b]
+        rw.state[a] = c * qx - s * qy
+        rw.state[b] = s * qx + c * qy
+    sa, da, _ = oracle.run(w)
+    sb, db, _ = oracle.run(rw)
+    assert np.abs(da - db).max() <= 1e-12 * da.max()
+    for (a, b) in nv_pairs:
+        qx, qy = sb[a], sb[b]
+        sb[a], sb[b] = c * qx + s * qy, -s * qx + c * qy
+    for v in range(len(sa)):
+        scale = np.abs(sa[v]).max()
+        assert np.abs(sa[v] - sb[v]).max() <= 1e-12 * max(scale, 1.0)
+
+
+# ---------------------------------------------------------------- pollutant
+
+def test_constant_concentration_is_preserved_exactly():
+    w = inputs.config2(n=48, nsteps=120)
+    w.state[3] = w.state[0].copy()          # c = 1 everywhere
+    st, _, _ = oracle.run(w)
+    assert (st[3] == st[0]).all()
+
+
+def test_pollutant_bounded():
+    # a first-order upwind transport keeps c inside the initial range
+    w = inputs.config1()
+    st, _, _ = oracle.run(w)
+    c = st[3] / st[0]
+    assert c.min() >= -1e-14 and c.max() <= 1.0 + 1e-14
+
+
+# ---------------------------------------------------------------- time step
+
+def test_first_time_step_is_eq5():
+    # at rest the fastest wave is sqrt(g h) on every side of a depth-2 cell
+    w = inputs.config1()
+    _, dts, _ = oracle.run(w, nsteps=1)
+    assert dts[0] == pytest.approx(2 * 0.9 * 1.0 / (4 * math.sqrt(G * 2.0)), rel=1e-15)
+
+
+def test_thread_count_does_not_change_results():
+    w = inputs.config4(nq=20, nsteps=30)
+    a, da, _ = oracle.run(w, nthreads=1)
+    b, db, _ = oracle.run(w, nthreads=4)
+    assert (da == db).all()
+    for x, y in zip(a, b):
+        assert (x == y).all()
+
+
+def test_depth_failure_is_reported():
+    w = inputs.config1(nx=8, ny=4)
+    w.state[0][5] = -1.0
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.run(w, nsteps=1)
+    assert e.value.code == 2

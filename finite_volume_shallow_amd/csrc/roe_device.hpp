@@ -1,0 +1,304 @@
+// Device-side Roe edge fluxes in fluctuation form.
+//
+// The IR-Roe flux of [IR] Sec. 2.2 (de la Asuncion et al., "An MPI-CUDA
+// implementation of an improved Roe method for two-layer shallow water
+// systems") is, in the frame of the edge normal eta (pointing from cell a to
+// cell b),
+//     Phi^- = F(W_a) + P^- X,   X = F(W_b) - F(W_a) - B dW - S dH,
+//     P^- = 1/2 K (I - sgn D) K^-1,
+// plus the transverse momentum carried by the mass flux and upwinded by its
+// sign (step 3).  Cell a's update uses |G| T^-1 Phi^-; cell b's (outward
+// normal -eta) uses -|G| T^-1 Phi^+ with Phi^+ = Phi^- + B dW + S dH.
+// Because sum_j |G_ij| eta_ij = 0 on a closed cell, the physical flux of the
+// cell itself drops out of the sum of Eq. (4), so each edge only has to hand
+// its two cells the fluctuations (in the frame of eta)
+//     a:  Phi^- - F(W_a)           =  P^- X
+//     b:  -(Phi^+ - F(W_b))        =  X - P^- X      (Phi^+ = F(W_b) - X + P^- X)
+// plus the matching transverse-momentum and pollutant parts; the update is
+// W_i -= dt/|V_i| sum |G| T^-1 (fluctuation).  This form carries only
+// differences, which keeps the float32 path accurate (no cancellation of
+// the large hydrostatic terms).
+//
+// The pollutant flux is a passive scalar carried by the mass flux and
+// upwinded like the transverse momentum ([MG] Vinas et al., "A multi-GPU
+// shallow-water simulation with transport of contaminants": a transport
+// equation on top of the one-layer model).
+//
+// Reflective walls are the mirror-ghost Riemann problem with the mass,
+// transverse and pollutant fluxes set to exactly zero; the normal-momentum
+// fluctuation of that problem is sqrt(g h) q_n.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace swe {
+
+template <typename T> __device__ __forceinline__ T rcp(T x) { return T(1) / x; }
+
+template <typename T> struct Eps;
+template <> struct Eps<double> { static constexpr double v = 2.220446049250313e-16; };
+template <> struct Eps<float> { static constexpr float v = 1.1920929e-7f; };
+
+// sgn-weights 1/2 (1 - sgn(lambda)) with sgn(0) = 0
+template <typename T> __device__ __forceinline__ T wminus(T lam)
+{
+    return lam < T(0) ? T(1) : (lam > T(0) ? T(0) : T(0.5));
+}
+
+// One-layer interior edge.  Inputs are edge-frame states: depth h, normal
+// discharge qn, transverse discharge qt, pollutant hc, bed z.
+// Output: fluctuations for side a (da*) and side b (db*), in the edge frame,
+// and the largest |eigenvalue| of the Roe matrix (|u| + c).
+template <typename T, bool TRACER> struct Flux1 {
+    T am, an, at, ac;
+    T bm, bn, bt, bc;
+    T speed;
+};
+
+template <typename T, bool TRACER>
+__device__ __forceinline__ Flux1<T, TRACER> roe1_interior(T hL, T qnL, T qtL, T cL, T zL,
+                                                           T hR, T qnR, T qtR, T cR, T zR, T g)
+{
+    Flux1<T, TRACER> o;
+    const T ihL = rcp(hL), ihR = rcp(hR);
+    const T uL = qnL * ihL, uR = qnR * ihR;
+    const T sL = sqrt(hL), sR = sqrt(hR);
+    const T ubar = (sL * uL + sR * uR) * rcp(sL + sR);
+    const T hbar = T(0.5) * (hL + hR);
+    const T c = sqrt(g * hbar);
+    const T lam1 = ubar - c, lam2 = ubar + c;
+    // X = (dqn, d(qn u) + g hbar (dh + dz)); g/2 (hR^2 - hL^2) = g hbar dh.
+    const T X0 = qnR - qnL;
+    const T X1 = (qnR * uR - qnL * uL) + g * hbar * ((hR - hL) + (zR - zL));
+    const T i2c = T(0.5) * rcp(c);
+    const T a1 = (lam2 * X0 - X1) * i2c;
+    const T a2 = (X1 - lam1 * X0) * i2c;
+    const T w1 = wminus(lam1), w2 = wminus(lam2);
+    const T pm0 = w1 * a1 + w2 * a2;
+    const T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    o.am = pm0;
+    o.an = pm1;
+    o.bm = X0 - pm0;
+    o.bn = X1 - pm1;
+    const T phi0 = qnL + pm0; // mass flux through the edge
+    const T utL = qtL * ihL, utR = qtR * ihR;
+    if (phi0 > T(0)) {
+        o.at = pm0 * utL;                    // phi0 utL - qnL utL
+        o.bt = qnR * utR - phi0 * utL;       // -(phi0 utL - qnR utR)
+    } else {
+        o.at = phi0 * utR - qnL * utL;
+        o.bt = (X0 - pm0) * utR;             // -(phi0 - qnR) utR
+    }
+    if (TRACER) {
+        const T ccL = cL * ihL, ccR = cR * ihR;
+        if (phi0 > T(0)) {
+            o.ac = pm0 * ccL;
+            o.bc = qnR * ccR - phi0 * ccL;
+        } else {
+            o.ac = phi0 * ccR - qnL * ccL;
+            o.bc = (X0 - pm0) * ccR;
+        }
+    } else {
+        o.ac = T(0);
+        o.bc = T(0);
+    }
+    o.speed = fabs(ubar) + c;
+    return o;
+}
+
+// One-layer reflective wall seen from side a.
+template <typename T, bool TRACER>
+__device__ __forceinline__ Flux1<T, TRACER> roe1_wall(T h, T qn, T qt, T hc, T g)
+{
+    Flux1<T, TRACER> o;
+    const T c = sqrt(g * h);
+    const T ih = rcp(h);
+    o.am = -qn;
+    o.an = c * qn;
+    o.at = -qn * qt * ih;
+    o.ac = TRACER ? -qn * hc * ih : T(0);
+    o.bm = o.bn = o.bt = o.bc = T(0);
+    o.speed = c;
+    return o;
+}
+
+// ---------------------------------------------------------------------------
+// Two layers.  The 4x4 Roe matrix of [IR] Sec. 2.2 on (h1, q1, h2, q2):
+//   A = [[0, 1, 0, 0], [c1^2 - u1^2, 2 u1, c1^2, 0], [0, 0, 0, 1],
+//        [r c2^2, 0, c2^2 - u2^2, 2 u2]],   c_k^2 = g hbar_k,
+// (r sits in the lower-layer row: -r g h2 d(h1) is the lower layer's
+// coupling term).  Its eigenvalues are the roots of
+//   Q(l) = ((l - u1)^2 - c1^2) ((l - u2)^2 - c2^2) - r c1^2 c2^2,
+// right eigenvectors (1, l, s, l s) with s = ((l - u1)^2 - c1^2) / c1^2 and
+// left eigenvectors ((l - 2 u1) t, t, (l - 2 u2) c1^2, c1^2) with
+// t = (l - u2)^2 - c2^2; the product of a left and its right eigenvector is
+// Q'(l).  So alpha_k = l_k . X / Q'(l_k) needs no matrix inversion.
+//
+// Roots: the two outer roots by Newton from outside bounds (Q is convex and
+// increasing beyond its largest root when all four roots are real, so the
+// iteration decreases monotonically onto it; likewise from the left), the
+// two inner roots from the deflated quadratic, each polished by Newton on
+// the factored form of Q.  A negative discriminant of the deflated
+// quadratic means complex speeds: the state is flagged non-hyperbolic.
+// ---------------------------------------------------------------------------
+
+template <typename T> struct Flux2 {
+    T a[6]; // side a: h1, q1n, q1t, h2, q2n, q2t
+    T b[6]; // side b
+    T speed;
+    bool nonhyp;
+};
+
+template <typename T>
+__device__ __forceinline__ T quartic_q(T mu, T d1, T d2, T c1, T c2, T rc)
+{
+    const T e1 = mu - d1, e2 = mu - d2;
+    return (e1 * e1 - c1) * (e2 * e2 - c2) - rc;
+}
+
+template <typename T>
+__device__ __forceinline__ T quartic_dq(T mu, T d1, T d2, T c1, T c2)
+{
+    const T e1 = mu - d1, e2 = mu - d2;
+    return T(2) * (e1 * (e2 * e2 - c2) + e2 * (e1 * e1 - c1));
+}
+
+template <typename T>
+__device__ __forceinline__ T newton_outer(T mu, T d1, T d2, T c1, T c2, T rc)
+{
+    // monotone from outside; bounded iteration count
+    for (int it = 0; it < 40; ++it) {
+        const T f = quartic_q(mu, d1, d2, c1, c2, rc);
+        const T df = quartic_dq(mu, d1, d2, c1, c2);
+        if (df == T(0)) break;
+        const T step = f / df;
+        mu -= step;
+        if (fabs(step) <= T(4) * Eps<T>::v * fabs(mu) || !(fabs(step) > T(0))) break;
+    }
+    return mu;
+}
+
+template <typename T>
+__device__ __forceinline__ T newton_polish(T mu, T d1, T d2, T c1, T c2, T rc)
+{
+    for (int it = 0; it < 3; ++it) {
+        const T df = quartic_dq(mu, d1, d2, c1, c2);
+        if (df != T(0)) mu -= quartic_q(mu, d1, d2, c1, c2, rc) / df;
+    }
+    return mu;
+}
+
+// L/R: h1, q1n, q1t, h2, q2n, q2t (edge frame), z.
+template <typename T>
+__device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, T zR, T g, T r)
+{
+    Flux2<T> o;
+    o.nonhyp = false;
+    const T h1L = L[0], q1L = L[1], t1L = L[2], h2L = L[3], q2L = L[4], t2L = L[5];
+    const T h1R = R[0], q1R = R[1], t1R = R[2], h2R = R[3], q2R = R[4], t2R = R[5];
+    const T i1L = rcp(h1L), i1R = rcp(h1R), i2L = rcp(h2L), i2R = rcp(h2R);
+    const T v1L = q1L * i1L, v1R = q1R * i1R, v2L = q2L * i2L, v2R = q2R * i2R;
+    const T s1L = sqrt(h1L), s1R = sqrt(h1R), s2L = sqrt(h2L), s2R = sqrt(h2R);
+    const T u1 = (s1L * v1L + s1R * v1R) * rcp(s1L + s1R);
+    const T u2 = (s2L * v2L + s2R * v2R) * rcp(s2L + s2R);
+    const T c1 = g * T(0.5) * (h1L + h1R); // c1^2
+    const T c2 = g * T(0.5) * (h2L + h2R); // c2^2
+    const T rc = r * c1 * c2;
+
+    // X = dF - B dW - S dH with H = -z, written with g/2 d(h^2) = g hbar dh
+    const T dh1 = h1R - h1L, dh2 = h2R - h2L, dz = zR - zL;
+    T X[4];
+    X[0] = q1R - q1L;
+    X[1] = (q1R * v1R - q1L * v1L) + c1 * ((dh1 + dh2) + dz);
+    X[2] = q2R - q2L;
+    X[3] = (q2R * v2R - q2L * v2L) + c2 * ((dh2 + r * dh1) + dz);
+
+    // eigenvalues in the shifted variable mu = lambda - m
+    const T m = T(0.5) * (u1 + u2);
+    const T d1 = u1 - m, d2 = u2 - m;
+    const T bound = sqrt(c1 + c2);
+    const T muhi = newton_outer(fmax(d1, d2) + bound, d1, d2, c1, c2, rc);
+    const T mulo = newton_outer(fmin(d1, d2) - bound, d1, d2, c1, c2, rc);
+    // Q(mu) = mu^4 + a3 mu^3 + a2 mu^2 + a1 mu + a0; divide by (mu-muhi)(mu-mulo)
+    const T p1 = d1 * d1 - c1, p2 = d2 * d2 - c2;
+    const T a3 = T(-2) * (d1 + d2);
+    const T a2 = p1 + p2 + T(4) * d1 * d2;
+    const T sum = muhi + mulo, prod = muhi * mulo;
+    const T b1 = a3 + sum;
+    const T b0 = a2 + sum * b1 - prod;
+    T disc = b1 * b1 - T(4) * b0;
+    if (disc < T(0)) {
+        o.nonhyp = true;
+        disc = T(0);
+    }
+    const T sq = sqrt(disc);
+    T mid1 = T(-0.5) * (b1 + sq), mid2 = T(-0.5) * (b1 - sq);
+    mid1 = newton_polish(mid1, d1, d2, c1, c2, rc);
+    mid2 = newton_polish(mid2, d1, d2, c1, c2, rc);
+
+    T lam[4] = {mulo + m, mid1 + m, mid2 + m, muhi + m};
+    T PX[4] = {T(0), T(0), T(0), T(0)};
+    T smax = T(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const T l = lam[k];
+        const T e1 = l - u1, e2 = l - u2;
+        const T rho = e1 * e1 - c1;     // c1^2 s
+        const T tau = e2 * e2 - c2;
+        const T dq = T(2) * (tau * e1 + rho * e2);
+        const T lx = (l - T(2) * u1) * tau * X[0] + tau * X[1] + (l - T(2) * u2) * c1 * X[2] + c1 * X[3];
+        const T alpha = lx / dq;
+        const T w = wminus(l);
+        const T sgm = rho / c1;
+        PX[0] += w * alpha;
+        PX[1] += w * alpha * l;
+        PX[2] += w * alpha * sgm;
+        PX[3] += w * alpha * l * sgm;
+        smax = fmax(smax, fabs(l));
+    }
+    o.speed = smax;
+    o.a[0] = PX[0];
+    o.a[1] = PX[1];
+    o.a[3] = PX[2];
+    o.a[4] = PX[3];
+    o.b[0] = X[0] - PX[0];
+    o.b[1] = X[1] - PX[1];
+    o.b[3] = X[2] - PX[2];
+    o.b[4] = X[3] - PX[3];
+    // transverse momentum of each layer, upwinded by that layer's mass flux
+    const T phi1 = q1L + PX[0], phi2 = q2L + PX[2];
+    const T w1L = t1L * i1L, w1R = t1R * i1R, w2L = t2L * i2L, w2R = t2R * i2R;
+    if (phi1 > T(0)) {
+        o.a[2] = PX[0] * w1L;
+        o.b[2] = q1R * w1R - phi1 * w1L;
+    } else {
+        o.a[2] = phi1 * w1R - q1L * w1L;
+        o.b[2] = (X[0] - PX[0]) * w1R;
+    }
+    if (phi2 > T(0)) {
+        o.a[5] = PX[2] * w2L;
+        o.b[5] = q2R * w2R - phi2 * w2L;
+    } else {
+        o.a[5] = phi2 * w2R - q2L * w2L;
+        o.b[5] = (X[2] - PX[2]) * w2R;
+    }
+    return o;
+}
+
+// Two-layer reflective wall seen from side a: the mirror ghost through the
+// 4x4 flux, then both mass fluxes (hence the transverse fluxes) set to zero.
+template <typename T>
+__device__ __forceinline__ Flux2<T> roe2_wall(const T *L, T z, T g, T r)
+{
+    const T G[6] = {L[0], -L[1], L[2], L[3], -L[4], L[5]};
+    Flux2<T> o = roe2_interior<T>(L, z, G, z, g, r);
+    o.a[0] = -L[1];
+    o.a[3] = -L[4];
+    o.a[2] = -L[1] * L[2] * rcp(L[0]);
+    o.a[5] = -L[4] * L[5] * rcp(L[3]);
+#pragma unroll
+    for (int v = 0; v < 6; ++v) o.b[v] = T(0);
+    return o;
+}
+
+} // namespace swe

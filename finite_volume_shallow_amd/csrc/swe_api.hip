@@ -1,0 +1,435 @@
+// C ABI of the shallow-water step library (see include/swe.h).
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "swe_internal.hpp"
+
+using namespace swe;
+
+namespace {
+
+thread_local std::string g_create_err; // detail of the last failed create
+
+struct Fail {
+    int code;
+};
+
+#define HIPTRY(call)                                                                         \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess) {                                                              \
+            c->err = std::string(#call) + ": " + hipGetErrorString(e_);                      \
+            throw Fail{SWE_E_HIP};                                                           \
+        }                                                                                    \
+    } while (0)
+
+void *dev_alloc(swe_ctx *c, size_t bytes)
+{
+    void *p = nullptr;
+    if (bytes == 0) bytes = 8;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        c->err = std::string("hipMalloc(") + std::to_string(bytes) + "): " + hipGetErrorString(e);
+        (void)hipGetLastError();
+        throw Fail{e == hipErrorOutOfMemory ? SWE_E_NOMEM : SWE_E_HIP};
+    }
+    c->allocs.push_back(p);
+    return p;
+}
+
+// Upload a host double array as the context's real type.
+void upload_real(swe_ctx *c, void *dst, const double *src, int64_t n)
+{
+    if (c->prec == SWE_F64) {
+        HIPTRY(hipMemcpyAsync(dst, src, n * sizeof(double), hipMemcpyHostToDevice, c->stream));
+        HIPTRY(hipStreamSynchronize(c->stream));
+    } else {
+        std::vector<float> tmp(n);
+        for (int64_t i = 0; i < n; ++i) tmp[i] = (float)src[i];
+        HIPTRY(hipMemcpyAsync(dst, tmp.data(), n * sizeof(float), hipMemcpyHostToDevice, c->stream));
+        HIPTRY(hipStreamSynchronize(c->stream));
+    }
+}
+
+void upload_raw(swe_ctx *c, void *dst, const void *src, size_t bytes)
+{
+    HIPTRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, c->stream));
+    HIPTRY(hipStreamSynchronize(c->stream));
+}
+
+int validate(const swe_mesh_desc *d, std::string &err)
+{
+    if (d->abi_version != SWE_ABI_VERSION) { err = "abi_version mismatch"; return SWE_E_INVAL; }
+    if (d->nlayers != 1 && d->nlayers != 2) { err = "nlayers must be 1 or 2"; return SWE_E_INVAL; }
+    if (d->ntracers != 0 && d->ntracers != 1) { err = "ntracers must be 0 or 1"; return SWE_E_INVAL; }
+    if (d->nlayers == 2 && d->ntracers) { err = "a pollutant is supported with one layer only"; return SWE_E_INVAL; }
+    if (d->precision != SWE_F64 && d->precision != SWE_F32) { err = "bad precision"; return SWE_E_INVAL; }
+    if (d->path < SWE_PATH_AUTO || d->path > SWE_PATH_FUSED) { err = "bad path"; return SWE_E_INVAL; }
+    if (!(d->g > 0.0) || !std::isfinite(d->g)) { err = "g must be > 0"; return SWE_E_INVAL; }
+    if (d->nlayers == 2 && !(d->r > 0.0 && d->r < 1.0)) { err = "r must lie in (0, 1)"; return SWE_E_INVAL; }
+    if (d->mesh_kind == SWE_MESH_CART) {
+        if (d->nlayers != 1) { err = "two layers are supported on triangle meshes only"; return SWE_E_INVAL; }
+        if (d->nx < 2 || d->ny < 2) { err = "nx and ny must be >= 2"; return SWE_E_INVAL; }
+        if (!(d->dx > 0.0) || !(d->dy > 0.0)) { err = "dx and dy must be > 0"; return SWE_E_INVAL; }
+        if ((d->bc_x != SWE_BC_WALL && d->bc_x != SWE_BC_PERIODIC) ||
+            (d->bc_y != SWE_BC_WALL && d->bc_y != SWE_BC_PERIODIC)) { err = "bad boundary condition"; return SWE_E_INVAL; }
+    } else if (d->mesh_kind == SWE_MESH_TRI) {
+        if (!d->node_xy || !d->tri) { err = "node_xy and tri are required"; return SWE_E_INVAL; }
+        if (d->nnodes < 3 || d->ncells < 1) { err = "empty triangle mesh"; return SWE_E_INVAL; }
+        if (d->path == SWE_PATH_FUSED) { err = "no fused path for triangle meshes"; return SWE_E_INVAL; }
+    } else {
+        err = "bad mesh_kind";
+        return SWE_E_INVAL;
+    }
+    return SWE_OK;
+}
+
+template <typename T> void upload_geometry(swe_ctx *c, const HostEdges &h)
+{
+    const int64_t E = c->E, N = c->N;
+    auto put = [&](const std::vector<double> &src) {
+        void *p = dev_alloc(c, E * sizeof(T));
+        std::vector<T> tmp(src.begin(), src.end());
+        upload_raw(c, p, tmp.data(), E * sizeof(T));
+        return p;
+    };
+    c->e_nx = put(h.nx);
+    c->e_ny = put(h.ny);
+    c->e_len = put(h.len);
+    std::vector<T> ar(N), iar(N);
+    for (int64_t i = 0; i < N; ++i) {
+        ar[i] = (T)h.area[i];
+        iar[i] = (T)(1.0 / h.area[i]);
+    }
+    c->c_area = dev_alloc(c, N * sizeof(T));
+    c->c_iarea = dev_alloc(c, N * sizeof(T));
+    upload_raw(c, c->c_area, ar.data(), N * sizeof(T));
+    upload_raw(c, c->c_iarea, iar.data(), N * sizeof(T));
+}
+
+void free_all(swe_ctx *c)
+{
+    for (void *p : c->allocs) (void)hipFree(p);
+    c->allocs.clear();
+    if (c->h_pinned) (void)hipHostFree(c->h_pinned);
+    c->h_pinned = nullptr;
+    if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
+    c->stream = nullptr;
+}
+
+int status_from_flags(unsigned f)
+{
+    if (f & FLAG_NONHYPERBOLIC) return SWE_E_NONHYPERBOLIC;
+    if (f & FLAG_DEPTH) return SWE_E_DEPTH;
+    if (f & FLAG_NONFINITE) return SWE_E_NONFINITE;
+    return SWE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *swe_strerror(int s)
+{
+    switch (s) {
+    case SWE_OK: return "ok";
+    case SWE_E_INVAL: return "invalid argument or mesh";
+    case SWE_E_NOMEM: return "out of memory";
+    case SWE_E_HIP: return "HIP runtime error";
+    case SWE_E_NOSTATE: return "no state set";
+    case SWE_E_DEPTH: return "a layer depth became <= 0";
+    case SWE_E_NONFINITE: return "a state value became non-finite";
+    case SWE_E_NONHYPERBOLIC: return "two-layer Roe matrix with complex eigenvalues";
+    default: return "unknown status";
+    }
+}
+
+const char *swe_last_error(const swe_ctx *c) { return c ? c->err.c_str() : g_create_err.c_str(); }
+int swe_nvars(const swe_ctx *c) { return c ? c->nv : -1; }
+int64_t swe_ncells(const swe_ctx *c) { return c ? c->N : -1; }
+int swe_path(const swe_ctx *c) { return c ? c->path : -1; }
+
+int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
+{
+    if (!out) return SWE_E_INVAL;
+    *out = nullptr;
+    if (!d) return SWE_E_INVAL;
+    swe_ctx *c = new (std::nothrow) swe_ctx();
+    if (!c) return SWE_E_NOMEM;
+    g_create_err.clear();
+    int st = validate(d, c->err);
+    if (st != SWE_OK) {
+        g_create_err = c->err;
+        delete c;
+        return st;
+    }
+    try {
+        c->kind = d->mesh_kind;
+        c->nlayers = d->nlayers;
+        c->ntracers = d->ntracers;
+        c->prec = d->precision;
+        c->g = d->g;
+        c->r = d->nlayers == 2 ? d->r : 0.0;
+        c->nx = d->nx;
+        c->ny = d->ny;
+        c->dx = d->dx;
+        c->dy = d->dy;
+        c->bc_x = d->bc_x;
+        c->bc_y = d->bc_y;
+        c->nv = d->nlayers == 2 ? 6 : 3 + d->ntracers;
+        c->rs = c->prec == SWE_F32 ? 4 : 8;
+        c->path = SWE_PATH_EDGE;
+        if (d->path == SWE_PATH_FUSED) {
+            c->err = "fused path not available in this build";
+            throw Fail{SWE_E_INVAL};
+        }
+        // host-side mesh work first: mesh errors are reported without
+        // touching the GPU
+        HostEdges he;
+        if (d->mesh_kind == SWE_MESH_CART) {
+            c->N = d->nx * d->ny;
+            st = build_cart_edges(d->nx, d->ny, d->dx, d->dy, d->bc_x, d->bc_y, he, c->err);
+        } else {
+            c->N = d->ncells;
+            st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, d->tri, he, c->err);
+        }
+        if (st != SWE_OK) throw Fail{st};
+
+        HIPTRY(hipGetDevice(&c->device));
+        if (d->hip_stream) {
+            c->stream = (hipStream_t)d->hip_stream;
+        } else {
+            HIPTRY(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
+            c->own_stream = true;
+        }
+        c->E = (int64_t)he.a.size();
+
+        c->e_a = (int32_t *)dev_alloc(c, c->E * sizeof(int32_t));
+        c->e_b = (int32_t *)dev_alloc(c, c->E * sizeof(int32_t));
+        upload_raw(c, c->e_a, he.a.data(), c->E * sizeof(int32_t));
+        upload_raw(c, c->e_b, he.b.data(), c->E * sizeof(int32_t));
+        c->c_off = (int32_t *)dev_alloc(c, (c->N + 1) * sizeof(int32_t));
+        c->c_edge = (int32_t *)dev_alloc(c, he.ce.size() * sizeof(int32_t));
+        upload_raw(c, c->c_off, he.off.data(), (c->N + 1) * sizeof(int32_t));
+        upload_raw(c, c->c_edge, he.ce.data(), he.ce.size() * sizeof(int32_t));
+        if (c->prec == SWE_F32) upload_geometry<float>(c, he);
+        else upload_geometry<double>(c, he);
+
+        c->state[0] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);
+        c->state[1] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);
+        c->zbed = dev_alloc(c, (size_t)c->N * c->rs);
+        c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
+
+        double *bk = (double *)dev_alloc(c, 8 * sizeof(double));
+        c->book.slots = bk;
+        c->book.t = bk + 3;
+        c->book.flags = reinterpret_cast<unsigned *>(bk + 4);
+        c->hist_cap = 1024;
+        c->book.hist = (double *)dev_alloc(c, c->hist_cap * sizeof(double));
+        HIPTRY(hipHostMalloc((void **)&c->h_pinned, 8 * sizeof(double), hipHostMallocDefault));
+    } catch (const Fail &f) {
+        g_create_err = c->err;
+        free_all(c);
+        delete c;
+        return f.code;
+    }
+    *out = c;
+    return SWE_OK;
+}
+
+void swe_destroy(swe_ctx *c)
+{
+    if (!c) return;
+    if (c->stream) (void)hipStreamSynchronize(c->stream);
+    free_all(c);
+    delete c;
+}
+
+int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
+{
+    if (!c) return SWE_E_INVAL;
+    if (!z || !cons) {
+        c->err = "NULL argument";
+        return SWE_E_INVAL;
+    }
+    for (int v = 0; v < c->nv; ++v)
+        if (!cons[v]) {
+            c->err = "NULL state array " + std::to_string(v);
+            return SWE_E_INVAL;
+        }
+    try {
+        c->cur = 0;
+        upload_real(c, c->zbed, z, c->N);
+        for (int v = 0; v < c->nv; ++v)
+            upload_real(c, (char *)c->state[0] + (size_t)v * c->N * c->rs, cons[v], c->N);
+    } catch (const Fail &f) {
+        return f.code;
+    }
+    c->has_state = true;
+    c->err.clear();
+    return SWE_OK;
+}
+
+int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
+{
+    if (!c) return SWE_E_INVAL;
+    if (!z || !cons) {
+        c->err = "NULL argument";
+        return SWE_E_INVAL;
+    }
+    for (int v = 0; v < c->nv; ++v)
+        if (!cons[v]) {
+            c->err = "NULL state array " + std::to_string(v);
+            return SWE_E_INVAL;
+        }
+    try {
+        c->cur = 0;
+        const size_t bytes = (size_t)c->N * c->rs;
+        HIPTRY(hipMemcpyAsync(c->zbed, z, bytes, hipMemcpyDeviceToDevice, c->stream));
+        for (int v = 0; v < c->nv; ++v)
+            HIPTRY(hipMemcpyAsync((char *)c->state[0] + v * bytes, cons[v], bytes, hipMemcpyDeviceToDevice,
+                                  c->stream));
+    } catch (const Fail &f) {
+        return f.code;
+    }
+    c->has_state = true;
+    c->err.clear();
+    return SWE_OK;
+}
+
+int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last_dt)
+{
+    if (!c) return SWE_E_INVAL;
+    if (nsteps < 0 || !(cfl > 0.0 && cfl <= 1.0)) {
+        c->err = "nsteps must be >= 0 and cfl in (0, 1]";
+        return SWE_E_INVAL;
+    }
+    if (!c->has_state) {
+        c->err = "swe_step before swe_set_state";
+        return SWE_E_NOSTATE;
+    }
+    if (t_adv) *t_adv = 0.0;
+    if (last_dt) *last_dt = 0.0;
+    c->hist_count = 0;
+    if (nsteps == 0) return SWE_OK;
+    unsigned flags = 0;
+    try {
+        if (nsteps > c->hist_cap) {
+            int64_t cap = c->hist_cap;
+            while (cap < nsteps) cap *= 2;
+            HIPTRY(hipStreamSynchronize(c->stream));
+            void *old = c->book.hist;
+            c->book.hist = (double *)dev_alloc(c, cap * sizeof(double));
+            for (auto &p : c->allocs)
+                if (p == old) {
+                    (void)hipFree(old);
+                    p = c->allocs.back();
+                    c->allocs.pop_back();
+                    break;
+                }
+            c->hist_cap = cap;
+        }
+        HIPTRY(launch_batch_init(c));
+        for (int64_t s = 0; s < nsteps; ++s) HIPTRY(launch_edge_step(c, s, cfl));
+        HIPTRY(hipMemcpyAsync(c->h_pinned, c->book.slots, 8 * sizeof(double), hipMemcpyDeviceToHost, c->stream));
+        HIPTRY(hipMemcpyAsync(c->h_pinned + 5, c->book.hist + (nsteps - 1), sizeof(double),
+                              hipMemcpyDeviceToHost, c->stream));
+        HIPTRY(hipStreamSynchronize(c->stream));
+        std::memcpy(&flags, c->h_pinned + 4, sizeof(unsigned));
+    } catch (const Fail &f) {
+        return f.code;
+    }
+    c->hist_count = nsteps;
+    if (t_adv) *t_adv = c->h_pinned[3];
+    if (last_dt) *last_dt = c->h_pinned[5];
+    const int st = status_from_flags(flags);
+    if (st != SWE_OK) c->err = swe_strerror(st);
+    return st;
+}
+
+int swe_get_state(swe_ctx *c, double *const *out)
+{
+    if (!c) return SWE_E_INVAL;
+    if (!out) {
+        c->err = "NULL argument";
+        return SWE_E_INVAL;
+    }
+    for (int v = 0; v < c->nv; ++v)
+        if (!out[v]) {
+            c->err = "NULL output array " + std::to_string(v);
+            return SWE_E_INVAL;
+        }
+    if (!c->has_state) {
+        c->err = "swe_get_state before swe_set_state";
+        return SWE_E_NOSTATE;
+    }
+    try {
+        const char *base = (const char *)c->state[c->cur];
+        for (int v = 0; v < c->nv; ++v) {
+            if (c->prec == SWE_F64) {
+                HIPTRY(hipMemcpyAsync(out[v], base + (size_t)v * c->N * 8, c->N * 8, hipMemcpyDeviceToHost,
+                                      c->stream));
+                HIPTRY(hipStreamSynchronize(c->stream));
+            } else {
+                std::vector<float> tmp(c->N);
+                HIPTRY(hipMemcpyAsync(tmp.data(), base + (size_t)v * c->N * 4, c->N * 4, hipMemcpyDeviceToHost,
+                                      c->stream));
+                HIPTRY(hipStreamSynchronize(c->stream));
+                for (int64_t i = 0; i < c->N; ++i) out[v][i] = tmp[i];
+            }
+        }
+    } catch (const Fail &f) {
+        return f.code;
+    }
+    return SWE_OK;
+}
+
+int swe_get_state_device(swe_ctx *c, void *const *out)
+{
+    if (!c) return SWE_E_INVAL;
+    if (!out) {
+        c->err = "NULL argument";
+        return SWE_E_INVAL;
+    }
+    for (int v = 0; v < c->nv; ++v)
+        if (!out[v]) {
+            c->err = "NULL output array " + std::to_string(v);
+            return SWE_E_INVAL;
+        }
+    if (!c->has_state) {
+        c->err = "swe_get_state before swe_set_state";
+        return SWE_E_NOSTATE;
+    }
+    try {
+        const size_t bytes = (size_t)c->N * c->rs;
+        for (int v = 0; v < c->nv; ++v)
+            HIPTRY(hipMemcpyAsync(out[v], (const char *)c->state[c->cur] + v * bytes, bytes,
+                                  hipMemcpyDeviceToDevice, c->stream));
+    } catch (const Fail &f) {
+        return f.code;
+    }
+    return SWE_OK;
+}
+
+int swe_get_dt_history(swe_ctx *c, double *out, int64_t cap, int64_t *count)
+{
+    if (!c) return SWE_E_INVAL;
+    if (!count || cap < 0 || (cap > 0 && !out)) {
+        c->err = "bad arguments";
+        return SWE_E_INVAL;
+    }
+    *count = c->hist_count;
+    const int64_t n = cap < c->hist_count ? cap : c->hist_count;
+    if (n == 0) return SWE_OK;
+    try {
+        HIPTRY(hipMemcpyAsync(out, c->book.hist, n * sizeof(double), hipMemcpyDeviceToHost, c->stream));
+        HIPTRY(hipStreamSynchronize(c->stream));
+    } catch (const Fail &f) {
+        return f.code;
+    }
+    return SWE_OK;
+}
+
+} // extern "C"

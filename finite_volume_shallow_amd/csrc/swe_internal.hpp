@@ -1,0 +1,92 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/swe.h"
+
+namespace swe {
+
+// Device error flags, OR-ed by the kernels and read once per batch.
+enum : unsigned { FLAG_DEPTH = 1u, FLAG_NONFINITE = 2u, FLAG_NONHYPERBOLIC = 4u };
+
+// Host-side explicit edge list with geometry ([IR] Sec. 2.2 notation: edge
+// G_ij between cells a = i and b = j, unit normal eta pointing from a to b,
+// length |G_ij|; b = -1 marks a reflective wall, eta then points outward).
+struct HostEdges {
+    std::vector<int32_t> a, b;
+    std::vector<double> nx, ny, len;
+    std::vector<int32_t> off; // cell -> [off[c], off[c+1]) in ce
+    std::vector<int32_t> ce;  // (edge << 1) | side, side 0 = a, 1 = b
+    std::vector<double> area;
+};
+
+int build_cart_edges(int64_t nx, int64_t ny, double dx, double dy, int bcx, int bcy,
+                     HostEdges &out, std::string &err);
+int build_tri_edges(int64_t nnodes, const double *xy, int64_t ncells, const int32_t *tri,
+                    HostEdges &out, std::string &err);
+
+// Pointer bundle of the state arrays (SoA, one array per variable).
+template <typename T> struct StatePtrs {
+    T *v[6];
+};
+
+// Per-batch bookkeeping on the device: three dt slots used round-robin,
+// the accumulated time, error flags and the dt history of the batch.
+struct StepBook {
+    double *slots;   // [3], non-negative doubles compared as uint64 bits
+    double *t;       // [1]
+    unsigned *flags; // [1]
+    double *hist;    // [hist_cap]
+};
+
+} // namespace swe
+
+struct swe_ctx {
+    // configuration
+    int kind = 0, nlayers = 1, ntracers = 0, prec = SWE_F64, path = SWE_PATH_EDGE;
+    double g = 9.81, r = 0.0;
+    int64_t nx = 0, ny = 0;
+    double dx = 0, dy = 0;
+    int bc_x = 0, bc_y = 0;
+    int64_t N = 0;
+    int nv = 3;
+    size_t rs = 8; // bytes per real
+    int device = 0;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    std::string err;
+    bool has_state = false;
+
+    // state: two SoA copies (ping-pong), nv arrays of N reals each
+    void *state[2] = {nullptr, nullptr};
+    int cur = 0;
+    void *zbed = nullptr;
+
+    // generic edge path
+    int64_t E = 0;
+    int32_t *e_a = nullptr, *e_b = nullptr;
+    void *e_nx = nullptr, *e_ny = nullptr, *e_len = nullptr;
+    int32_t *c_off = nullptr, *c_edge = nullptr;
+    void *c_area = nullptr, *c_iarea = nullptr;
+    void *e_out = nullptr; // (2 nv + 1) * E reals
+
+    // step bookkeeping
+    swe::StepBook book{nullptr, nullptr, nullptr, nullptr};
+    int64_t hist_cap = 0, hist_count = 0;
+    double *h_pinned = nullptr; // t, last dt, flags
+
+    std::vector<void *> allocs; // every device allocation, freed on destroy
+};
+
+namespace swe {
+
+// Kernel launchers (kern_*.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_batch_init(swe_ctx *c);
+hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl);
+
+} // namespace swe

@@ -84,16 +84,18 @@ def round_to_f32(w: Workload) -> Workload:
 # ----------------------------------------------------------------------------
 
 def _gauss_sum_grid(xc, yc, amps, sigmas, cx, cy, x_period=None):
-    """Sum of isotropic Gaussians a*exp(-|x-x0|^2/(2 s^2)) on a tensor grid."""
-    out = np.zeros((yc.size, xc.size))
+    """Sum of isotropic Gaussians a*exp(-|x-x0|^2/(2 s^2)) on a tensor grid.
+
+    Each Gaussian separates into a y factor times an x factor, so the sum is
+    the product of a (ny, k) and a (k, nx) matrix."""
     shifts = [0.0] if x_period is None else [-x_period, 0.0, x_period]
-    for a, s, x0, y0 in zip(amps, sigmas, cx, cy):
-        gy = np.exp(-((yc - y0) ** 2) / (2.0 * s * s))
-        gx = np.zeros_like(xc)
-        for sh in shifts:
-            gx = gx + np.exp(-((xc - x0 - sh) ** 2) / (2.0 * s * s))
-        out += a * np.outer(gy, gx)
-    return out
+    amps = np.asarray(amps)[:, None]
+    sig = np.asarray(sigmas)[:, None]
+    gy = np.exp(-((yc[None, :] - np.asarray(cy)[:, None]) ** 2) / (2.0 * sig * sig))
+    gx = np.zeros((len(amps), xc.size))
+    for sh in shifts:
+        gx += np.exp(-((xc[None, :] - np.asarray(cx)[:, None] - sh) ** 2) / (2.0 * sig * sig))
+    return (gy * amps).T @ gx
 
 
 def _gauss_sum_points(px, py, amps, sigmas, cx, cy):
@@ -264,24 +266,23 @@ def config3(nx=4096, ny=4096, nsteps=500, precision="f32", seed=1003,
     z = _gauss_sum_grid(X, Y, amps, sig, cx, cy, x_period=Lx)
     if flat:
         z = np.zeros_like(z)
-    u = np.zeros((ny, nx))
-    v = np.zeros((ny, nx))
-    psi_c = np.zeros((ny, nx))
+    cos_y = np.empty((ny, 8))
+    sin_y = np.empty((ny, 8))
+    ux = np.zeros((8, nx))
+    vx = np.zeros((8, nx))
+    cxr = np.zeros((8, nx))
     for n in range(1, 9):
         ky = n * math.pi / Ly
-        cos_y = np.cos(ky * Y)
-        sin_y = np.sin(ky * Y)
-        ux = np.zeros(nx)
-        vx = np.zeros(nx)
-        cxr = np.zeros(nx)
+        cos_y[:, n - 1] = np.cos(ky * Y)
+        sin_y[:, n - 1] = np.sin(ky * Y)
         for m in range(9):
             kx = 2.0 * math.pi * m / Lx
-            ux += a_u[m, n - 1] * ky * np.cos(kx * X + ph_u[m, n - 1])
-            vx += a_u[m, n - 1] * kx * np.sin(kx * X + ph_u[m, n - 1])
-            cxr += a_c[m, n - 1] * np.cos(kx * X + ph_c[m, n - 1])
-        u += np.outer(cos_y, ux)
-        v += np.outer(sin_y, vx)
-        psi_c += np.outer(sin_y, cxr)
+            ux[n - 1] += a_u[m, n - 1] * ky * np.cos(kx * X + ph_u[m, n - 1])
+            vx[n - 1] += a_u[m, n - 1] * kx * np.sin(kx * X + ph_u[m, n - 1])
+            cxr[n - 1] += a_c[m, n - 1] * np.cos(kx * X + ph_c[m, n - 1])
+    u = cos_y @ ux
+    v = sin_y @ vx
+    psi_c = sin_y @ cxr
     speed = np.sqrt(u * u + v * v).max()
     u /= speed
     v /= speed

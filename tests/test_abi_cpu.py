@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/swe.h declares, and rejects bad descriptions before any device work.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import finite_volume_shallow_amd as swe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "swe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared()
+    assert len(declared) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", swe.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    assert sorted(swe.EXPORTS) == declared
+
+
+def test_struct_layout_matches_header():
+    # offsets follow the C layout of swe_mesh_desc on x86-64
+    d = swe.swe_mesh_desc
+    assert d.g.offset == 24 and d.nx.offset == 40 and d.bc_x.offset == 72
+    assert d.nnodes.offset == 80 and d.node_xy.offset == 96 and d.hip_stream.offset == 112
+    assert ctypes.sizeof(d) == 120
+
+
+def test_strerror_covers_all_codes():
+    for code in range(0, -8, -1):
+        assert swe.swe_strerror(code) != "unknown status"
+    assert swe.swe_strerror(-99) == "unknown status"
+
+
+def _cart(**kw):
+    args = dict(kind="cart", nx=8, ny=8, dx=1.0, dy=1.0)
+    args.update(kw)
+    return swe.mesh_desc(**args)
+
+
+@pytest.mark.parametrize("kw, msg", [
+    (dict(nx=1), "nx and ny"),
+    (dict(dx=0.0), "dx and dy"),
+    (dict(g=-1.0), "g must"),
+    (dict(nlayers=2, r=0.5), "two layers"),
+    (dict(nlayers=3), "nlayers"),
+    (dict(ntracers=2), "ntracers"),
+    (dict(precision="f16"), None),
+])
+def test_create_rejects_bad_cartesian(kw, msg):
+    d, keep = _cart(**kw)
+    if kw.get("precision") == "f16":
+        d.precision = 7
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
+    if msg:
+        assert msg in str(e.value)
+
+
+def test_create_rejects_bad_abi_version():
+    d, keep = _cart()
+    d.abi_version = 99
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
+
+
+def _square_mesh():
+    xy = np.array([[0, 0], [1, 0], [1, 1], [0, 1]], dtype=float)
+    tri = np.array([[0, 1, 2], [0, 2, 3]], dtype=np.int32)
+    return xy, tri
+
+
+@pytest.mark.parametrize("case", ["clockwise", "node-range", "triple-edge", "two-layer-tracer", "bad-r"])
+def test_create_rejects_bad_triangles(case):
+    xy, tri = _square_mesh()
+    kw = {}
+    if case == "clockwise":
+        tri = tri[:, ::-1].copy()
+    elif case == "node-range":
+        tri[1, 2] = 7
+    elif case == "triple-edge":
+        xy = np.vstack([xy, [[2.0, 0.5]], [[0.5, -1.0]]])
+        tri = np.array([[0, 1, 2], [0, 2, 3], [1, 4, 2], [0, 5, 1], [1, 5, 4]], dtype=np.int32)
+        # edge (1, 2) is used by three triangles once a duplicate is added
+        tri = np.vstack([tri, [[2, 1, 4]]]).astype(np.int32)
+    elif case == "two-layer-tracer":
+        kw = dict(nlayers=2, ntracers=1, r=0.9)
+    elif case == "bad-r":
+        kw = dict(nlayers=2, r=1.0)
+    d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, **kw)
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
+
+
+def test_null_handles_are_safe():
+    assert swe.swe_nvars(None) == -1
+    assert swe.swe_ncells(None) == -1
+    assert swe.swe_path(None) == -1
+    swe.swe_destroy(None)
+    assert swe._lib.swe_step(None, 1, 0.5, None, None) == swe.SWE_E_INVAL
+    assert swe._lib.swe_create_mesh(None, None) == swe.SWE_E_INVAL
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    # the package never imports the oracle and never carries a CPU stepper
+    pkg = os.path.join(ROOT, "finite_volume_shallow_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "swe_oracle" not in text, f

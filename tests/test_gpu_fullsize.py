@@ -1,0 +1,73 @@
+"""GPU runs at the workloads' full sizes.
+
+* Parity with the oracle, every cell, at full size: configs 1, 2 (fp64, all
+  1000 steps), 2 and 3 in fp32 (100 steps, the fp32 parity point), 4 (all
+  200 steps) and 5 (the first steps: the two-layer oracle is too slow for
+  all 200 at a million cells).
+* Full step counts on the GPU with properties that hold at any size: all
+  values finite, depths positive, water, pollutant and layer masses
+  conserved.
+"""
+import numpy as np
+import pytest
+
+import inputs
+from helpers import (FP32_TOL, FP64_TOL, field_errors, fsum, gpu_run,
+                     oracle_reference, say, tri_areas)
+
+pytestmark = pytest.mark.gpu
+
+FULL = {
+    "c1-64x64-f64": (lambda: inputs.config1(), "f64", 100),
+    "c2-1024-f64": (lambda: inputs.config2(), "f64", 1000),
+    "c2-1024-f32": (lambda: inputs.config2(), "f32", 100),
+    "c3-4096-f32": (lambda: inputs.config3(), "f32", 100),
+    "c4-2M-tri-f64": (lambda: inputs.config4(), "f64", 200),
+    "c5-1M-two-layer-f64": (lambda: inputs.config5(), "f64", 4),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_fullsize_parity(name):
+    make, prec, nsteps = FULL[name]
+    w = make()
+    say(f"[full parity] {name} cells={w.ncells} steps={nsteps}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, precision=prec)
+    say("    gpu done; oracle running")
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    errs = field_errors(got, ref, w.g)
+    say(f"    field errors {['%.2e' % e for e in errs]}")
+    assert max(errs) <= (FP64_TOL if prec == "f64" else FP32_TOL), errs
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+
+
+LONG = {
+    "c2-1024-f32-1000": (lambda: inputs.config2(), "f32", 1000),
+    "c3-4096-f32-500": (lambda: inputs.config3(), "f32", 500),
+    "c3-4096-f64-500": (lambda: inputs.config3(), "f64", 500),
+    "c5-1M-two-layer-200": (lambda: inputs.config5(), "f64", 200),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG))
+def test_fullsize_full_length_properties(name):
+    make, prec, nsteps = LONG[name]
+    w = make()
+    say(f"[full length] {name} cells={w.ncells} steps={nsteps}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, precision=prec)
+    assert dts.shape == (nsteps,) and (dts > 0).all() and np.isfinite(dts).all()
+    for a in got:
+        assert np.isfinite(a).all()
+    depth_vars = (0, 3) if w.nlayers == 2 else (0,)
+    for v in depth_vars:
+        assert got[v].min() > 0
+    area = tri_areas(w) if w.kind == "tri" else np.full(w.ncells, w.dx * w.dy)
+    init = inputs.round_to_f32(w) if prec == "f32" else w
+    mass_vars = (0, 3) if (w.nlayers == 2 or w.ntracers) else (0,)
+    tol = 1e-12 if prec == "f64" else 2e-5
+    for v in mass_vars:
+        m0 = fsum(init.state[v] * area)
+        m1 = fsum(got[v] * area)
+        say(f"    var {v}: relative mass change {abs(m1 - m0) / m0:.2e}")
+        assert abs(m1 - m0) <= tol * m0

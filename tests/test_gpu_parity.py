@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case runs the same seeded inputs through both and compares every cell
+of every conserved field (max relative error per field, normalised by the
+field's maximum), the dt of every step and the elapsed time.  fp64 runs must
+agree within 1e-10, fp32 runs within 1e-4 after 100 steps.  Sizes are small
+enough for the oracle to finish in seconds while spanning many thread blocks
+and ragged tails.
+"""
+import numpy as np
+import pytest
+
+import inputs
+from helpers import (FP32_TOL, FP64_TOL, field_errors, fsum, gpu_run,
+                     oracle_reference, say, tri_areas)
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"auto": 0, "edge": 1}
+
+CASES = {
+    # name: (workload factory, steps, precision)
+    "c1-dam-break-64x64": (lambda: inputs.config1(), 100, "f64"),
+    "c2-hump-96-f64": (lambda: inputs.config2(n=96), 300, "f64"),
+    "c2-hump-96-f32": (lambda: inputs.config2(n=96), 100, "f32"),
+    "c3-flow-160x96-f32": (lambda: inputs.config3(nx=160, ny=96), 100, "f32"),
+    "c3-flow-160x96-f64": (lambda: inputs.config3(nx=160, ny=96), 150, "f64"),
+    "c3-ragged-67x33-f64": (lambda: inputs.config3(nx=67, ny=33), 80, "f64"),
+    "c1-ragged-131x5": (lambda: inputs.config1(nx=131, ny=5), 60, "f64"),
+    "c4-tri-36": (lambda: inputs.config4(nq=36), 120, "f64"),
+    "c4-tri-ragged-19": (lambda: inputs.config4(nq=19), 25, "f64"),
+    "c5-two-layer-30": (lambda: inputs.config5(nq=30), 200, "f64"),
+    "c5-two-layer-13": (lambda: inputs.config5(nq=13), 100, "f64"),
+}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity(name, path):
+    make, nsteps, prec = CASES[name]
+    w = make()
+    say(f"[parity] {name} path={path} steps={nsteps} prec={prec} cells={w.ncells}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, path=PATHS[path], precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    errs = field_errors(got, ref, w.g)
+    say(f"    field errors {['%.2e' % e for e in errs]}")
+    assert max(errs) <= tol, errs
+    assert dts.shape == rdts.shape
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+    assert abs(t - rdts.sum()) <= dtol * rdts.sum()
+
+
+def test_config1_symmetry_on_gpu():
+    w = inputs.config1()
+    say("[sym] config1 rows identical, qy == 0")
+    got, _, _ = gpu_run(w)
+    assert np.abs(got[2]).max() <= 1e-14
+    for a in got:
+        g2 = a.reshape(64, 64)
+        assert np.abs(g2 - g2[0]).max() <= 1e-14 * max(np.abs(g2).max(), 1.0)
+
+
+def test_conservation_on_gpu():
+    say("[cons] config2 96^2 and config5 30 conservation")
+    w = inputs.config2(n=96)
+    got, _, _ = gpu_run(w, nsteps=500)
+    area = w.dx * w.dy
+    for v in (0, 3):
+        assert abs(fsum(got[v]) - fsum(w.state[v])) * area <= 1e-12 * fsum(w.state[v]) * area
+    w = inputs.config5(nq=30)
+    got, _, _ = gpu_run(w, nsteps=200)
+    ar = tri_areas(w)
+    for v in (0, 3):
+        m0 = fsum(w.state[v] * ar)
+        assert abs(fsum(got[v] * ar) - m0) <= 1e-12 * m0
+
+
+def test_lake_at_rest_on_gpu():
+    say("[rest] lake at rest, Cartesian fp64 and fp32, triangles")
+    w = inputs.config2(n=96, hump=False, blob=False)
+    got, _, _ = gpu_run(w, nsteps=500)
+    assert np.abs(got[1] / got[0]).max() <= 1e-12
+    assert np.abs(got[0] + w.z - 5.0).max() <= 1e-12
+    got, _, _ = gpu_run(w, nsteps=200, precision="f32")
+    z32 = w.z.astype(np.float32).astype(np.float64)
+    assert np.abs(got[1] / got[0]).max() <= 1e-5
+    assert np.abs(got[0] + z32 - 5.0).max() <= 1e-5
+    w = inputs.config4(nq=24, still=True)
+    got, _, _ = gpu_run(w, nsteps=200)
+    assert np.abs(got[1] / got[0]).max() <= 1e-12
+    assert np.abs(got[0] + w.z - 5.0).max() <= 1e-12
+
+
+def test_determinism_and_resume():
+    import finite_volume_shallow_amd as swe
+    w = inputs.config4(nq=30)
+    say("[det] two runs bitwise equal; 2n steps == n + get/set + n")
+    a, da, _ = gpu_run(w, nsteps=40)
+    b, db, _ = gpu_run(w, nsteps=40)
+    assert (da == db).all()
+    for x, y in zip(a, b):
+        assert (x == y).all()
+    desc, keep = swe.desc_from_workload(w)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        swe.swe_set_state(ctx, w.z, w.state)
+        swe.swe_step(ctx, 20, w.cfl)
+        mid = swe.swe_get_state(ctx)
+        swe.swe_set_state(ctx, w.z, mid)
+        swe.swe_step(ctx, 20, w.cfl)
+        c = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    for x, y in zip(a, c):
+        assert (x == y).all()
+
+
+def test_device_state_roundtrip_and_stream():
+    import torch
+    import finite_volume_shallow_amd as swe
+    say("[dev] device set/get on a torch stream")
+    w = inputs.config3(nx=64, ny=40)
+    s = torch.cuda.Stream()
+    desc, keep = swe.desc_from_workload(w, stream=s, precision="f32")
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        dev = [torch.tensor(a, dtype=torch.float32, device="cuda") for a in w.state]
+        z = torch.tensor(w.z, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        swe.swe_set_state_device(ctx, z, dev)
+        swe.swe_step(ctx, 30, w.cfl)
+        outs = [torch.empty_like(d) for d in dev]
+        swe.swe_get_state_device(ctx, outs)
+        s.synchronize()
+        host = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    for o, h in zip(outs, host):
+        assert (o.cpu().double().numpy() == h).all()
+    got, _, _ = gpu_run(w, nsteps=30, precision="f32")
+    for o, g in zip(host, got):
+        assert (o == g).all()
+
+
+def test_error_paths():
+    import finite_volume_shallow_amd as swe
+    say("[err] depth, non-hyperbolic, bad arguments, zero steps")
+    w = inputs.config1(nx=16, ny=8)
+    w.state[0][17] = -0.5
+    with pytest.raises(swe.SweError) as e:
+        gpu_run(w, nsteps=2)
+    assert e.value.status == swe.SWE_E_DEPTH
+
+    w = inputs.config5(nq=6)
+    for v in (1, 4):
+        w.state[v] = (1.5 if v == 1 else -1.5) * w.state[v - 1]
+    with pytest.raises(swe.SweError) as e:
+        gpu_run(w, nsteps=1)
+    assert e.value.status == swe.SWE_E_NONHYPERBOLIC
+
+    w = inputs.config1(nx=8, ny=8)
+    desc, keep = swe.desc_from_workload(w)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        with pytest.raises(swe.SweError) as e:
+            swe.swe_step(ctx, 1, 0.9)
+        assert e.value.status == swe.SWE_E_NOSTATE
+        swe.swe_set_state(ctx, w.z, w.state)
+        for bad in ((-1, 0.9), (1, 0.0), (1, 1.5)):
+            with pytest.raises(swe.SweError) as e:
+                swe.swe_step(ctx, *bad)
+            assert e.value.status == swe.SWE_E_INVAL
+        assert swe.swe_step(ctx, 0, 0.9) == (0.0, 0.0)
+        got = swe.swe_get_state(ctx)
+        for a, b in zip(got, w.state):
+            assert (a == b).all()
+    finally:
+        swe.swe_destroy(ctx)
+
+
+@pytest.mark.parametrize("case", ["2x2-walls", "2x3-periodic", "one-triangle", "two-triangles"])
+def test_degenerate_meshes(case):
+    say(f"[degenerate] {case}")
+    if case == "2x2-walls":
+        w = inputs.config1(nx=2, ny=2)
+        w.state[0] = np.array([2.0, 1.0, 1.5, 1.2])
+    elif case == "2x3-periodic":
+        w = inputs.config3(nx=2, ny=3)
+        w.bc_y = "periodic"
+        w.precision = "f64"
+    else:
+        xy = np.array([[0, 0], [1, 0], [1, 1], [0, 1]], dtype=float)
+        tri = np.array([[0, 1, 2]] if case == "one-triangle" else [[0, 1, 2], [0, 2, 3]], dtype=np.int32)
+        n = tri.shape[0]
+        w = inputs.Workload(name=case, kind="tri", nlayers=1, ntracers=1, precision="f64",
+                            g=9.81, r=0.0, cfl=0.9, nsteps=10, z=np.array([0.0, 0.1][:n]),
+                            state=[np.array([1.0, 1.3][:n]), np.array([0.2, -0.1][:n]),
+                                   np.array([0.1, 0.0][:n]), np.array([0.5, 0.0][:n])],
+                            node_xy=xy, tri=tri)
+    got, dts, _ = gpu_run(w, nsteps=10, precision="f64")
+    ref, rdts = oracle_reference(w, nsteps=10, precision="f64")
+    assert max(field_errors(got, ref)) <= FP64_TOL
+    assert np.abs(dts - rdts).max() <= 1e-12 * rdts.max()

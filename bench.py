@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the shallow-water Roe step on one MI355X.
+
+A "step" is one explicit time step of the whole hot path: Roe edge fluxes
+with the bed term and pollutant transport, per-cell accumulation and CFL
+wave speeds with the global dt minimum, and the conserved-variable update.
+
+Default workload: the 4096 x 4096 structured grid (one layer + pollutant,
+fp32, x periodic / y walls, seeded smooth flow over a 64-Gaussian bed),
+500 steps per timed call.  Inputs are uploaded before the timed region; the
+timed region is one swe_step(K) call bracketed by HIP events recorded on the
+context's stream, after `warmup` untimed steps.
+
+Prints ONE JSON line with the metric, a roofline object for the dominant
+kernel and the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {
+    1: "one-layer SWE + pollutant, 64x64 structured, 1 m cells, flat bed, dam break, walls, fp64",
+    2: "one-layer SWE + pollutant, 1024x1024 structured, 1 m cells, 16-Gaussian bed, Gaussian hump, walls",
+    3: "one-layer SWE + pollutant, 4096x4096 structured, 10 m cells, 64-Gaussian bed, smooth flow, "
+       "periodic x / walls y, fp32",
+    4: "one-layer SWE, 2M-triangle jittered Morton-ordered mesh, circular dam break, walls, fp64",
+    5: "two-layer SWE (IR-Roe 4x4), 1M-triangle jittered mesh, internal dam break, walls, fp64",
+}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def alg_bytes_per_cell(w, prec, E=None):
+    """Algorithmic bytes per cell-update: read W^n and the bed, write W^{n+1};
+    triangle meshes also read per-cell area and the edge list (two int32
+    cell ids, normal x/y and length per edge)."""
+    s = 4 if prec == "f32" else 8
+    nv = w.nvars
+    if w.kind == "cart":
+        return (2 * nv + 1) * s
+    return (2 * nv + 2) * s + (E / w.ncells) * (8 + 3 * s)
+
+
+def kernel_source_hash(path):
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "finite_volume_shallow_amd", "csrc"))):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(ROOT, "finite_volume_shallow_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload_id, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except Exception:
+        return None
+    rec = data.get(f"{kernel}@config{workload_id}")
+    if not rec or rec.get("src_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _pmc_mean(csv_path, kernel_substr, counter):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} in {csv_path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def ingest_pmc(args):
+    """Turn four rocprofv3 --pmc CSVs into HBM bytes per launch of a kernel.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel are scaled by
+    bytes_known / counter of a plain device copy of known size, so that the
+    result is in actual bytes moved; stored in profiles/traffic.json with the
+    hash of the kernel sources the counters were taken on."""
+    kf, kw, cf, cw = args.ingest_pmc
+    kern = args.ingest_kernel
+    copy_bytes = int(args.ingest_copy_gib * (1 << 30))
+    f_k, n_f = _pmc_mean(kf, kern, "FETCH_SIZE")
+    w_k, n_w = _pmc_mean(kw, kern, "WRITE_SIZE")
+    f_c, _ = _pmc_mean(cf, "copyBuffer", "FETCH_SIZE")
+    w_c, _ = _pmc_mean(cw, "copyBuffer", "WRITE_SIZE")
+    f_scale = copy_bytes / (f_c * 1024.0)
+    w_scale = copy_bytes / (w_c * 1024.0)
+    rd = f_k * 1024.0 * f_scale
+    wr = w_k * 1024.0 * w_scale
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    key = f"{args.ingest_name}@config{args.config}"
+    data[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                 "fetch_scale": f_scale, "write_scale": w_scale,
+                 "dispatches": [n_f, n_w], "src_hash": kernel_source_hash(ROOT)}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    json.dump(data, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps({key: data[key]}))
+
+
+def cpu_baseline(w, prec, budget_s):
+    """The oracle as it stands, on this host's cores, on the first steps of
+    the same workload (about budget_s seconds of CPU work)."""
+    import inputs
+    import oracle
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    src = inputs.round_to_f32(w) if prec == "f32" else w
+    t0 = time.perf_counter()
+    oracle.run(src, nsteps=1, nthreads=nthreads)
+    one = time.perf_counter() - t0
+    steps = max(1, min(w.nsteps, int(budget_s / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.run(src, nsteps=steps, nthreads=nthreads)
+    el = time.perf_counter() - t0
+    return {"value": w.ncells * steps / el, "unit": "cell-updates/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"first {steps} step(s) of the same workload ({w.ncells} cells), "
+                      f"fp64 oracle, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
+    ap.add_argument("--precision", choices=["f32", "f64"], default=None)
+    ap.add_argument("--path", choices=["auto", "edge"], default="auto")
+    ap.add_argument("--repeats", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", type=float, default=0.0, metavar="GIB",
+                    help="instead of the benchmark: time a plain device copy of GIB GiB "
+                         "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=4, metavar=("KERN_FETCH", "KERN_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="instead of the benchmark: record HBM bytes per launch from rocprofv3 "
+                         "counter CSVs into profiles/traffic.json")
+    ap.add_argument("--ingest-kernel", default="k_cart_fused")
+    ap.add_argument("--ingest-name", default="k_cart_fused")
+    ap.add_argument("--ingest-copy-gib", type=float, default=1.0)
+    args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding design notes); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import finite_volume_shallow_amd as swe
+    import inputs
+
+    torch.cuda.set_device(0)
+    if args.copy_ref > 0:
+        n = int(args.copy_ref * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        ev0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        ev1.record()
+        ev1.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "ms": ms,
+                          "GBps_read_plus_write": 8 * n / (ms / 1e3) / 1e9}), flush=True)
+        return
+    w = inputs.make_config(args.config)
+    prec = args.precision or w.precision
+    K = args.steps or w.nsteps
+    stream = torch.cuda.Stream()
+    path = {"auto": swe.SWE_PATH_AUTO, "edge": swe.SWE_PATH_EDGE}[args.path]
+    desc, keep = swe.desc_from_workload(w, path=path, stream=stream, precision=prec)
+    ctx = swe.swe_create_mesh(desc)
+    del keep
+    used_path = "fused" if swe.swe_path(ctx) == swe.SWE_PATH_FUSED else "edge"
+
+    swe.swe_set_state(ctx, w.z, w.state)
+    if args.warmup:
+        swe.swe_step(ctx, args.warmup, w.cfl)
+    best = None
+    for _ in range(max(1, args.repeats)):
+        swe.swe_set_state(ctx, w.z, w.state)   # every timed call starts from W^0
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        t_adv, _ = swe.swe_step(ctx, K, w.cfl)
+        ev1.record(stream)
+        ev1.synchronize()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1)
+        if best is None or ms < best:
+            best = ms
+    swe.swe_destroy(ctx)
+
+    N = w.ncells
+    value = N * K / (best / 1e3)
+    ms_step = best / K
+    E = None
+    if w.kind == "tri":
+        # edges of a triangle mesh: (3 N + boundary) / 2, counted from the mesh
+        import numpy as np
+        t = w.tri
+        e = np.sort(np.stack([t, np.roll(t, -1, axis=1)], axis=2).reshape(-1, 2), axis=1)
+        E = int(np.unique(e, axis=0).shape[0])
+    bpc = alg_bytes_per_cell(w, prec, E)
+    kernel = "k_cart_fused" if used_path == "fused" else "k_edge_flux+k_cell_dt+k_cell_update"
+    # one fused launch per step: the average launch duration is the time per
+    # step (the batch also holds one small dt-prologue launch)
+    achieved = bpc * N / (ms_step / 1e3) / 1e9
+    src_hash = kernel_source_hash(ROOT)
+    traffic = measured_traffic(kernel, args.config, src_hash)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": kernel, "alg_bytes_per_cell": bpc, "src_hash": src_hash}
+    out = {
+        "metric": "cell-updates/sec per Roe time step",
+        "value": value,
+        "unit": "cell-updates/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prec,
+        "data": "synthetic",
+        "config": {"workload": f"config {args.config}: {WORKLOADS[args.config]}", "cells": N,
+                   "precision": prec, "path": used_path, "simulated_seconds": t_adv},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, prec, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,624 @@
+// Fused structured-grid path: one kernel launch per time step.
+//
+// [IR] Eq. (4) needs the global dt of the step before any cell can be
+// updated, and dt comes from the wave speeds of the state at the start of
+// the step (Eq. (5)).  Splitting the step at that dependency would cost a
+// second pass over the state.  Instead the launch for step n
+//   1. reads W^n on its tile plus a two-cell halo,
+//   2. computes the Roe fluctuations of every edge it needs ([IR] Sec. 2.2,
+//      one layer plus the upwinded pollutant of [MG]) and updates W^{n+1}
+//      on the tile plus a one-cell ring, using dt^n reduced by the previous
+//      launch,
+//   3. forms the Eq. (5) wave speeds of W^{n+1} on the tile's edges and
+//      folds the tile's minimum of 2 gamma |V| / sum |G| ||D|| into the
+//      partial minima that the next launch reduces to dt^{n+1},
+//   4. writes W^{n+1} of the tile (ping-pong buffers, no in-place hazard).
+// The halo work (a one-cell ring of fluxes, a two-cell ring of loads) is
+// the price of reading and writing the state exactly once per step.
+//
+// Work layout (CDNA 64-wide wavefronts): one wavefront per tile; a tile is
+// 60 columns (lanes 2..61; lanes 0, 1, 62, 63 carry the halo columns) by
+// TY rows.  The wavefront marches up its tile row by row: a row of every
+// field is one coalesced load, the neighbour across an x-edge is the next
+// lane (a DPP wave shift, no LDS), and the neighbour across a y-edge is the
+// previous row, still in registers.  No LDS tile and no barrier are needed.
+// Each edge is evaluated once per pass by the lane on its left (x) or by
+// the row above it (y), and both cells take their part of it, as in the
+// right/bottom-edge ownership of [MG]'s thread-block kernel.
+//
+// Per cell and row the lane prepares 1/h, sqrt(h) and the velocities once
+// (one reciprocal square root in float32), so an edge costs one reciprocal
+// and one reciprocal square root on top of its arithmetic.  Float32 runs use
+// the hardware reciprocal / square-root approximations (about 1 ulp); the
+// float64 path keeps IEEE division and square root.
+//
+// dt: each wavefront min-reduces its candidates with shuffles and issues one
+// atomic min (on the IEEE bits of a non-negative double) into one of 64
+// partial slots; the next launch reads the 64 partials and reduces them in
+// one wavefront.  Three slot banks rotate (read / written / cleared).
+//
+// Workgroup order is XCD-aware: workgroups are dealt round-robin to the
+// eight XCDs, so tile t is mapped to a contiguous band of tiles per XCD and
+// the wavefronts sharing halo rows and columns share one L2.
+#include "dt_reduce.hpp"
+#include "roe_device.hpp"
+#include "swe_internal.hpp"
+
+namespace swe {
+
+constexpr int CART_LANES = 64;
+constexpr int CART_COLS = 60; // useful columns per tile
+constexpr int NUM_XCD = 8;
+constexpr int NPART = 64;     // partial dt slots per bank
+
+template <typename T, bool TR> struct CartArgs {
+    const T *__restrict__ h;
+    const T *__restrict__ qx;
+    const T *__restrict__ qy;
+    const T *__restrict__ hc;
+    const T *__restrict__ z;
+    T *__restrict__ oh;
+    T *__restrict__ oqx;
+    T *__restrict__ oqy;
+    T *__restrict__ ohc;
+    int nx, ny, perx, pery;
+    T dx, dy, g, cfl;
+    int ty;        // rows per tile
+    int nstrips;   // tiles across x
+    int ntiles;    // tiles in total
+    int per_xcd;   // tiles per XCD band
+    double *part;  // [3][NPART] partial minima
+    StepBook book;
+    int64_t step;
+};
+
+// ---------------------------------------------------------------- math
+
+template <typename T> struct FM;
+template <> struct FM<float> {
+    static __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+    static __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+    static __device__ __forceinline__ float sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+};
+template <> struct FM<double> {
+    static __device__ __forceinline__ double rcp(double x) { return 1.0 / x; }
+    static __device__ __forceinline__ double rsq(double x) { return 1.0 / ::sqrt(x); }
+    static __device__ __forceinline__ double sqrt(double x) { return ::sqrt(x); }
+};
+
+// ---------------------------------------------------------------- lane moves
+// DPP wave shifts: wave_shl:1 gives lane i the value of lane i+1, wave_shr:1
+// the value of lane i-1; the lane without a source (63, resp. 0) reads 0.
+// Those two lanes are halo lanes whose own results are never used.
+constexpr int DPP_WAVE_SHL1 = 0x130;
+constexpr int DPP_WAVE_SHR1 = 0x138;
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL> __device__ __forceinline__ double dpp(double v)
+{
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true);
+    return __hiloint2double(hi, lo);
+}
+template <typename T> __device__ __forceinline__ T nxt(T v) { return dpp<DPP_WAVE_SHL1>(v); }
+template <typename T> __device__ __forceinline__ T prv(T v) { return dpp<DPP_WAVE_SHR1>(v); }
+
+// ---------------------------------------------------------------- cells
+
+// A cell of W^n with the per-cell quantities its edges share.
+template <typename T> struct PC {
+    T h, s, u, v, cc, qx, qy, c, z;
+};
+
+template <typename T> __device__ __forceinline__ PC<T> prep(T h, T qx, T qy, T c, T z)
+{
+    PC<T> p;
+    p.h = h;
+    p.qx = qx;
+    p.qy = qy;
+    p.c = c;
+    p.z = z;
+    T ih;
+    if constexpr (sizeof(T) == 4) {
+        const T r = FM<T>::rsq(h);
+        p.s = h * r;
+        ih = r * r;
+    } else {
+        p.s = ::sqrt(h);
+        ih = T(1) / h;
+    }
+    p.u = qx * ih;
+    p.v = qy * ih;
+    p.cc = c * ih;
+    return p;
+}
+
+// Fluctuations of one edge for its two cells, in the edge frame:
+// mass, normal momentum, transverse momentum, pollutant.
+template <typename T> struct EF {
+    T am, an, at, ac, bm, bn, bt, bc;
+};
+
+// Interior edge, states given in the edge frame (qn, un normal; ut
+// transverse).  [IR] Sec. 2.2 steps 1-3 with one layer: Roe averages,
+// X = F(W_b) - F(W_a) - S dH, P^- X by the 2x2 eigen-decomposition,
+// the transverse momentum and the pollutant upwinded by the mass flux.
+template <typename T, bool TR>
+__device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, T hR, T sR, T qR, T uR, T tR,
+                                      T cR, T zR, T g)
+{
+    EF<T> o;
+    const T ubar = (sL * uL + sR * uR) * FM<T>::rcp(sL + sR);
+    const T c2 = g * T(0.5) * (hL + hR);
+    const T irc = FM<T>::rsq(c2);
+    const T c = c2 * irc;
+    const T i2c = T(0.5) * irc;
+    const T lam1 = ubar - c, lam2 = ubar + c;
+    const T X0 = qR - qL;
+    const T X1 = (qR * uR - qL * uL) + c2 * ((hR - hL) + (zR - zL));
+    const T a1 = (lam2 * X0 - X1) * i2c;
+    const T a2 = (X1 - lam1 * X0) * i2c;
+    const T w1 = lam1 < T(0) ? T(1) : (lam1 > T(0) ? T(0) : T(0.5));
+    const T w2 = lam2 < T(0) ? T(1) : (lam2 > T(0) ? T(0) : T(0.5));
+    const T pm0 = w1 * a1 + w2 * a2;
+    const T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    o.am = pm0;
+    o.an = pm1;
+    o.bm = X0 - pm0;
+    o.bn = X1 - pm1;
+    const T phi0 = qL + pm0;
+    const bool up = phi0 > T(0);
+    o.at = up ? pm0 * tL : phi0 * tR - qL * tL;
+    o.bt = up ? qR * tR - phi0 * tL : o.bm * tR;
+    if (TR) {
+        o.ac = up ? pm0 * cL : phi0 * cR - qL * cL;
+        o.bc = up ? qR * cR - phi0 * cL : o.bm * cR;
+    } else {
+        o.ac = o.bc = T(0);
+    }
+    return o;
+}
+
+// Reflective wall seen from the cell (edge frame, outward normal): mass,
+// transverse and pollutant fluxes are zero, the normal momentum gets the
+// mirror-problem term sqrt(g h) qn.
+template <typename T>
+__device__ __forceinline__ void wall(T h, T qn, T ut, T cc, T g, T &m, T &n, T &t, T &c)
+{
+    m = -qn;
+    n = FM<T>::sqrt(g * h) * qn;
+    t = -qn * ut;
+    c = -qn * cc;
+}
+
+// Eq. (5) speed |u_Roe| + c of an edge from per-cell s = sqrt(h) and
+// a = qn / sqrt(h):  u_Roe = (a_L + a_R) / (s_L + s_R).
+template <typename T> __device__ __forceinline__ T espeed(T hL, T sL, T aL, T hR, T sR, T aR, T g)
+{
+    return fabs((aL + aR) * FM<T>::rcp(sL + sR)) + FM<T>::sqrt(g * T(0.5) * (hL + hR));
+}
+
+// Element k of an array through a 32-bit byte offset (scalar base + vector
+// offset addressing; grids on this path hold < 2^31 cells, < 2^32 bytes per
+// float32 field, < 2^32 bytes per float64 field below 2^29 cells).
+template <typename T> __device__ __forceinline__ const T &at(const T *base, uint32_t k)
+{
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + (uint32_t)(k * (uint32_t)sizeof(T)));
+}
+template <typename T> __device__ __forceinline__ T &at(T *base, uint32_t k)
+{
+    return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + (uint32_t)(k * (uint32_t)sizeof(T)));
+}
+
+// Load a row of W^n for this lane.  CHECK: the row or the column may lie
+// outside the domain (walls); such cells get benign placeholder values.
+template <bool CHECK, typename T, bool TR>
+__device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int col, bool colok, T &h, T &qx,
+                                         T &qy, T &c, T &z, bool &rowok)
+{
+    rowok = true;
+    if (row < 0 || row >= A.ny) {
+        if (A.pery) row = row < 0 ? row + A.ny : row - A.ny;
+        else rowok = false;
+    }
+    if (!CHECK || (rowok && colok)) {
+        const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
+        h = at(A.h, k);
+        qx = at(A.qx, k);
+        qy = at(A.qy, k);
+        c = TR ? at(A.hc, k) : T(0);
+        z = at(A.z, k);
+    } else {
+        h = T(1);
+        qx = qy = c = z = T(0);
+    }
+}
+
+// Registers a wavefront carries from one row to the next.
+template <typename T> struct Carry {
+    PC<T> prev;                  // W^n of row r-1
+    bool prevrow;                // row r-1 inside the domain (uniform)
+    T ax_m, ax_x, ax_y, ax_c;    // x-edge fluctuation sums of row r-1 (times |G|)
+    T yb_m, yb_x, yb_y, yb_c;    // its bottom y-edge part
+    T np_h, np_s, np_b;          // W^{n+1} of row r-2: h, sqrt(h), qy / sqrt(h)
+    bool nprow;                  // row r-2 inside the domain
+    T sx_prev, sybot_prev;       // Eq. (5) speed sums of row r-2 (x-edges, bottom edge)
+};
+
+// A prefetched row of W^n for this lane.
+template <typename T> struct Ld {
+    T h, qx, qy, c, z;
+    bool rowok;
+};
+
+// Per-tile constants.
+template <typename T> struct TileC {
+    int i, col, j0, rlast, rstore_end;
+    bool colok, xwall_lane, wlane;
+    T f, g, lx, ly, g_half;
+};
+
+// Rows of W^n a wavefront keeps in flight ahead of the row it computes.
+constexpr int PREFETCH = 2;
+
+// One row step of a tile: row r of W^n arrives (cur), row r+PREFETCH is
+// requested into nxt_ld, row r-1 of W^{n+1} is completed and stored, and
+// the Eq. (5) speed sum of row r-2 is closed.  XW / YW: walls in x / y.
+template <typename T, bool TR, bool XW, bool YW>
+__device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
+                                         Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
+                                         bool &bad_depth, bool &bad_val)
+{
+    const PC<T> cur = prep(cur_ld.h, cur_ld.qx, cur_ld.qy, cur_ld.c, cur_ld.z);
+    const bool currow = cur_ld.rowok; // uniform across the wavefront
+    if (r + PREFETCH <= K.rlast)
+        load_row<XW || YW>(A, r + PREFETCH, K.col, K.colok, nxt_ld.h, nxt_ld.qx, nxt_ld.qy, nxt_ld.c, nxt_ld.z,
+                           nxt_ld.rowok);
+    const PC<T> &prev = I.prev;
+    const T g = K.g, lx = K.lx, ly = K.ly;
+
+    // ---- x-edge (lane, lane+1) of row r
+    const T Rh = nxt(cur.h), Rs = nxt(cur.s), Ru = nxt(cur.u), Rv = nxt(cur.v), Rc = nxt(cur.cc),
+            Rz = nxt(cur.z), Rq = nxt(cur.qx);
+    EF<T> ex = flux<T, TR>(cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, Rh, Rs, Rq, Ru, Rv, Rc, Rz, g);
+    if (XW && K.xwall_lane) {
+        if (K.colok) { // wall on the right of this lane's cell
+            wall(cur.h, cur.qx, cur.v, cur.cc, g, ex.am, ex.an, ex.at, ex.ac);
+            ex.bm = ex.bn = ex.bt = ex.bc = T(0);
+        } else { // wall on the left of the next lane's cell: qn = -qx, ut = -v;
+                 // back-rotation (m, n, t, c) -> (m, -n, -t, c)
+            T m, n, t, c;
+            wall(Rh, -Rq, -Rv, Rc, g, m, n, t, c);
+            ex.am = ex.an = ex.at = ex.ac = T(0);
+            ex.bm = m;
+            ex.bn = -n;
+            ex.bt = -t;
+            ex.bc = c;
+        }
+    }
+    O.ax_m = lx * (ex.am + prv(ex.bm));
+    O.ax_x = lx * (ex.an + prv(ex.bn));
+    O.ax_y = lx * (ex.at + prv(ex.bt));
+    O.ax_c = TR ? lx * (ex.ac + prv(ex.bc)) : T(0);
+
+    // ---- y-edge (row r-1, row r): normal (0, 1), qn = qy, ut = -u;
+    // back-rotation (m, n, t, c) -> (m, -t, n, c)
+    EF<T> ey = flux<T, TR>(prev.h, prev.s, prev.qy, prev.v, -prev.u, prev.cc, prev.z, cur.h, cur.s, cur.qy, cur.v,
+                           -cur.u, cur.cc, cur.z, g);
+    if (YW && I.prevrow != currow) {
+        if (I.prevrow) { // wall above row r-1
+            wall(prev.h, prev.qy, -prev.u, prev.cc, g, ey.am, ey.an, ey.at, ey.ac);
+            ey.bm = ey.bn = ey.bt = ey.bc = T(0);
+        } else { // wall below row r: normal (0, -1), qn = -qy, ut = u,
+                 // back-rotation (m, n, t, c) -> (m, t, -n, c), stored so
+                 // that the common map (m, -t, n, c) below yields it
+            T m, n, t, c;
+            wall(cur.h, -cur.qy, cur.u, cur.cc, g, m, n, t, c);
+            ey.am = ey.an = ey.at = ey.ac = T(0);
+            ey.bm = m;
+            ey.bt = -t;
+            ey.bn = -n;
+            ey.bc = c;
+        }
+    }
+
+    O.np_h = I.np_h;
+    O.np_s = I.np_s;
+    O.np_b = I.np_b;
+    O.nprow = I.nprow;
+    O.sx_prev = I.sx_prev;
+    O.sybot_prev = I.sybot_prev;
+    if (r >= K.j0) {
+        // ---- complete row r-1: W^{n+1} = W^n - dt/|V| sum |G| fluct
+        const T am = I.ax_m + I.yb_m + ly * ey.am;
+        const T ax = I.ax_x + I.yb_x + ly * (-ey.at);
+        const T ay = I.ax_y + I.yb_y + ly * ey.an;
+        const T ac = I.ax_c + I.yb_c + ly * ey.ac;
+        const T f = K.f;
+        const T h1 = prev.h - f * am;
+        const T qx1 = prev.qx - f * ax;
+        const T qy1 = prev.qy - f * ay;
+        const T c1 = TR ? prev.c - f * ac : T(0);
+        // ---- Eq. (5) speeds of W^{n+1}
+        T s1, a1, b1;
+        if constexpr (sizeof(T) == 4) {
+            const T rq = FM<T>::rsq(h1);
+            s1 = h1 * rq;
+            a1 = qx1 * rq;
+            b1 = qy1 * rq;
+        } else {
+            s1 = ::sqrt(h1);
+            a1 = qx1 / s1;
+            b1 = qy1 / s1;
+        }
+        const T Nh = nxt(h1), Ns = nxt(s1), Na = nxt(a1);
+        T exs = espeed(h1, s1, a1, Nh, Ns, Na, g);
+        if (XW && K.xwall_lane) exs = FM<T>::sqrt(g * (K.colok ? h1 : Nh));
+        const T sx_cur = lx * (exs + prv(exs));
+        if (r >= K.j0 + 1) {
+            // y-edge (r-2, r-1) of W^{n+1} completes the speed sum of row r-2
+            T eys;
+            if (!YW || (I.nprow && I.prevrow)) eys = espeed(I.np_h, I.np_s, I.np_b, h1, s1, b1, g);
+            else eys = FM<T>::sqrt(g * (I.nprow ? I.np_h : h1));
+            eys *= ly;
+            const int rr = r - 2;
+            if (rr >= K.j0 && rr < K.rstore_end && K.wlane) smax = fmax(smax, I.sx_prev + I.sybot_prev + eys);
+            O.sybot_prev = eys;
+        }
+        // ---- store row r-1 of the tile
+        const int wr = r - 1;
+        if (wr >= K.j0 && wr < K.rstore_end && K.wlane) {
+            const uint32_t k = (uint32_t)wr * (uint32_t)A.nx + (uint32_t)K.i;
+            at(A.oh, k) = h1;
+            at(A.oqx, k) = qx1;
+            at(A.oqy, k) = qy1;
+            if (TR) at(A.ohc, k) = c1;
+            bad_depth |= !(h1 > T(0));
+            bad_val |= !isfinite(h1 + qx1 + qy1 + c1);
+        }
+        O.np_h = h1;
+        O.np_s = s1;
+        O.np_b = b1;
+        O.nprow = I.prevrow;
+        O.sx_prev = sx_cur;
+    }
+    // bottom part of the y-edge for row r: (m, n, t, c) -> (m, -t, n, c)
+    O.yb_m = ly * ey.bm;
+    O.yb_x = ly * (-ey.bt);
+    O.yb_y = ly * ey.bn;
+    O.yb_c = ly * ey.bc;
+    O.prev = cur;
+    O.prevrow = currow;
+}
+
+// One wavefront's tile.  XW: the tile has a wall among its x-edges; YW: the
+// tile's rows reach a wall in y.  Tiles with neither (almost all of them)
+// run without any wall code.  Returns the tile's largest Eq. (5) speed sum
+// sum |G| ||D|| (the smallest dt candidate is 2 gamma |V| over it).
+template <typename T, bool TR, bool XW, bool YW>
+__device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, int lane, double dtd, T &smax_out,
+                                          unsigned &bad_out)
+{
+    const int strip = tile % A.nstrips, rb = tile / A.nstrips;
+    TileC<T> K;
+    K.i = strip * CART_COLS - 2 + lane; // column of this lane
+    K.j0 = rb * A.ty;
+    auto wrapc = [&](int c, bool &ok) {
+        ok = true;
+        if (c < 0 || c >= A.nx) {
+            if (A.perx) c = ((c % A.nx) + A.nx) % A.nx;
+            else ok = false;
+        }
+        return c;
+    };
+    bool nxtok;
+    K.col = wrapc(K.i, K.colok);
+    (void)wrapc(K.i + 1, nxtok);
+    // lanes whose x-edge to the right is a wall (either side outside)
+    K.xwall_lane = K.colok != nxtok;
+    K.wlane = lane >= 2 && lane < 2 + CART_COLS && K.i >= 0 && K.i < A.nx;
+    K.rlast = K.j0 + A.ty + 1; // last row loaded
+    K.rstore_end = min(K.j0 + A.ty, A.ny);
+    K.f = (T)dtd / (A.dx * A.dy);
+    K.g = A.g;
+    K.lx = A.dy; // length of an x-edge
+    K.ly = A.dx; // length of a y-edge
+
+    T smax = T(0);
+    bool bad_depth = false, bad_val = false;
+    Carry<T> c0, c1;
+    Ld<T> l0, l1, l2, l3;
+    {
+        Ld<T> p;
+        load_row<XW || YW>(A, K.j0 - 2, K.col, K.colok, p.h, p.qx, p.qy, p.c, p.z, p.rowok);
+        c0.prev = prep(p.h, p.qx, p.qy, p.c, p.z);
+        c0.prevrow = p.rowok;
+        c0.ax_m = c0.ax_x = c0.ax_y = c0.ax_c = T(0);
+        c0.yb_m = c0.yb_x = c0.yb_y = c0.yb_c = T(0);
+        c0.np_h = T(1);
+        c0.np_s = T(1);
+        c0.np_b = T(0);
+        c0.nprow = false;
+        c0.sx_prev = c0.sybot_prev = T(0);
+        load_row<XW || YW>(A, K.j0 - 1, K.col, K.colok, l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
+        load_row<XW || YW>(A, K.j0, K.col, K.colok, l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
+    }
+    // Four rows per trip: the carried registers alternate between c0 and c1
+    // and the four row buffers rotate (row r in one, row r+2 requested into
+    // another), so no register is copied between rows.
+    int r = K.j0 - 1;
+    for (; r + 3 <= K.rlast; r += 4) {
+        row_step<T, TR, XW, YW>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
+    }
+    if (r <= K.rlast) row_step<T, TR, XW, YW>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+    smax_out = smax;
+    bad_out = (bad_depth ? FLAG_DEPTH : 0u) | (bad_val ? FLAG_NONFINITE : 0u);
+}
+
+template <typename T, bool TR>
+__global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
+{
+    const int lane = threadIdx.x;
+    // XCD-aware tile index: workgroup w runs on XCD w % 8
+    const int w = blockIdx.x;
+    const int tile = (w % NUM_XCD) * A.per_xcd + w / NUM_XCD;
+
+    // dt^n from the partial minima of the previous launch
+    const int bank = (int)(A.step % 3);
+    double dtd = A.part[bank * NPART + lane];
+    dtd = wave_min(dtd);
+    if (w == 0) {
+        A.part[((bank + 2) % 3) * NPART + lane] = __builtin_inf();
+        if (lane == 0) {
+            A.book.hist[A.step] = dtd;
+            A.book.t[0] += dtd;
+        }
+    }
+    if (tile >= A.ntiles) return;
+
+    const int strip = tile % A.nstrips, rb = tile / A.nstrips;
+    const int i0 = strip * CART_COLS - 2, j0 = rb * A.ty;
+    const bool xw = !A.perx && (i0 < 0 || i0 + CART_LANES > A.nx);
+    const bool yw = !A.pery && (j0 - 2 < 0 || j0 + A.ty + 1 >= A.ny);
+    T smax;
+    unsigned bad;
+    if (!xw && !yw) cart_tile<T, TR, false, false>(A, tile, lane, dtd, smax, bad);
+    else if (!yw) cart_tile<T, TR, true, false>(A, tile, lane, dtd, smax, bad);
+    else if (!xw) cart_tile<T, TR, false, true>(A, tile, lane, dtd, smax, bad);
+    else cart_tile<T, TR, true, true>(A, tile, lane, dtd, smax, bad);
+
+    // the tile's dt candidate 2 gamma |V| / max sum |G| ||D|| (Eq. (5))
+    const double dmin = wave_min(smax > T(0) ? (double)(T(2) * A.cfl * A.dx * A.dy / smax) : __builtin_inf());
+    if (lane == 0 && dmin >= 0.0 && dmin < __builtin_inf())
+        atomicMin(reinterpret_cast<unsigned long long *>(A.part + ((bank + 1) % 3) * NPART + (w % NPART)),
+                  (unsigned long long)__double_as_longlong(dmin));
+    if (bad) atomicOr(A.book.flags, bad);
+}
+
+// Eq. (5) wave speed of an edge between a and b along qn: |u_Roe| + c
+// (IEEE arithmetic; used once per batch for dt of the initial state).
+template <typename T> __device__ __forceinline__ T roe_speed(T ha, T qa, T hb, T qb, T g)
+{
+    const T sa = sqrt(ha), sb = sqrt(hb);
+    const T ubar = (qa / sa + qb / sb) / (sa + sb);
+    return fabs(ubar) + sqrt(g * T(0.5) * (ha + hb));
+}
+
+// dt of the initial state (step 0) into bank 0, one thread per cell.
+template <typename T>
+__global__ __launch_bounds__(256) void k_cart_dt0(const T *__restrict__ h, const T *__restrict__ qx,
+                                                  const T *__restrict__ qy, int nx, int ny, int perx,
+                                                  int pery, T dx, T dy, T g, T cfl, double *part)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    double cand = __builtin_inf();
+    if (k < (int64_t)nx * ny) {
+        const int i = (int)(k % nx), j = (int)(k / nx);
+        const T hk = h[k], qxk = qx[k], qyk = qy[k];
+        T S = T(0);
+        // left, right (length dy) and bottom, top (length dx)
+        for (int s = 0; s < 4; ++s) {
+            int ii = i + (s == 0 ? -1 : s == 1 ? 1 : 0);
+            int jj = j + (s == 2 ? -1 : s == 3 ? 1 : 0);
+            bool ok = true;
+            if (ii < 0 || ii >= nx) { if (perx) ii = (ii + nx) % nx; else ok = false; }
+            if (jj < 0 || jj >= ny) { if (pery) jj = (jj + ny) % ny; else ok = false; }
+            const T len = s < 2 ? dy : dx;
+            if (!ok) { S += len * sqrt(g * hk); continue; }
+            const int64_t m = (int64_t)jj * nx + ii;
+            const T qa = s < 2 ? qxk : qyk, qb = s < 2 ? qx[m] : qy[m];
+            S += len * roe_speed(hk, qa, h[m], qb, g);
+        }
+        cand = (double)(T(2) * cfl * dx * dy / S);
+    }
+    __shared__ double red[4];
+    double v = wave_min(cand);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        v = fmin(fmin(red[0], red[1]), fmin(red[2], red[3]));
+        if (v >= 0.0 && v < __builtin_inf())
+            atomicMin(reinterpret_cast<unsigned long long *>(part + (blockIdx.x % NPART)),
+                      (unsigned long long)__double_as_longlong(v));
+    }
+}
+
+__global__ void k_cart_init(double *part, StepBook book)
+{
+    const int t = threadIdx.x;
+    for (int k = t; k < 3 * NPART; k += blockDim.x) part[k] = __builtin_inf();
+    if (t == 0) {
+        book.t[0] = 0.0;
+        book.flags[0] = 0u;
+    }
+}
+
+template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int64_t step, double cfl)
+{
+    CartArgs<T, TR> A;
+    const int in = c->cur ^ (int)(step & 1), out = in ^ 1;
+    const T *src = (const T *)c->state[in];
+    T *dst = (T *)c->state[out];
+    const int64_t N = c->N;
+    A.h = src;
+    A.qx = src + N;
+    A.qy = src + 2 * N;
+    A.hc = TR ? src + 3 * N : nullptr;
+    A.z = (const T *)c->zbed;
+    A.oh = dst;
+    A.oqx = dst + N;
+    A.oqy = dst + 2 * N;
+    A.ohc = TR ? dst + 3 * N : nullptr;
+    A.nx = (int)c->nx;
+    A.ny = (int)c->ny;
+    A.perx = c->bc_x == SWE_BC_PERIODIC;
+    A.pery = c->bc_y == SWE_BC_PERIODIC;
+    A.dx = (T)c->dx;
+    A.dy = (T)c->dy;
+    A.g = (T)c->g;
+    A.cfl = (T)cfl;
+    A.ty = c->cart_ty;
+    A.nstrips = (int)((c->nx + CART_COLS - 1) / CART_COLS);
+    const int nrb = (int)((c->ny + A.ty - 1) / A.ty);
+    A.ntiles = A.nstrips * nrb;
+    A.per_xcd = (A.ntiles + NUM_XCD - 1) / NUM_XCD;
+    A.part = c->cart_part;
+    A.book = c->book;
+    A.step = step;
+    return A;
+}
+
+template <typename T, bool TR> static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
+    const T *src = (const T *)c->state[c->cur];
+    const int64_t N = c->N;
+    const unsigned nb0 = (unsigned)((N + 255) / 256);
+    hipLaunchKernelGGL((k_cart_dt0<T>), dim3(nb0), dim3(256), 0, c->stream, src, src + N, src + 2 * N,
+                       (int)c->nx, (int)c->ny, (int)(c->bc_x == SWE_BC_PERIODIC),
+                       (int)(c->bc_y == SWE_BC_PERIODIC), (T)c->dx, (T)c->dy, (T)c->g, (T)cfl,
+                       c->cart_part);
+    for (int64_t s = 0; s < nsteps; ++s) {
+        const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
+        const unsigned grid = (unsigned)(A.per_xcd * NUM_XCD);
+        hipLaunchKernelGGL((k_cart_fused<T, TR>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    const bool f32 = c->prec == SWE_F32;
+    if (c->ntracers) return f32 ? cart_batch_t<float, true>(c, nsteps, cfl) : cart_batch_t<double, true>(c, nsteps, cfl);
+    return f32 ? cart_batch_t<float, false>(c, nsteps, cfl) : cart_batch_t<double, false>(c, nsteps, cfl);
+}
+
+} // namespace swe

@@ -1,5 +1,6 @@
 // C ABI of the shallow-water step library (see include/swe.h).
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -109,6 +110,22 @@ template <typename T> void upload_geometry(swe_ctx *c, const HostEdges &h)
     upload_raw(c, c->c_iarea, iar.data(), N * sizeof(T));
 }
 
+// Rows per tile of the fused Cartesian kernel: at most 32 (measured best on
+// the 4096^2 grid: taller tiles lose latency hiding, shorter ones add halo
+// rows), reduced until the grid gives at least 2048 wavefronts (two per SIMD
+// of the 1024 SIMDs), never below 8 rows.  SWE_CART_TY overrides it (tuning).
+int cart_tile_rows(int64_t nx, int64_t ny)
+{
+    if (const char *e = std::getenv("SWE_CART_TY")) {
+        const int v = std::atoi(e);
+        if (v >= 4 && v <= 4096) return v;
+    }
+    const int64_t strips = (nx + 59) / 60;
+    int ty = 32;
+    while (ty > 8 && strips * ((ny + ty - 1) / ty) < 2048) ty /= 2;
+    return ty;
+}
+
 void free_all(swe_ctx *c)
 {
     for (void *p : c->allocs) (void)hipFree(p);
@@ -180,22 +197,33 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         c->bc_y = d->bc_y;
         c->nv = d->nlayers == 2 ? 6 : 3 + d->ntracers;
         c->rs = c->prec == SWE_F32 ? 4 : 8;
-        c->path = SWE_PATH_EDGE;
-        if (d->path == SWE_PATH_FUSED) {
-            c->err = "fused path not available in this build";
+        // the fused path covers one-layer Cartesian grids; everything else
+        // runs the explicit-edge path
+        const bool fused_ok = d->mesh_kind == SWE_MESH_CART && d->nlayers == 1;
+        if (d->path == SWE_PATH_FUSED && !fused_ok) {
+            c->err = "no fused path for this mesh";
             throw Fail{SWE_E_INVAL};
         }
+        c->path = (d->path == SWE_PATH_EDGE || !fused_ok) ? SWE_PATH_EDGE : SWE_PATH_FUSED;
+        // the fused kernel addresses a field with 32-bit byte offsets
+        if (d->mesh_kind == SWE_MESH_CART &&
+            (d->nx > (int64_t)1 << 30 || d->ny > (int64_t)1 << 30 ||
+             d->nx * d->ny * (d->precision == SWE_F32 ? 4 : 8) >= (int64_t)1 << 32)) {
+            c->err = "grid too large";
+            throw Fail{SWE_E_INVAL};
+        }
+        c->N = d->mesh_kind == SWE_MESH_CART ? d->nx * d->ny : d->ncells;
+
         // host-side mesh work first: mesh errors are reported without
         // touching the GPU
         HostEdges he;
-        if (d->mesh_kind == SWE_MESH_CART) {
-            c->N = d->nx * d->ny;
-            st = build_cart_edges(d->nx, d->ny, d->dx, d->dy, d->bc_x, d->bc_y, he, c->err);
-        } else {
-            c->N = d->ncells;
-            st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, d->tri, he, c->err);
+        if (c->path == SWE_PATH_EDGE) {
+            if (d->mesh_kind == SWE_MESH_CART)
+                st = build_cart_edges(d->nx, d->ny, d->dx, d->dy, d->bc_x, d->bc_y, he, c->err);
+            else
+                st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, d->tri, he, c->err);
+            if (st != SWE_OK) throw Fail{st};
         }
-        if (st != SWE_OK) throw Fail{st};
 
         HIPTRY(hipGetDevice(&c->device));
         if (d->hip_stream) {
@@ -204,23 +232,28 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             HIPTRY(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
             c->own_stream = true;
         }
-        c->E = (int64_t)he.a.size();
 
-        c->e_a = (int32_t *)dev_alloc(c, c->E * sizeof(int32_t));
-        c->e_b = (int32_t *)dev_alloc(c, c->E * sizeof(int32_t));
-        upload_raw(c, c->e_a, he.a.data(), c->E * sizeof(int32_t));
-        upload_raw(c, c->e_b, he.b.data(), c->E * sizeof(int32_t));
-        c->c_off = (int32_t *)dev_alloc(c, (c->N + 1) * sizeof(int32_t));
-        c->c_edge = (int32_t *)dev_alloc(c, he.ce.size() * sizeof(int32_t));
-        upload_raw(c, c->c_off, he.off.data(), (c->N + 1) * sizeof(int32_t));
-        upload_raw(c, c->c_edge, he.ce.data(), he.ce.size() * sizeof(int32_t));
-        if (c->prec == SWE_F32) upload_geometry<float>(c, he);
-        else upload_geometry<double>(c, he);
+        if (c->path == SWE_PATH_EDGE) {
+            c->E = (int64_t)he.a.size();
+            c->e_a = (int32_t *)dev_alloc(c, c->E * sizeof(int32_t));
+            c->e_b = (int32_t *)dev_alloc(c, c->E * sizeof(int32_t));
+            upload_raw(c, c->e_a, he.a.data(), c->E * sizeof(int32_t));
+            upload_raw(c, c->e_b, he.b.data(), c->E * sizeof(int32_t));
+            c->c_off = (int32_t *)dev_alloc(c, (c->N + 1) * sizeof(int32_t));
+            c->c_edge = (int32_t *)dev_alloc(c, he.ce.size() * sizeof(int32_t));
+            upload_raw(c, c->c_off, he.off.data(), (c->N + 1) * sizeof(int32_t));
+            upload_raw(c, c->c_edge, he.ce.data(), he.ce.size() * sizeof(int32_t));
+            if (c->prec == SWE_F32) upload_geometry<float>(c, he);
+            else upload_geometry<double>(c, he);
+            c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
+        } else {
+            c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
+            c->cart_ty = cart_tile_rows(d->nx, d->ny);
+        }
 
         c->state[0] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);
         c->state[1] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);
         c->zbed = dev_alloc(c, (size_t)c->N * c->rs);
-        c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
 
         double *bk = (double *)dev_alloc(c, 8 * sizeof(double));
         c->book.slots = bk;
@@ -331,8 +364,13 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
                 }
             c->hist_cap = cap;
         }
-        HIPTRY(launch_batch_init(c));
-        for (int64_t s = 0; s < nsteps; ++s) HIPTRY(launch_edge_step(c, s, cfl));
+        if (c->path == SWE_PATH_FUSED) {
+            HIPTRY(launch_cart_batch(c, nsteps, cfl));
+            c->cur ^= (nsteps & 1); // ping-pong: the last launch wrote the other buffer
+        } else {
+            HIPTRY(launch_batch_init(c));
+            for (int64_t s = 0; s < nsteps; ++s) HIPTRY(launch_edge_step(c, s, cfl));
+        }
         HIPTRY(hipMemcpyAsync(c->h_pinned, c->book.slots, 8 * sizeof(double), hipMemcpyDeviceToHost, c->stream));
         HIPTRY(hipMemcpyAsync(c->h_pinned + 5, c->book.hist + (nsteps - 1), sizeof(double),
                               hipMemcpyDeviceToHost, c->stream));

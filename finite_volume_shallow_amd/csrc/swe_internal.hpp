@@ -75,6 +75,10 @@ struct swe_ctx {
     void *c_area = nullptr, *c_iarea = nullptr;
     void *e_out = nullptr; // (2 nv + 1) * E reals
 
+    // fused Cartesian path
+    int cart_ty = 64;            // rows per tile
+    double *cart_part = nullptr; // [3][64] partial dt minima
+
     // step bookkeeping
     swe::StepBook book{nullptr, nullptr, nullptr, nullptr};
     int64_t hist_cap = 0, hist_count = 0;
@@ -88,5 +92,6 @@ namespace swe {
 // Kernel launchers (kern_*.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_batch_init(swe_ctx *c);
 hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl);
+hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl);
 
 } // namespace swe

@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libswe.so")
 ARCH = os.environ.get("SWE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["swe_api.hip", "mesh_host.cpp", "kern_edge.hip", "kern_cart.hip"]
+SOURCES = ["swe_api.hip", "mesh_host.cpp", "kern_edge.hip", "kern_cart.hip", "kern_tri.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

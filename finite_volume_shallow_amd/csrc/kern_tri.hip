@@ -1,0 +1,400 @@
+// Fused triangle-mesh path: one kernel launch per time step.
+//
+// The mesh is cut into blocks of B consecutive cells of a Morton order (the
+// library sorts the cells by the Morton code of their centroids, so a block
+// is a compact patch).  The launch for step n gives each block one
+// workgroup, which
+//   1. loads W^n and the bed of its cells plus two rings of neighbours into
+//      LDS (block cells are one coalesced range, the rings a gather list),
+//   2. evaluates every edge touching the block or ring 1 once ([IR] Sec. 2.2
+//      steps 1-4: rotate to the edge frame, Roe fluctuations with the
+//      path-conservative bed term, upwinded transverse momentum and [MG]
+//      pollutant, rotate back) and parks |G| T^-1 (fluctuation) of both
+//      sides in per-edge LDS slots,
+//   3. updates the block and ring 1 (Eq. (4) with dt^n): each cell gathers
+//      its three edge slots in a fixed order -- no atomics, deterministic,
+//   4. evaluates the Eq. (5) wave speeds of W^{n+1} on the block's edges
+//      (both sides of those edges are now in LDS), forms each block cell's
+//      2 gamma |V| / sum |G| ||D|| and folds the block minimum into the
+//      partial minima the next launch reduces to dt^{n+1},
+//   5. writes W^{n+1} of the block (ping-pong buffers).
+// Ring-1 cells are updated redundantly by the neighbouring blocks that need
+// them; that is what lets one launch read and write the state once.
+//
+// Workgroups are mapped XCD-aware: workgroup w runs on XCD w % 8 and the
+// blocks are dealt to the XCDs in contiguous bands, so neighbouring patches
+// (which share halo cells) share an L2.
+#include "dt_reduce.hpp"
+#include "roe_device.hpp"
+#include "swe_internal.hpp"
+
+namespace swe {
+
+constexpr int TRI_THREADS = 256;
+constexpr int TRI_XCD = 8;
+constexpr int TRI_NPART = 64;
+
+template <typename T> struct TriArgs {
+    const T *in[6];
+    T *out[6];
+    const T *z;
+    int64_t N;
+    int B, nblocks, per_xcd, lc_max, e_max;
+    const int32_t *halo_off, *halo_ids, *n1, *edge_off, *e_s0, *slot_off;
+    const uint32_t *e_ab;
+    const T *e_nx, *e_ny, *e_len;
+    const uint16_t *slots;
+    const T *iarea;
+    T g, r, cfl;
+    double *part;
+    StepBook book;
+    int64_t step;
+};
+
+// Largest |eigenvalue| of the two-layer Roe matrix (the outer roots of the
+// quartic, see roe_device.hpp), edge-frame states L, R.
+template <typename T> __device__ __forceinline__ T roe2_speed(const T *L, const T *R, T g, T r, bool &nonhyp)
+{
+    const T s1L = sqrt(L[0]), s1R = sqrt(R[0]), s2L = sqrt(L[3]), s2R = sqrt(R[3]);
+    const T u1 = (L[1] / s1L + R[1] / s1R) / (s1L + s1R);
+    const T u2 = (L[4] / s2L + R[4] / s2R) / (s2L + s2R);
+    const T c1 = g * T(0.5) * (L[0] + R[0]);
+    const T c2 = g * T(0.5) * (L[3] + R[3]);
+    const T rc = r * c1 * c2;
+    const T m = T(0.5) * (u1 + u2), d1 = u1 - m, d2 = u2 - m;
+    const T bound = sqrt(c1 + c2);
+    const T hi = newton_outer(fmax(d1, d2) + bound, d1, d2, c1, c2, rc);
+    const T lo = newton_outer(fmin(d1, d2) - bound, d1, d2, c1, c2, rc);
+    // inner pair real?  (deflated quadratic discriminant)
+    const T p1 = d1 * d1 - c1, p2 = d2 * d2 - c2;
+    const T a3 = T(-2) * (d1 + d2), a2 = p1 + p2 + T(4) * d1 * d2;
+    const T b1 = a3 + (hi + lo), b0 = a2 + (hi + lo) * b1 - hi * lo;
+    if (b1 * b1 - T(4) * b0 < T(0)) nonhyp = true;
+    return fmax(fabs(hi + m), fabs(lo + m));
+}
+
+template <typename T, int NL, bool TR, bool DT0>
+__global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
+{
+    constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
+    extern __shared__ double smem_d[];
+    T *sm = reinterpret_cast<T *>(smem_d);
+    const int LCM = A.lc_max, EM = A.e_max;
+    T *fl = sm + (NV + 1) * LCM; // fluctuation slots: side s, var v at fl[(s * NV + v) * EM + e]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = blockIdx.x;
+    const int blk = (w % TRI_XCD) * A.per_xcd + w / TRI_XCD;
+    const int bank = (int)(A.step % 3);
+    double dtd = 0.0;
+    if (!DT0) {
+        dtd = wave_min(A.part[bank * TRI_NPART + lane]);
+        if (w == 0 && tid < 64) {
+            A.part[((bank + 2) % 3) * TRI_NPART + lane] = __builtin_inf();
+            if (lane == 0) {
+                A.book.hist[A.step] = dtd;
+                A.book.t[0] += dtd;
+            }
+        }
+    }
+    if (blk >= A.nblocks) return; // uniform over the workgroup
+
+    const int64_t base = (int64_t)blk * A.B;
+    const int B0 = (int)min((int64_t)A.B, A.N - base);
+    const int h0 = A.halo_off[blk], nh = A.halo_off[blk + 1] - h0;
+    const int n1 = A.n1[blk];
+    const int LC = B0 + nh;
+    const int e0 = A.edge_off[blk], ne = A.edge_off[blk + 1] - e0, es0 = A.e_s0[blk];
+    const int s0 = A.slot_off[blk];
+    const T g = A.g, rr = A.r;
+    unsigned bad = 0;
+
+    // 1. W^n and z of the block and its two rings
+    for (int l = tid; l < LC; l += TRI_THREADS) {
+        const int64_t gid = l < B0 ? base + l : (int64_t)A.halo_ids[h0 + l - B0];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) sm[v * LCM + l] = A.in[v][gid];
+        sm[NV * LCM + l] = A.z[gid];
+    }
+    __syncthreads();
+
+    if (!DT0) {
+        // 2. every edge touching the block or ring 1, once
+        for (int k = tid; k < ne; k += TRI_THREADS) {
+            const uint32_t ab = A.e_ab[e0 + k];
+            const int la = (int)(ab & 0xFFFFu), lb = (int)(ab >> 16);
+            const T nx = A.e_nx[e0 + k], ny = A.e_ny[e0 + k], len = A.e_len[e0 + k];
+            T Fa[NV], Fb[NV];
+            if constexpr (NL == 1) {
+                const T ha = sm[la], qxa = sm[LCM + la], qya = sm[2 * LCM + la];
+                const T ca = TR ? sm[3 * LCM + la] : T(0);
+                const T qna = qxa * nx + qya * ny, qta = -qxa * ny + qya * nx;
+                Flux1<T, TR> f;
+                if (lb != 0xFFFF) {
+                    const T hb = sm[lb], qxb = sm[LCM + lb], qyb = sm[2 * LCM + lb];
+                    const T cb = TR ? sm[3 * LCM + lb] : T(0);
+                    const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
+                    f = roe1_interior<T, TR>(ha, qna, qta, ca, sm[NV * LCM + la], hb, qnb, qtb, cb,
+                                             sm[NV * LCM + lb], g);
+                } else {
+                    f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
+                }
+                Fa[0] = len * f.am;
+                Fa[1] = len * (f.an * nx - f.at * ny);
+                Fa[2] = len * (f.an * ny + f.at * nx);
+                Fb[0] = len * f.bm;
+                Fb[1] = len * (f.bn * nx - f.bt * ny);
+                Fb[2] = len * (f.bn * ny + f.bt * nx);
+                if constexpr (TR) {
+                    Fa[3] = len * f.ac;
+                    Fb[3] = len * f.bc;
+                }
+            } else {
+                T L[6], R[6];
+#pragma unroll
+                for (int l2 = 0; l2 < 2; ++l2) {
+                    const T qx = sm[(3 * l2 + 1) * LCM + la], qy = sm[(3 * l2 + 2) * LCM + la];
+                    L[3 * l2] = sm[3 * l2 * LCM + la];
+                    L[3 * l2 + 1] = qx * nx + qy * ny;
+                    L[3 * l2 + 2] = -qx * ny + qy * nx;
+                }
+                Flux2<T> f;
+                if (lb != 0xFFFF) {
+#pragma unroll
+                    for (int l2 = 0; l2 < 2; ++l2) {
+                        const T qx = sm[(3 * l2 + 1) * LCM + lb], qy = sm[(3 * l2 + 2) * LCM + lb];
+                        R[3 * l2] = sm[3 * l2 * LCM + lb];
+                        R[3 * l2 + 1] = qx * nx + qy * ny;
+                        R[3 * l2 + 2] = -qx * ny + qy * nx;
+                    }
+                    f = roe2_interior<T>(L, sm[NV * LCM + la], R, sm[NV * LCM + lb], g, rr);
+                } else {
+                    f = roe2_wall<T>(L, sm[NV * LCM + la], g, rr);
+                }
+                if (f.nonhyp) bad |= FLAG_NONHYPERBOLIC;
+#pragma unroll
+                for (int l2 = 0; l2 < 2; ++l2) {
+                    Fa[3 * l2] = len * f.a[3 * l2];
+                    Fa[3 * l2 + 1] = len * (f.a[3 * l2 + 1] * nx - f.a[3 * l2 + 2] * ny);
+                    Fa[3 * l2 + 2] = len * (f.a[3 * l2 + 1] * ny + f.a[3 * l2 + 2] * nx);
+                    Fb[3 * l2] = len * f.b[3 * l2];
+                    Fb[3 * l2 + 1] = len * (f.b[3 * l2 + 1] * nx - f.b[3 * l2 + 2] * ny);
+                    Fb[3 * l2 + 2] = len * (f.b[3 * l2 + 1] * ny + f.b[3 * l2 + 2] * nx);
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                fl[v * EM + k] = Fa[v];
+                fl[(NV + v) * EM + k] = Fb[v];
+            }
+        }
+        __syncthreads();
+
+        // 3. W^{n+1} of the block and ring 1, gathered in a fixed order
+        for (int l = tid; l < B0 + n1; l += TRI_THREADS) {
+            T acc[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[v] = T(0);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int sl = A.slots[3 * (s0 + l) + j];
+                const int e = sl >> 1, side = sl & 1;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[v] += fl[(side * NV + v) * EM + e];
+            }
+            const T fct = (T)dtd * A.iarea[s0 + l];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) sm[v * LCM + l] -= fct * acc[v];
+        }
+        __syncthreads();
+    }
+
+    // 4. Eq. (5) speeds on the edges touching the block (of W^{n+1}, or of
+    // W^0 for the prologue), parked in the first slot array
+    for (int k = tid; k < es0; k += TRI_THREADS) {
+        const uint32_t ab = A.e_ab[e0 + k];
+        const int la = (int)(ab & 0xFFFFu), lb = (int)(ab >> 16);
+        const T nx = A.e_nx[e0 + k], ny = A.e_ny[e0 + k], len = A.e_len[e0 + k];
+        T sp;
+        if constexpr (NL == 1) {
+            const T ha = sm[la], qna = sm[LCM + la] * nx + sm[2 * LCM + la] * ny;
+            if (lb != 0xFFFF) {
+                const T hb = sm[lb], qnb = sm[LCM + lb] * nx + sm[2 * LCM + lb] * ny;
+                const T sa = sqrt(ha), sb = sqrt(hb);
+                sp = fabs((qna / sa + qnb / sb) / (sa + sb)) + sqrt(g * T(0.5) * (ha + hb));
+            } else {
+                sp = sqrt(g * ha);
+            }
+        } else {
+            T L[6], R[6];
+#pragma unroll
+            for (int l2 = 0; l2 < 2; ++l2) {
+                L[3 * l2] = sm[3 * l2 * LCM + la];
+                L[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + la] * nx + sm[(3 * l2 + 2) * LCM + la] * ny;
+                L[3 * l2 + 2] = T(0);
+            }
+            if (lb != 0xFFFF) {
+#pragma unroll
+                for (int l2 = 0; l2 < 2; ++l2) {
+                    R[3 * l2] = sm[3 * l2 * LCM + lb];
+                    R[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + lb] * nx + sm[(3 * l2 + 2) * LCM + lb] * ny;
+                    R[3 * l2 + 2] = T(0);
+                }
+            } else { // mirror state
+                R[0] = L[0];
+                R[1] = -L[1];
+                R[3] = L[3];
+                R[4] = -L[4];
+                R[2] = R[5] = T(0);
+            }
+            bool nh2 = false;
+            sp = roe2_speed<T>(L, R, g, rr, nh2);
+            if (nh2) bad |= FLAG_NONHYPERBOLIC;
+        }
+        fl[k] = len * sp;
+    }
+    __syncthreads();
+
+    // 5. dt candidates of the block cells, W^{n+1} out
+    double cand = __builtin_inf();
+    for (int l = tid; l < B0; l += TRI_THREADS) {
+        T S = T(0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) S += fl[A.slots[3 * (s0 + l) + j] >> 1];
+        cand = fmin(cand, (double)(T(2) * A.cfl / (A.iarea[s0 + l] * S)));
+        if (!DT0) {
+            bool badv = false;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const T x = sm[v * LCM + l];
+                A.out[v][base + l] = x;
+                badv |= !isfinite(x);
+            }
+            if (!(sm[l] > T(0)) || (NL == 2 && !(sm[3 * LCM + l] > T(0)))) bad |= FLAG_DEPTH;
+            if (badv) bad |= FLAG_NONFINITE;
+        }
+    }
+    const int slot_bank = DT0 ? 0 : (bank + 1) % 3;
+    block_min_to_slot(cand, A.part + slot_bank * TRI_NPART + (w % TRI_NPART));
+    if (bad) atomicOr(A.book.flags, bad);
+}
+
+__global__ void k_tri_init(double *part, StepBook book)
+{
+    const int t = threadIdx.x;
+    for (int k = t; k < 3 * TRI_NPART; k += blockDim.x) part[k] = __builtin_inf();
+    if (t == 0) {
+        book.t[0] = 0.0;
+        book.flags[0] = 0u;
+    }
+}
+
+// caller order <-> internal (Morton) order
+template <typename T>
+__global__ void k_permute(const T *__restrict__ src, T *__restrict__ dst, const int32_t *__restrict__ perm,
+                          int64_t n, int to_internal)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (to_internal) dst[i] = src[perm[i]];
+    else dst[perm[i]] = src[i];
+}
+
+hipError_t launch_permute(swe_ctx *c, const void *src, void *dst, int to_internal)
+{
+    const unsigned nb = (unsigned)((c->N + 255) / 256);
+    if (c->prec == SWE_F32)
+        hipLaunchKernelGGL(k_permute<float>, dim3(nb), dim3(256), 0, c->stream, (const float *)src, (float *)dst,
+                           c->perm, c->N, to_internal);
+    else
+        hipLaunchKernelGGL(k_permute<double>, dim3(nb), dim3(256), 0, c->stream, (const double *)src,
+                           (double *)dst, c->perm, c->N, to_internal);
+    return hipGetLastError();
+}
+
+template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, double cfl)
+{
+    TriArgs<T> A;
+    const int in = c->cur ^ (int)(step & 1), out = in ^ 1;
+    for (int v = 0; v < 6; ++v) {
+        A.in[v] = v < c->nv ? (const T *)c->state[in] + (int64_t)v * c->N : nullptr;
+        A.out[v] = v < c->nv ? (T *)c->state[out] + (int64_t)v * c->N : nullptr;
+    }
+    A.z = (const T *)c->zbed;
+    A.N = c->N;
+    A.B = c->tb.B;
+    A.nblocks = c->tb.nblocks;
+    A.per_xcd = (A.nblocks + TRI_XCD - 1) / TRI_XCD;
+    A.lc_max = c->tb.lc_max;
+    A.e_max = c->tb.e_max;
+    A.halo_off = c->tb.halo_off;
+    A.halo_ids = c->tb.halo_ids;
+    A.n1 = c->tb.n1;
+    A.edge_off = c->tb.edge_off;
+    A.e_s0 = c->tb.e_s0;
+    A.slot_off = c->tb.slot_off;
+    A.e_ab = c->tb.e_ab;
+    A.e_nx = (const T *)c->tb.e_nx;
+    A.e_ny = (const T *)c->tb.e_ny;
+    A.e_len = (const T *)c->tb.e_len;
+    A.slots = c->tb.slots;
+    A.iarea = (const T *)c->tb.iarea;
+    A.g = (T)c->g;
+    A.r = (T)c->r;
+    A.cfl = (T)cfl;
+    A.part = c->cart_part;
+    A.book = c->book;
+    A.step = step;
+    return A;
+}
+
+template <typename T, int NL, bool TR> static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
+    const size_t lds = ((size_t)(NV + 1) * c->tb.lc_max + (size_t)2 * NV * c->tb.e_max) * sizeof(T);
+    const int per_xcd = (c->tb.nblocks + TRI_XCD - 1) / TRI_XCD;
+    const dim3 grid((unsigned)(per_xcd * TRI_XCD)), block(TRI_THREADS);
+    hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
+    hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true>), grid, block, lds, c->stream, tri_args<T>(c, 0, cfl));
+    for (int64_t s = 0; s < nsteps; ++s)
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false>), grid, block, lds, c->stream, tri_args<T>(c, s, cfl));
+    return hipGetLastError();
+}
+
+hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    const bool f32 = c->prec == SWE_F32;
+    if (c->nlayers == 2) return f32 ? tri_batch_t<float, 2, false>(c, nsteps, cfl) : tri_batch_t<double, 2, false>(c, nsteps, cfl);
+    if (c->ntracers) return f32 ? tri_batch_t<float, 1, true>(c, nsteps, cfl) : tri_batch_t<double, 1, true>(c, nsteps, cfl);
+    return f32 ? tri_batch_t<float, 1, false>(c, nsteps, cfl) : tri_batch_t<double, 1, false>(c, nsteps, cfl);
+}
+
+// LDS bytes a block size needs (for choosing B and the launch attribute)
+size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max)
+{
+    return ((size_t)(nv + 1) * lc_max + (size_t)2 * nv * e_max) * rs;
+}
+
+hipError_t tri_set_lds_limit(swe_ctx *c, size_t bytes)
+{
+    hipError_t e = hipSuccess;
+    auto setf = [&](const void *f) {
+        hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (r != hipSuccess) e = r;
+    };
+    setf((const void *)k_tri_fused<double, 1, false, true>);
+    setf((const void *)k_tri_fused<double, 1, false, false>);
+    setf((const void *)k_tri_fused<double, 1, true, true>);
+    setf((const void *)k_tri_fused<double, 1, true, false>);
+    setf((const void *)k_tri_fused<double, 2, false, true>);
+    setf((const void *)k_tri_fused<double, 2, false, false>);
+    setf((const void *)k_tri_fused<float, 1, false, true>);
+    setf((const void *)k_tri_fused<float, 1, false, false>);
+    setf((const void *)k_tri_fused<float, 1, true, true>);
+    setf((const void *)k_tri_fused<float, 1, true, false>);
+    setf((const void *)k_tri_fused<float, 2, false, true>);
+    setf((const void *)k_tri_fused<float, 2, false, false>);
+    return e;
+}
+
+} // namespace swe

@@ -161,4 +161,151 @@ int build_tri_edges(int64_t nnodes, const double *xy, int64_t ncells, const int3
     return SWE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Morton order of triangle centroids
+// ---------------------------------------------------------------------------
+
+static uint64_t spread_bits16(uint64_t v)
+{
+    v &= 0xFFFFu;
+    v = (v | (v << 8)) & 0x00FF00FFu;
+    v = (v | (v << 4)) & 0x0F0F0F0Fu;
+    v = (v | (v << 2)) & 0x33333333u;
+    v = (v | (v << 1)) & 0x55555555u;
+    return v;
+}
+
+void morton_perm(int64_t nnodes, const double *xy, int64_t ncells, const int32_t *tri,
+                 std::vector<int32_t> &perm)
+{
+    (void)nnodes;
+    std::vector<double> cx(ncells), cy(ncells);
+    double x0 = 1e300, x1 = -1e300, y0 = 1e300, y1 = -1e300;
+    for (int64_t t = 0; t < ncells; ++t) {
+        double sx = 0, sy = 0;
+        for (int k = 0; k < 3; ++k) {
+            sx += xy[2 * (int64_t)tri[3 * t + k]];
+            sy += xy[2 * (int64_t)tri[3 * t + k] + 1];
+        }
+        cx[t] = sx / 3.0;
+        cy[t] = sy / 3.0;
+        x0 = std::min(x0, cx[t]);
+        x1 = std::max(x1, cx[t]);
+        y0 = std::min(y0, cy[t]);
+        y1 = std::max(y1, cy[t]);
+    }
+    const double sx = 65535.0 / std::max(x1 - x0, 1e-300), sy = 65535.0 / std::max(y1 - y0, 1e-300);
+    std::vector<uint64_t> code(ncells);
+    for (int64_t t = 0; t < ncells; ++t) {
+        const uint64_t qx = (uint64_t)std::floor((cx[t] - x0) * sx);
+        const uint64_t qy = (uint64_t)std::floor((cy[t] - y0) * sy);
+        code[t] = spread_bits16(qx) | (spread_bits16(qy) << 1);
+    }
+    perm.resize(ncells);
+    for (int64_t t = 0; t < ncells; ++t) perm[t] = (int32_t)t;
+    std::stable_sort(perm.begin(), perm.end(), [&](int32_t a, int32_t b) { return code[a] < code[b]; });
+}
+
+// ---------------------------------------------------------------------------
+// Blocks of the fused triangle path
+// ---------------------------------------------------------------------------
+
+int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std::string &err)
+{
+    out = HostBlocks();
+    out.B = B;
+    const int64_t E = (int64_t)he.a.size();
+    const int nb = (int)((N + B - 1) / B);
+    out.nblocks = nb;
+    std::vector<int32_t> cstamp(N, -1), cloc(N, 0), estamp(E, -1), eloc(E, 0);
+    out.halo_off.push_back(0);
+    out.edge_off.push_back(0);
+    out.slot_off.push_back(0);
+    auto other = [&](int64_t e, int64_t c) -> int64_t { return he.a[e] == c ? he.b[e] : he.a[e]; };
+    std::vector<int32_t> ring1, ring2, ledges;
+    for (int b = 0; b < nb; ++b) {
+        const int64_t base = (int64_t)b * B;
+        const int B0 = (int)std::min<int64_t>(B, N - base);
+        for (int l = 0; l < B0; ++l) {
+            cstamp[base + l] = b;
+            cloc[base + l] = l;
+        }
+        ring1.clear();
+        ring2.clear();
+        for (int l = 0; l < B0; ++l) {
+            const int64_t c = base + l;
+            for (int32_t k = he.off[c]; k < he.off[c + 1]; ++k) {
+                const int64_t o = other(he.ce[k] >> 1, c);
+                if (o >= 0 && cstamp[o] != b) {
+                    cstamp[o] = b;
+                    ring1.push_back((int32_t)o);
+                }
+            }
+        }
+        for (int32_t c : ring1)
+            for (int32_t k = he.off[c]; k < he.off[c + 1]; ++k) {
+                const int64_t o = other(he.ce[k] >> 1, c);
+                if (o >= 0 && cstamp[o] != b) {
+                    cstamp[o] = b;
+                    ring2.push_back((int32_t)o);
+                }
+            }
+        const int n1 = (int)ring1.size(), n2 = (int)ring2.size();
+        for (int i = 0; i < n1; ++i) cloc[ring1[i]] = B0 + i;
+        for (int i = 0; i < n2; ++i) cloc[ring2[i]] = B0 + n1 + i;
+        const int lc = B0 + n1 + n2;
+        // local edges: those of the block's cells first, then ring 1's
+        ledges.clear();
+        auto add_edges_of = [&](int64_t c) {
+            for (int32_t k = he.off[c]; k < he.off[c + 1]; ++k) {
+                const int32_t e = he.ce[k] >> 1;
+                if (estamp[e] != b) {
+                    estamp[e] = b;
+                    eloc[e] = (int32_t)ledges.size();
+                    ledges.push_back(e);
+                }
+            }
+        };
+        for (int l = 0; l < B0; ++l) add_edges_of(base + l);
+        const int es0 = (int)ledges.size();
+        for (int32_t c : ring1) add_edges_of(c);
+        const int ne = (int)ledges.size();
+        if (lc >= 0xFFFF || 2 * ne >= 0xFFFF) {
+            err = "triangle block too large for 16-bit local indices";
+            return SWE_E_INVAL;
+        }
+        for (int32_t e : ledges) {
+            const uint32_t la = (uint32_t)cloc[he.a[e]];
+            const uint32_t lb = he.b[e] >= 0 ? (uint32_t)cloc[he.b[e]] : 0xFFFFu;
+            out.e_ab.push_back(la | (lb << 16));
+            out.e_nx.push_back(he.nx[e]);
+            out.e_ny.push_back(he.ny[e]);
+            out.e_len.push_back(he.len[e]);
+        }
+        auto add_slots_of = [&](int64_t c) {
+            if (he.off[c + 1] - he.off[c] != 3) return false;
+            for (int32_t k = he.off[c]; k < he.off[c + 1]; ++k) {
+                const int32_t e = he.ce[k] >> 1, side = he.ce[k] & 1;
+                out.slots.push_back((uint16_t)((eloc[e] << 1) | side));
+            }
+            out.iarea.push_back(1.0 / he.area[c]);
+            return true;
+        };
+        for (int l = 0; l < B0; ++l)
+            if (!add_slots_of(base + l)) { err = "a triangle without three edges"; return SWE_E_INVAL; }
+        for (int32_t c : ring1)
+            if (!add_slots_of(c)) { err = "a triangle without three edges"; return SWE_E_INVAL; }
+        out.halo_ids.insert(out.halo_ids.end(), ring1.begin(), ring1.end());
+        out.halo_ids.insert(out.halo_ids.end(), ring2.begin(), ring2.end());
+        out.halo_off.push_back((int32_t)out.halo_ids.size());
+        out.n1.push_back(n1);
+        out.e_s0.push_back(es0);
+        out.edge_off.push_back((int32_t)out.e_ab.size());
+        out.slot_off.push_back(out.slot_off.back() + B0 + n1);
+        out.lc_max = std::max(out.lc_max, lc);
+        out.e_max = std::max(out.e_max, ne);
+    }
+    return SWE_OK;
+}
+
 } // namespace swe

@@ -79,7 +79,6 @@ int validate(const swe_mesh_desc *d, std::string &err)
     } else if (d->mesh_kind == SWE_MESH_TRI) {
         if (!d->node_xy || !d->tri) { err = "node_xy and tri are required"; return SWE_E_INVAL; }
         if (d->nnodes < 3 || d->ncells < 1) { err = "empty triangle mesh"; return SWE_E_INVAL; }
-        if (d->path == SWE_PATH_FUSED) { err = "no fused path for triangle meshes"; return SWE_E_INVAL; }
     } else {
         err = "bad mesh_kind";
         return SWE_E_INVAL;
@@ -124,6 +123,39 @@ int cart_tile_rows(int64_t nx, int64_t ny)
     int ty = 32;
     while (ty > 8 && strips * ((ny + ty - 1) / ty) < 2048) ty /= 2;
     return ty;
+}
+
+template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
+{
+    auto ints = [&](const std::vector<int32_t> &v) {
+        int32_t *p = (int32_t *)dev_alloc(c, v.size() * sizeof(int32_t));
+        upload_raw(c, p, v.data(), v.size() * sizeof(int32_t));
+        return p;
+    };
+    auto reals = [&](const std::vector<double> &v) {
+        void *p = dev_alloc(c, v.size() * sizeof(T));
+        std::vector<T> tmp(v.begin(), v.end());
+        upload_raw(c, p, tmp.data(), v.size() * sizeof(T));
+        return p;
+    };
+    c->tb.B = hb.B;
+    c->tb.nblocks = hb.nblocks;
+    c->tb.lc_max = hb.lc_max;
+    c->tb.e_max = hb.e_max;
+    c->tb.halo_off = ints(hb.halo_off);
+    c->tb.halo_ids = ints(hb.halo_ids);
+    c->tb.n1 = ints(hb.n1);
+    c->tb.edge_off = ints(hb.edge_off);
+    c->tb.e_s0 = ints(hb.e_s0);
+    c->tb.slot_off = ints(hb.slot_off);
+    c->tb.e_ab = (uint32_t *)dev_alloc(c, hb.e_ab.size() * sizeof(uint32_t));
+    upload_raw(c, c->tb.e_ab, hb.e_ab.data(), hb.e_ab.size() * sizeof(uint32_t));
+    c->tb.e_nx = reals(hb.e_nx);
+    c->tb.e_ny = reals(hb.e_ny);
+    c->tb.e_len = reals(hb.e_len);
+    c->tb.iarea = reals(hb.iarea);
+    c->tb.slots = (uint16_t *)dev_alloc(c, hb.slots.size() * sizeof(uint16_t));
+    upload_raw(c, c->tb.slots, hb.slots.data(), hb.slots.size() * sizeof(uint16_t));
 }
 
 void free_all(swe_ctx *c)
@@ -197,9 +229,9 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         c->bc_y = d->bc_y;
         c->nv = d->nlayers == 2 ? 6 : 3 + d->ntracers;
         c->rs = c->prec == SWE_F32 ? 4 : 8;
-        // the fused path covers one-layer Cartesian grids; everything else
-        // runs the explicit-edge path
-        const bool fused_ok = d->mesh_kind == SWE_MESH_CART && d->nlayers == 1;
+        // fused paths: one-layer Cartesian grids and every triangle mesh;
+        // SWE_PATH_EDGE forces the explicit-edge path
+        const bool fused_ok = d->mesh_kind == SWE_MESH_TRI || d->nlayers == 1;
         if (d->path == SWE_PATH_FUSED && !fused_ok) {
             c->err = "no fused path for this mesh";
             throw Fail{SWE_E_INVAL};
@@ -217,12 +249,39 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         // host-side mesh work first: mesh errors are reported without
         // touching the GPU
         HostEdges he;
+        HostBlocks hb;
+        std::vector<int32_t> tri_int;
         if (c->path == SWE_PATH_EDGE) {
             if (d->mesh_kind == SWE_MESH_CART)
                 st = build_cart_edges(d->nx, d->ny, d->dx, d->dy, d->bc_x, d->bc_y, he, c->err);
             else
                 st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, d->tri, he, c->err);
             if (st != SWE_OK) throw Fail{st};
+        } else if (d->mesh_kind == SWE_MESH_TRI) {
+            // validate the caller's mesh first (node range, orientation)
+            for (int64_t t = 0; t < 3 * d->ncells; ++t)
+                if (d->tri[t] < 0 || d->tri[t] >= d->nnodes) {
+                    c->err = "node id out of range in triangle " + std::to_string(t / 3);
+                    throw Fail{SWE_E_INVAL};
+                }
+            morton_perm(d->nnodes, d->node_xy, d->ncells, d->tri, c->perm_host);
+            tri_int.resize(3 * d->ncells);
+            for (int64_t i = 0; i < d->ncells; ++i)
+                for (int k = 0; k < 3; ++k) tri_int[3 * i + k] = d->tri[3 * (int64_t)c->perm_host[i] + k];
+            st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, tri_int.data(), he, c->err);
+            if (st != SWE_OK) throw Fail{st};
+            // the largest block (cells per workgroup) whose LDS fits in 64 KiB
+            int B = 256;
+            for (;;) {
+                st = build_tri_blocks(he, c->N, B, hb, c->err);
+                if (st != SWE_OK) throw Fail{st};
+                if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= 65536 || B <= 32) break;
+                B /= 2;
+            }
+            if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) > 65536) {
+                c->err = "triangle blocks do not fit in LDS (mesh too irregular); use SWE_PATH_EDGE";
+                throw Fail{SWE_E_INVAL};
+            }
         }
 
         HIPTRY(hipGetDevice(&c->device));
@@ -246,9 +305,15 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             if (c->prec == SWE_F32) upload_geometry<float>(c, he);
             else upload_geometry<double>(c, he);
             c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
-        } else {
+        } else if (d->mesh_kind == SWE_MESH_CART) {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             c->cart_ty = cart_tile_rows(d->nx, d->ny);
+        } else {
+            c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
+            if (c->prec == SWE_F32) upload_blocks<float>(c, hb);
+            else upload_blocks<double>(c, hb);
+            c->perm = (int32_t *)dev_alloc(c, c->N * sizeof(int32_t));
+            upload_raw(c, c->perm, c->perm_host.data(), c->N * sizeof(int32_t));
         }
 
         c->state[0] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);
@@ -294,9 +359,16 @@ int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
         }
     try {
         c->cur = 0;
-        upload_real(c, c->zbed, z, c->N);
+        std::vector<double> tmp;
+        auto ordered = [&](const double *src) -> const double * {
+            if (!c->perm) return src;
+            tmp.resize(c->N);
+            for (int64_t i = 0; i < c->N; ++i) tmp[i] = src[c->perm_host[i]];
+            return tmp.data();
+        };
+        upload_real(c, c->zbed, ordered(z), c->N);
         for (int v = 0; v < c->nv; ++v)
-            upload_real(c, (char *)c->state[0] + (size_t)v * c->N * c->rs, cons[v], c->N);
+            upload_real(c, (char *)c->state[0] + (size_t)v * c->N * c->rs, ordered(cons[v]), c->N);
     } catch (const Fail &f) {
         return f.code;
     }
@@ -320,10 +392,16 @@ int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
     try {
         c->cur = 0;
         const size_t bytes = (size_t)c->N * c->rs;
-        HIPTRY(hipMemcpyAsync(c->zbed, z, bytes, hipMemcpyDeviceToDevice, c->stream));
-        for (int v = 0; v < c->nv; ++v)
-            HIPTRY(hipMemcpyAsync((char *)c->state[0] + v * bytes, cons[v], bytes, hipMemcpyDeviceToDevice,
-                                  c->stream));
+        if (c->perm) {
+            HIPTRY(launch_permute(c, z, c->zbed, 1));
+            for (int v = 0; v < c->nv; ++v)
+                HIPTRY(launch_permute(c, cons[v], (char *)c->state[0] + v * bytes, 1));
+        } else {
+            HIPTRY(hipMemcpyAsync(c->zbed, z, bytes, hipMemcpyDeviceToDevice, c->stream));
+            for (int v = 0; v < c->nv; ++v)
+                HIPTRY(hipMemcpyAsync((char *)c->state[0] + v * bytes, cons[v], bytes, hipMemcpyDeviceToDevice,
+                                      c->stream));
+        }
     } catch (const Fail &f) {
         return f.code;
     }
@@ -365,7 +443,8 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
             c->hist_cap = cap;
         }
         if (c->path == SWE_PATH_FUSED) {
-            HIPTRY(launch_cart_batch(c, nsteps, cfl));
+            if (c->kind == SWE_MESH_CART) HIPTRY(launch_cart_batch(c, nsteps, cfl));
+            else HIPTRY(launch_tri_batch(c, nsteps, cfl));
             c->cur ^= (nsteps & 1); // ping-pong: the last launch wrote the other buffer
         } else {
             HIPTRY(launch_batch_init(c));
@@ -405,18 +484,29 @@ int swe_get_state(swe_ctx *c, double *const *out)
     }
     try {
         const char *base = (const char *)c->state[c->cur];
+        std::vector<double> d64;
+        std::vector<float> f32;
         for (int v = 0; v < c->nv; ++v) {
+            const double *src;
             if (c->prec == SWE_F64) {
-                HIPTRY(hipMemcpyAsync(out[v], base + (size_t)v * c->N * 8, c->N * 8, hipMemcpyDeviceToHost,
+                d64.resize(c->N);
+                HIPTRY(hipMemcpyAsync(d64.data(), base + (size_t)v * c->N * 8, c->N * 8, hipMemcpyDeviceToHost,
                                       c->stream));
                 HIPTRY(hipStreamSynchronize(c->stream));
+                src = d64.data();
             } else {
-                std::vector<float> tmp(c->N);
-                HIPTRY(hipMemcpyAsync(tmp.data(), base + (size_t)v * c->N * 4, c->N * 4, hipMemcpyDeviceToHost,
+                f32.resize(c->N);
+                d64.resize(c->N);
+                HIPTRY(hipMemcpyAsync(f32.data(), base + (size_t)v * c->N * 4, c->N * 4, hipMemcpyDeviceToHost,
                                       c->stream));
                 HIPTRY(hipStreamSynchronize(c->stream));
-                for (int64_t i = 0; i < c->N; ++i) out[v][i] = tmp[i];
+                for (int64_t i = 0; i < c->N; ++i) d64[i] = f32[i];
+                src = d64.data();
             }
+            if (c->perm)
+                for (int64_t i = 0; i < c->N; ++i) out[v][c->perm_host[i]] = src[i];
+            else
+                std::memcpy(out[v], src, c->N * sizeof(double));
         }
     } catch (const Fail &f) {
         return f.code;
@@ -442,9 +532,11 @@ int swe_get_state_device(swe_ctx *c, void *const *out)
     }
     try {
         const size_t bytes = (size_t)c->N * c->rs;
-        for (int v = 0; v < c->nv; ++v)
-            HIPTRY(hipMemcpyAsync(out[v], (const char *)c->state[c->cur] + v * bytes, bytes,
-                                  hipMemcpyDeviceToDevice, c->stream));
+        for (int v = 0; v < c->nv; ++v) {
+            const char *src = (const char *)c->state[c->cur] + v * bytes;
+            if (c->perm) HIPTRY(launch_permute(c, src, out[v], 0));
+            else HIPTRY(hipMemcpyAsync(out[v], src, bytes, hipMemcpyDeviceToDevice, c->stream));
+        }
     } catch (const Fail &f) {
         return f.code;
     }

@@ -25,6 +25,31 @@ struct HostEdges {
     std::vector<double> area;
 };
 
+// Per-block data of the fused triangle path.  Cells are taken in blocks of
+// B consecutive (Morton-ordered) cells; a block also reads two rings of
+// neighbours ("halo"): ring 1 = neighbours of the block, ring 2 = neighbours
+// of ring 1.  Its local edges are every edge touching the block or ring 1,
+// the ones touching the block first.  Local cell ids: block cells 0..B0-1,
+// then ring 1, then ring 2.
+struct HostBlocks {
+    int B = 0, nblocks = 0;
+    int lc_max = 0, e_max = 0;              // largest local cell / edge counts
+    std::vector<int32_t> halo_off, halo_ids; // global ids of ring 1 then ring 2
+    std::vector<int32_t> n1;                 // ring-1 size per block
+    std::vector<int32_t> edge_off, e_s0;     // local edges; leading edges touching the block
+    std::vector<uint32_t> e_ab;              // local a | local b << 16 (b = 0xFFFF: wall)
+    std::vector<double> e_nx, e_ny, e_len;
+    std::vector<int32_t> slot_off;           // per block: first slot row (block + ring 1 cells)
+    std::vector<uint16_t> slots;             // 3 per cell: local edge << 1 | side
+    std::vector<double> iarea;               // 1/|V| per slot row
+};
+
+int build_tri_blocks(const HostEdges &he, int64_t ncells, int B, HostBlocks &out, std::string &err);
+
+// Morton order of the triangle centroids (stable): perm[internal] = caller id.
+void morton_perm(int64_t nnodes, const double *xy, int64_t ncells, const int32_t *tri,
+                 std::vector<int32_t> &perm);
+
 int build_cart_edges(int64_t nx, int64_t ny, double dx, double dy, int bcx, int bcy,
                      HostEdges &out, std::string &err);
 int build_tri_edges(int64_t nnodes, const double *xy, int64_t ncells, const int32_t *tri,
@@ -77,7 +102,19 @@ struct swe_ctx {
 
     // fused Cartesian path
     int cart_ty = 64;            // rows per tile
-    double *cart_part = nullptr; // [3][64] partial dt minima
+    double *cart_part = nullptr; // [3][64] partial dt minima (both fused paths)
+
+    // fused triangle path: cells in internal (Morton) order
+    int32_t *perm = nullptr;          // device: internal index -> caller index
+    std::vector<int32_t> perm_host;   // same on the host
+    struct {
+        int B = 0, nblocks = 0, lc_max = 0, e_max = 0;
+        int32_t *halo_off = nullptr, *halo_ids = nullptr, *n1 = nullptr, *edge_off = nullptr,
+                *e_s0 = nullptr, *slot_off = nullptr;
+        uint32_t *e_ab = nullptr;
+        void *e_nx = nullptr, *e_ny = nullptr, *e_len = nullptr, *iarea = nullptr;
+        uint16_t *slots = nullptr;
+    } tb;
 
     // step bookkeeping
     swe::StepBook book{nullptr, nullptr, nullptr, nullptr};
@@ -93,5 +130,8 @@ namespace swe {
 hipError_t launch_batch_init(swe_ctx *c);
 hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl);
 hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl);
+hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl);
+hipError_t launch_permute(swe_ctx *c, const void *src, void *dst, int to_internal);
+size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max);
 
 } // namespace swe

@@ -50,9 +50,11 @@ enum swe_mesh_kind { SWE_MESH_CART = 0, SWE_MESH_TRI = 1 };
 enum swe_precision { SWE_F64 = 0, SWE_F32 = 1 };
 enum swe_bc { SWE_BC_WALL = 0, SWE_BC_PERIODIC = 1 };
 
-/* Kernel path.  AUTO picks the fused path where one exists for the mesh
- * (Cartesian one-layer grids), else the edge path.  EDGE forces the generic
- * explicit-edge-list path on any mesh. */
+/* Kernel path.  AUTO picks the fused one-launch-per-step path (Cartesian
+ * one-layer grids and triangle meshes); EDGE forces the generic
+ * explicit-edge-list path (three launches per step) on any mesh; FUSED
+ * requests the fused path and fails with SWE_E_INVAL where none exists
+ * (two layers on a Cartesian grid are rejected anyway). */
 enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2 };
 
 typedef struct swe_mesh_desc {

@@ -18,6 +18,16 @@ pytestmark = pytest.mark.gpu
 
 PATHS = {"auto": 0, "edge": 1}
 
+def _shuffled_tri(nq, seed=77):
+    """config 4 with its cells listed in a random order (not Morton)."""
+    w = inputs.config4(nq=nq)
+    order = np.random.default_rng(seed).permutation(w.ncells)
+    w.tri = np.ascontiguousarray(w.tri[order])
+    w.z = w.z[order]
+    w.state = [a[order] for a in w.state]
+    return w
+
+
 CASES = {
     # name: (workload factory, steps, precision)
     "c1-dam-break-64x64": (lambda: inputs.config1(), 100, "f64"),
@@ -31,6 +41,8 @@ CASES = {
     "c4-tri-ragged-19": (lambda: inputs.config4(nq=19), 25, "f64"),
     "c5-two-layer-30": (lambda: inputs.config5(nq=30), 200, "f64"),
     "c5-two-layer-13": (lambda: inputs.config5(nq=13), 100, "f64"),
+    "c4-tri-shuffled-30": (lambda: _shuffled_tri(30), 60, "f64"),
+    "c4-tri-40-f32": (lambda: inputs.config4(nq=40), 100, "f32"),
 }
 
 
@@ -142,6 +154,31 @@ def test_device_state_roundtrip_and_stream():
     got, _, _ = gpu_run(w, nsteps=30, precision="f32")
     for o, g in zip(host, got):
         assert (o == g).all()
+
+
+def test_device_state_roundtrip_triangles():
+    import torch
+    import finite_volume_shallow_amd as swe
+    say("[dev] device set/get on a permuted triangle mesh")
+    w = _shuffled_tri(24)
+    desc, keep = swe.desc_from_workload(w)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        dev = [torch.tensor(a, dtype=torch.float64, device="cuda") for a in w.state]
+        z = torch.tensor(w.z, dtype=torch.float64, device="cuda")
+        torch.cuda.synchronize()
+        swe.swe_set_state_device(ctx, z, dev)
+        swe.swe_step(ctx, 20, w.cfl)
+        outs = [torch.empty_like(d) for d in dev]
+        swe.swe_get_state_device(ctx, outs)
+        torch.cuda.synchronize()
+        host = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    got, _, _ = gpu_run(w, nsteps=20)
+    for o, h, g in zip(outs, host, got):
+        assert (o.cpu().numpy() == h).all()
+        assert (h == g).all()
 
 
 def test_error_paths():

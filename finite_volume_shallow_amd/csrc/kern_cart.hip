@@ -27,10 +27,9 @@
 // right/bottom-edge ownership of [MG]'s thread-block kernel.
 //
 // Per cell and row the lane prepares 1/h, sqrt(h) and the velocities once
-// (one reciprocal square root in float32), so an edge costs one reciprocal
-// and one reciprocal square root on top of its arithmetic.  Float32 runs use
-// the hardware reciprocal / square-root approximations (about 1 ulp); the
-// float64 path keeps IEEE division and square root.
+// (one reciprocal square root), so an edge costs one reciprocal and one
+// reciprocal square root on top of its arithmetic (fastmath.hpp: hardware
+// approximations in float32, Newton-refined estimates in float64).
 //
 // dt: each wavefront min-reduces its candidates with shuffles and issues one
 // atomic min (on the IEEE bits of a non-negative double) into one of 64
@@ -74,18 +73,6 @@ template <typename T, bool TR> struct CartArgs {
 
 // ---------------------------------------------------------------- math
 
-template <typename T> struct FM;
-template <> struct FM<float> {
-    static __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-    static __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
-    static __device__ __forceinline__ float sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
-};
-template <> struct FM<double> {
-    static __device__ __forceinline__ double rcp(double x) { return 1.0 / x; }
-    static __device__ __forceinline__ double rsq(double x) { return 1.0 / ::sqrt(x); }
-    static __device__ __forceinline__ double sqrt(double x) { return ::sqrt(x); }
-};
-
 // ---------------------------------------------------------------- lane moves
 // DPP wave shifts: wave_shl:1 gives lane i the value of lane i+1, wave_shr:1
 // the value of lane i-1; the lane without a source (63, resp. 0) reads 0.
@@ -121,15 +108,9 @@ template <typename T> __device__ __forceinline__ PC<T> prep(T h, T qx, T qy, T c
     p.qy = qy;
     p.c = c;
     p.z = z;
-    T ih;
-    if constexpr (sizeof(T) == 4) {
-        const T r = FM<T>::rsq(h);
-        p.s = h * r;
-        ih = r * r;
-    } else {
-        p.s = ::sqrt(h);
-        ih = T(1) / h;
-    }
+    const T r = FM<T>::rsq(h);
+    p.s = h * r;
+    const T ih = r * r;
     p.u = qx * ih;
     p.v = qy * ih;
     p.cc = c * ih;
@@ -343,17 +324,8 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         const T qy1 = prev.qy - f * ay;
         const T c1 = TR ? prev.c - f * ac : T(0);
         // ---- Eq. (5) speeds of W^{n+1}
-        T s1, a1, b1;
-        if constexpr (sizeof(T) == 4) {
-            const T rq = FM<T>::rsq(h1);
-            s1 = h1 * rq;
-            a1 = qx1 * rq;
-            b1 = qy1 * rq;
-        } else {
-            s1 = ::sqrt(h1);
-            a1 = qx1 / s1;
-            b1 = qy1 / s1;
-        }
+        const T rq = FM<T>::rsq(h1);
+        const T s1 = h1 * rq, a1 = qx1 * rq, b1 = qy1 * rq;
         const T Nh = nxt(h1), Ns = nxt(s1), Na = nxt(a1);
         T exs = espeed(h1, s1, a1, Nh, Ns, Na, g);
         if (XW && K.xwall_lane) exs = FM<T>::sqrt(g * (K.colok ? h1 : Nh));

@@ -73,14 +73,135 @@ template <typename T> __device__ __forceinline__ T roe2_speed(const T *L, const 
     return fmax(fabs(hi + m), fabs(lo + m));
 }
 
-template <typename T, int NL, bool TR, bool DT0>
+// Fluctuations of one local edge for its two cells (x/y components, times
+// |G|), from the LDS states.
+// LDS layout of a block: NV state arrays and z ([NV + 1][LCM]), then
+// sqrt(h) and 1/h per layer of every local cell (pre[2 NL][LCM]), then the
+// per-edge fluctuation slots.
+template <typename T, int NL, bool TR, int NV>
+__device__ __forceinline__ void tri_edge_flux(const T *sm, int LCM, int la, int lb, T nx, T ny, T len, T g, T rr,
+                                              T (&Fa)[NV], T (&Fb)[NV], unsigned &bad)
+{
+    const T *pre = sm + (NV + 1) * LCM;
+    if constexpr (NL == 1) {
+        const T ha = sm[la], qxa = sm[LCM + la], qya = sm[2 * LCM + la];
+        const T ca = TR ? sm[3 * LCM + la] : T(0);
+        const T qna = qxa * nx + qya * ny, qta = -qxa * ny + qya * nx;
+        Flux1<T, TR> f;
+        if (lb != 0xFFFF) {
+            const T hb = sm[lb], qxb = sm[LCM + lb], qyb = sm[2 * LCM + lb];
+            const T cb = TR ? sm[3 * LCM + lb] : T(0);
+            const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
+            f = roe1_pre<T, TR>(ha, pre[la], pre[LCM + la], qna, qta, ca, sm[NV * LCM + la], hb, pre[lb],
+                                pre[LCM + lb], qnb, qtb, cb, sm[NV * LCM + lb], g);
+        } else {
+            f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
+        }
+        Fa[0] = len * f.am;
+        Fa[1] = len * (f.an * nx - f.at * ny);
+        Fa[2] = len * (f.an * ny + f.at * nx);
+        Fb[0] = len * f.bm;
+        Fb[1] = len * (f.bn * nx - f.bt * ny);
+        Fb[2] = len * (f.bn * ny + f.bt * nx);
+        if constexpr (TR) {
+            Fa[3] = len * f.ac;
+            Fb[3] = len * f.bc;
+        }
+    } else {
+        T L[6], R[6];
+#pragma unroll
+        for (int l2 = 0; l2 < 2; ++l2) {
+            const T qx = sm[(3 * l2 + 1) * LCM + la], qy = sm[(3 * l2 + 2) * LCM + la];
+            L[3 * l2] = sm[3 * l2 * LCM + la];
+            L[3 * l2 + 1] = qx * nx + qy * ny;
+            L[3 * l2 + 2] = -qx * ny + qy * nx;
+        }
+        Flux2<T> f;
+        if (lb != 0xFFFF) {
+#pragma unroll
+            for (int l2 = 0; l2 < 2; ++l2) {
+                const T qx = sm[(3 * l2 + 1) * LCM + lb], qy = sm[(3 * l2 + 2) * LCM + lb];
+                R[3 * l2] = sm[3 * l2 * LCM + lb];
+                R[3 * l2 + 1] = qx * nx + qy * ny;
+                R[3 * l2 + 2] = -qx * ny + qy * nx;
+            }
+            f = roe2_interior<T>(L, sm[NV * LCM + la], R, sm[NV * LCM + lb], g, rr);
+        } else {
+            f = roe2_wall<T>(L, sm[NV * LCM + la], g, rr);
+        }
+        if (f.nonhyp) bad |= FLAG_NONHYPERBOLIC;
+#pragma unroll
+        for (int l2 = 0; l2 < 2; ++l2) {
+            Fa[3 * l2] = len * f.a[3 * l2];
+            Fa[3 * l2 + 1] = len * (f.a[3 * l2 + 1] * nx - f.a[3 * l2 + 2] * ny);
+            Fa[3 * l2 + 2] = len * (f.a[3 * l2 + 1] * ny + f.a[3 * l2 + 2] * nx);
+            Fb[3 * l2] = len * f.b[3 * l2];
+            Fb[3 * l2 + 1] = len * (f.b[3 * l2 + 1] * nx - f.b[3 * l2 + 2] * ny);
+            Fb[3 * l2 + 2] = len * (f.b[3 * l2 + 1] * ny + f.b[3 * l2 + 2] * nx);
+        }
+    }
+}
+
+// Eq. (5) speed |G| ||D||_inf of a local edge from the LDS states.
+template <typename T, int NL, int NV>
+__device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb, T nx, T ny, T len, T g, T rr,
+                                            unsigned &bad)
+{
+    T sp;
+    if constexpr (NL == 1) {
+        const T *pre = sm + (NV + 1) * LCM;
+        const T ha = sm[la], qna = sm[LCM + la] * nx + sm[2 * LCM + la] * ny;
+        if (lb != 0xFFFF) {
+            const T hb = sm[lb], qnb = sm[LCM + lb] * nx + sm[2 * LCM + lb] * ny;
+            const T sa = pre[la], sb = pre[lb];
+            // u_Roe = (sa ua + sb ub) / (sa + sb), s u = qn sqrt(h) / h
+            const T ubar = (qna * sa * pre[LCM + la] + qnb * sb * pre[LCM + lb]) * FM<T>::rcp(sa + sb);
+            sp = fabs(ubar) + FM<T>::sqrt(g * T(0.5) * (ha + hb));
+        } else {
+            sp = FM<T>::sqrt(g * ha);
+        }
+    } else {
+        T L[6], R[6];
+#pragma unroll
+        for (int l2 = 0; l2 < 2; ++l2) {
+            L[3 * l2] = sm[3 * l2 * LCM + la];
+            L[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + la] * nx + sm[(3 * l2 + 2) * LCM + la] * ny;
+            L[3 * l2 + 2] = T(0);
+        }
+        if (lb != 0xFFFF) {
+#pragma unroll
+            for (int l2 = 0; l2 < 2; ++l2) {
+                R[3 * l2] = sm[3 * l2 * LCM + lb];
+                R[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + lb] * nx + sm[(3 * l2 + 2) * LCM + lb] * ny;
+                R[3 * l2 + 2] = T(0);
+            }
+        } else { // mirror state
+            R[0] = L[0];
+            R[1] = -L[1];
+            R[3] = L[3];
+            R[4] = -L[4];
+            R[2] = R[5] = T(0);
+        }
+        bool nh2 = false;
+        sp = roe2_speed<T>(L, R, g, rr, nh2);
+        if (nh2) bad |= FLAG_NONHYPERBOLIC;
+    }
+    return len * sp;
+}
+
+// RD: rounds of 256 threads covering the largest local cell / edge / slot
+// counts of any block.  Every global load a thread will need in the launch
+// (halo ids, its edges' geometry, its cells' slot lists and 1/|V|) is issued
+// at the start, so the phases after the first barrier only touch LDS.
+template <typename T, int NL, bool TR, bool DT0, int RD>
 __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
     extern __shared__ double smem_d[];
     T *sm = reinterpret_cast<T *>(smem_d);
     const int LCM = A.lc_max, EM = A.e_max;
-    T *fl = sm + (NV + 1) * LCM; // fluctuation slots: side s, var v at fl[(s * NV + v) * EM + e]
+    T *pre = sm + (NV + 1) * LCM;          // sqrt(h), 1/h per layer: pre[(2 k + 0/1) LCM + l]
+    T *fl = pre + 2 * NL * LCM;            // fluctuation slots: side s, var v at fl[(s * NV + v) * EM + e]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = blockIdx.x;
@@ -106,172 +227,131 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
     const int LC = B0 + nh;
     const int e0 = A.edge_off[blk], ne = A.edge_off[blk + 1] - e0, es0 = A.e_s0[blk];
     const int s0 = A.slot_off[blk];
+    const int nc = B0 + n1; // cells updated (block + ring 1)
     const T g = A.g, rr = A.r;
     unsigned bad = 0;
 
-    // 1. W^n and z of the block and its two rings
-    for (int l = tid; l < LC; l += TRI_THREADS) {
-        const int64_t gid = l < B0 ? base + l : (int64_t)A.halo_ids[h0 + l - B0];
+    // ---- all global reads of the launch, issued up front
+    int64_t gid[RD];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) sm[v * LCM + l] = A.in[v][gid];
-        sm[NV * LCM + l] = A.z[gid];
+    for (int m = 0; m < RD; ++m) {
+        const int l = tid + m * TRI_THREADS;
+        gid[m] = l < B0 ? base + l : (l < LC ? (int64_t)A.halo_ids[h0 + l - B0] : -1);
+    }
+    uint32_t eab[RD];
+    T enx[RD], eny[RD], elen[RD];
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+        const int k = tid + m * TRI_THREADS;
+        const bool ok = DT0 ? k < es0 : k < ne;
+        eab[m] = ok ? A.e_ab[e0 + k] : 0u;
+        enx[m] = ok ? A.e_nx[e0 + k] : T(0);
+        eny[m] = ok ? A.e_ny[e0 + k] : T(0);
+        elen[m] = ok ? A.e_len[e0 + k] : T(0);
+    }
+    uint16_t csl[RD][3];
+    T cia[RD];
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+        const int l = tid + m * TRI_THREADS;
+        const bool ok = l < nc;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) csl[m][j] = ok ? A.slots[3 * (s0 + l) + j] : (uint16_t)0;
+        cia[m] = ok ? A.iarea[s0 + l] : T(0);
+    }
+
+    // ---- 1. W^n and z of the block and its two rings into LDS
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+        const int l = tid + m * TRI_THREADS;
+        if (gid[m] >= 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) sm[v * LCM + l] = A.in[v][gid[m]];
+            sm[NV * LCM + l] = A.z[gid[m]];
+            if (NL == 1) {
+                const T rq = FM<T>::rsq(sm[l]);
+                pre[l] = sm[l] * rq;
+                pre[LCM + l] = rq * rq;
+            }
+        }
     }
     __syncthreads();
 
     if (!DT0) {
-        // 2. every edge touching the block or ring 1, once
-        for (int k = tid; k < ne; k += TRI_THREADS) {
-            const uint32_t ab = A.e_ab[e0 + k];
-            const int la = (int)(ab & 0xFFFFu), lb = (int)(ab >> 16);
-            const T nx = A.e_nx[e0 + k], ny = A.e_ny[e0 + k], len = A.e_len[e0 + k];
-            T Fa[NV], Fb[NV];
-            if constexpr (NL == 1) {
-                const T ha = sm[la], qxa = sm[LCM + la], qya = sm[2 * LCM + la];
-                const T ca = TR ? sm[3 * LCM + la] : T(0);
-                const T qna = qxa * nx + qya * ny, qta = -qxa * ny + qya * nx;
-                Flux1<T, TR> f;
-                if (lb != 0xFFFF) {
-                    const T hb = sm[lb], qxb = sm[LCM + lb], qyb = sm[2 * LCM + lb];
-                    const T cb = TR ? sm[3 * LCM + lb] : T(0);
-                    const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-                    f = roe1_interior<T, TR>(ha, qna, qta, ca, sm[NV * LCM + la], hb, qnb, qtb, cb,
-                                             sm[NV * LCM + lb], g);
-                } else {
-                    f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
-                }
-                Fa[0] = len * f.am;
-                Fa[1] = len * (f.an * nx - f.at * ny);
-                Fa[2] = len * (f.an * ny + f.at * nx);
-                Fb[0] = len * f.bm;
-                Fb[1] = len * (f.bn * nx - f.bt * ny);
-                Fb[2] = len * (f.bn * ny + f.bt * nx);
-                if constexpr (TR) {
-                    Fa[3] = len * f.ac;
-                    Fb[3] = len * f.bc;
-                }
-            } else {
-                T L[6], R[6];
+        // ---- 2. every edge touching the block or ring 1, once
 #pragma unroll
-                for (int l2 = 0; l2 < 2; ++l2) {
-                    const T qx = sm[(3 * l2 + 1) * LCM + la], qy = sm[(3 * l2 + 2) * LCM + la];
-                    L[3 * l2] = sm[3 * l2 * LCM + la];
-                    L[3 * l2 + 1] = qx * nx + qy * ny;
-                    L[3 * l2 + 2] = -qx * ny + qy * nx;
-                }
-                Flux2<T> f;
-                if (lb != 0xFFFF) {
+        for (int m = 0; m < RD; ++m) {
+            const int k = tid + m * TRI_THREADS;
+            if (k < ne) {
+                T Fa[NV], Fb[NV];
+                tri_edge_flux<T, NL, TR, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
+                                             eny[m], elen[m], g, rr, Fa, Fb, bad);
 #pragma unroll
-                    for (int l2 = 0; l2 < 2; ++l2) {
-                        const T qx = sm[(3 * l2 + 1) * LCM + lb], qy = sm[(3 * l2 + 2) * LCM + lb];
-                        R[3 * l2] = sm[3 * l2 * LCM + lb];
-                        R[3 * l2 + 1] = qx * nx + qy * ny;
-                        R[3 * l2 + 2] = -qx * ny + qy * nx;
-                    }
-                    f = roe2_interior<T>(L, sm[NV * LCM + la], R, sm[NV * LCM + lb], g, rr);
-                } else {
-                    f = roe2_wall<T>(L, sm[NV * LCM + la], g, rr);
+                for (int v = 0; v < NV; ++v) {
+                    fl[v * EM + k] = Fa[v];
+                    fl[(NV + v) * EM + k] = Fb[v];
                 }
-                if (f.nonhyp) bad |= FLAG_NONHYPERBOLIC;
-#pragma unroll
-                for (int l2 = 0; l2 < 2; ++l2) {
-                    Fa[3 * l2] = len * f.a[3 * l2];
-                    Fa[3 * l2 + 1] = len * (f.a[3 * l2 + 1] * nx - f.a[3 * l2 + 2] * ny);
-                    Fa[3 * l2 + 2] = len * (f.a[3 * l2 + 1] * ny + f.a[3 * l2 + 2] * nx);
-                    Fb[3 * l2] = len * f.b[3 * l2];
-                    Fb[3 * l2 + 1] = len * (f.b[3 * l2 + 1] * nx - f.b[3 * l2 + 2] * ny);
-                    Fb[3 * l2 + 2] = len * (f.b[3 * l2 + 1] * ny + f.b[3 * l2 + 2] * nx);
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                fl[v * EM + k] = Fa[v];
-                fl[(NV + v) * EM + k] = Fb[v];
             }
         }
         __syncthreads();
 
-        // 3. W^{n+1} of the block and ring 1, gathered in a fixed order
-        for (int l = tid; l < B0 + n1; l += TRI_THREADS) {
-            T acc[NV];
+        // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
 #pragma unroll
-            for (int v = 0; v < NV; ++v) acc[v] = T(0);
+        for (int m = 0; m < RD; ++m) {
+            const int l = tid + m * TRI_THREADS;
+            if (l < nc) {
+                T acc[NV];
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int sl = A.slots[3 * (s0 + l) + j];
-                const int e = sl >> 1, side = sl & 1;
+                for (int v = 0; v < NV; ++v) acc[v] = T(0);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) acc[v] += fl[(side * NV + v) * EM + e];
+                for (int j = 0; j < 3; ++j) {
+                    const int e = csl[m][j] >> 1, side = csl[m][j] & 1;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) acc[v] += fl[(side * NV + v) * EM + e];
+                }
+                const T fct = (T)dtd * cia[m];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) sm[v * LCM + l] -= fct * acc[v];
+                if (NL == 1) {
+                    const T rq = FM<T>::rsq(sm[l]);
+                    pre[l] = sm[l] * rq;
+                    pre[LCM + l] = rq * rq;
+                }
             }
-            const T fct = (T)dtd * A.iarea[s0 + l];
-#pragma unroll
-            for (int v = 0; v < NV; ++v) sm[v * LCM + l] -= fct * acc[v];
         }
         __syncthreads();
     }
 
-    // 4. Eq. (5) speeds on the edges touching the block (of W^{n+1}, or of
-    // W^0 for the prologue), parked in the first slot array
-    for (int k = tid; k < es0; k += TRI_THREADS) {
-        const uint32_t ab = A.e_ab[e0 + k];
-        const int la = (int)(ab & 0xFFFFu), lb = (int)(ab >> 16);
-        const T nx = A.e_nx[e0 + k], ny = A.e_ny[e0 + k], len = A.e_len[e0 + k];
-        T sp;
-        if constexpr (NL == 1) {
-            const T ha = sm[la], qna = sm[LCM + la] * nx + sm[2 * LCM + la] * ny;
-            if (lb != 0xFFFF) {
-                const T hb = sm[lb], qnb = sm[LCM + lb] * nx + sm[2 * LCM + lb] * ny;
-                const T sa = sqrt(ha), sb = sqrt(hb);
-                sp = fabs((qna / sa + qnb / sb) / (sa + sb)) + sqrt(g * T(0.5) * (ha + hb));
-            } else {
-                sp = sqrt(g * ha);
-            }
-        } else {
-            T L[6], R[6];
+    // ---- 4. Eq. (5) speeds on the edges touching the block (of W^{n+1}, or
+    // of W^0 for the prologue), parked in the first slot array
 #pragma unroll
-            for (int l2 = 0; l2 < 2; ++l2) {
-                L[3 * l2] = sm[3 * l2 * LCM + la];
-                L[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + la] * nx + sm[(3 * l2 + 2) * LCM + la] * ny;
-                L[3 * l2 + 2] = T(0);
-            }
-            if (lb != 0xFFFF) {
-#pragma unroll
-                for (int l2 = 0; l2 < 2; ++l2) {
-                    R[3 * l2] = sm[3 * l2 * LCM + lb];
-                    R[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + lb] * nx + sm[(3 * l2 + 2) * LCM + lb] * ny;
-                    R[3 * l2 + 2] = T(0);
-                }
-            } else { // mirror state
-                R[0] = L[0];
-                R[1] = -L[1];
-                R[3] = L[3];
-                R[4] = -L[4];
-                R[2] = R[5] = T(0);
-            }
-            bool nh2 = false;
-            sp = roe2_speed<T>(L, R, g, rr, nh2);
-            if (nh2) bad |= FLAG_NONHYPERBOLIC;
-        }
-        fl[k] = len * sp;
+    for (int m = 0; m < RD; ++m) {
+        const int k = tid + m * TRI_THREADS;
+        if (k < es0)
+            fl[k] = tri_edge_speed<T, NL, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
+                                              eny[m], elen[m], g, rr, bad);
     }
     __syncthreads();
 
-    // 5. dt candidates of the block cells, W^{n+1} out
+    // ---- 5. dt candidates of the block cells, W^{n+1} out
     double cand = __builtin_inf();
-    for (int l = tid; l < B0; l += TRI_THREADS) {
-        T S = T(0);
 #pragma unroll
-        for (int j = 0; j < 3; ++j) S += fl[A.slots[3 * (s0 + l) + j] >> 1];
-        cand = fmin(cand, (double)(T(2) * A.cfl / (A.iarea[s0 + l] * S)));
-        if (!DT0) {
-            bool badv = false;
+    for (int m = 0; m < RD; ++m) {
+        const int l = tid + m * TRI_THREADS;
+        if (l < B0) {
+            const T S = fl[csl[m][0] >> 1] + fl[csl[m][1] >> 1] + fl[csl[m][2] >> 1];
+            cand = fmin(cand, (double)(T(2) * A.cfl / (cia[m] * S)));
+            if (!DT0) {
+                bool badv = false;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const T x = sm[v * LCM + l];
-                A.out[v][base + l] = x;
-                badv |= !isfinite(x);
+                for (int v = 0; v < NV; ++v) {
+                    const T x = sm[v * LCM + l];
+                    A.out[v][base + l] = x;
+                    badv |= !isfinite(x);
+                }
+                if (!(sm[l] > T(0)) || (NL == 2 && !(sm[3 * LCM + l] > T(0)))) bad |= FLAG_DEPTH;
+                if (badv) bad |= FLAG_NONFINITE;
             }
-            if (!(sm[l] > T(0)) || (NL == 2 && !(sm[3 * LCM + l] > T(0)))) bad |= FLAG_DEPTH;
-            if (badv) bad |= FLAG_NONFINITE;
         }
     }
     const int slot_bank = DT0 ? 0 : (bank + 1) % 3;
@@ -348,17 +428,27 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     return A;
 }
 
-template <typename T, int NL, bool TR> static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
+template <typename T, int NL, bool TR, int RD>
+static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
-    const size_t lds = ((size_t)(NV + 1) * c->tb.lc_max + (size_t)2 * NV * c->tb.e_max) * sizeof(T);
+    const size_t lds = tri_lds_bytes(NV, sizeof(T), c->tb.lc_max, c->tb.e_max);
     const int per_xcd = (c->tb.nblocks + TRI_XCD - 1) / TRI_XCD;
     const dim3 grid((unsigned)(per_xcd * TRI_XCD)), block(TRI_THREADS);
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
-    hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true>), grid, block, lds, c->stream, tri_args<T>(c, 0, cfl));
+    hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD>), grid, block, lds, c->stream, tri_args<T>(c, 0, cfl));
     for (int64_t s = 0; s < nsteps; ++s)
-        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false>), grid, block, lds, c->stream, tri_args<T>(c, s, cfl));
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD>), grid, block, lds, c->stream,
+                           tri_args<T>(c, s, cfl));
     return hipGetLastError();
+}
+
+template <typename T, int NL, bool TR> static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    // rounds of 256 threads that cover the largest block (checked at create)
+    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1>(c, nsteps, cfl);
+    if (c->tb.rounds == 2) return tri_batch_rd<T, NL, TR, 2>(c, nsteps, cfl);
+    return tri_batch_rd<T, NL, TR, 3>(c, nsteps, cfl);
 }
 
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
@@ -372,29 +462,8 @@ hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
 // LDS bytes a block size needs (for choosing B and the launch attribute)
 size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max)
 {
-    return ((size_t)(nv + 1) * lc_max + (size_t)2 * nv * e_max) * rs;
-}
-
-hipError_t tri_set_lds_limit(swe_ctx *c, size_t bytes)
-{
-    hipError_t e = hipSuccess;
-    auto setf = [&](const void *f) {
-        hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-        if (r != hipSuccess) e = r;
-    };
-    setf((const void *)k_tri_fused<double, 1, false, true>);
-    setf((const void *)k_tri_fused<double, 1, false, false>);
-    setf((const void *)k_tri_fused<double, 1, true, true>);
-    setf((const void *)k_tri_fused<double, 1, true, false>);
-    setf((const void *)k_tri_fused<double, 2, false, true>);
-    setf((const void *)k_tri_fused<double, 2, false, false>);
-    setf((const void *)k_tri_fused<float, 1, false, true>);
-    setf((const void *)k_tri_fused<float, 1, false, false>);
-    setf((const void *)k_tri_fused<float, 1, true, true>);
-    setf((const void *)k_tri_fused<float, 1, true, false>);
-    setf((const void *)k_tri_fused<float, 2, false, true>);
-    setf((const void *)k_tri_fused<float, 2, false, false>);
-    return e;
+    const int nl = nv == 6 ? 2 : 1;
+    return ((size_t)(nv + 1 + 2 * nl) * lc_max + (size_t)2 * nv * e_max) * rs;
 }
 
 } // namespace swe

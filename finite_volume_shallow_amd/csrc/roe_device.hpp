@@ -31,9 +31,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fastmath.hpp"
+
 namespace swe {
 
-template <typename T> __device__ __forceinline__ T rcp(T x) { return T(1) / x; }
+template <typename T> __device__ __forceinline__ T rcp(T x) { return FM<T>::rcp(x); }
 
 template <typename T> struct Eps;
 template <> struct Eps<double> { static constexpr double v = 2.220446049250313e-16; };
@@ -55,22 +57,23 @@ template <typename T, bool TRACER> struct Flux1 {
     T speed;
 };
 
+// As roe1_interior, with sqrt(h) and 1/h of both cells supplied.
 template <typename T, bool TRACER>
-__device__ __forceinline__ Flux1<T, TRACER> roe1_interior(T hL, T qnL, T qtL, T cL, T zL,
-                                                           T hR, T qnR, T qtR, T cR, T zR, T g)
+__device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T qtL, T cL, T zL, T hR, T sR,
+                                                      T ihR, T qnR, T qtR, T cR, T zR, T g)
 {
     Flux1<T, TRACER> o;
-    const T ihL = rcp(hL), ihR = rcp(hR);
     const T uL = qnL * ihL, uR = qnR * ihR;
-    const T sL = sqrt(hL), sR = sqrt(hR);
     const T ubar = (sL * uL + sR * uR) * rcp(sL + sR);
     const T hbar = T(0.5) * (hL + hR);
-    const T c = sqrt(g * hbar);
+    const T c2 = g * hbar;
+    const T irc = FM<T>::rsq(c2);
+    const T c = c2 * irc;
     const T lam1 = ubar - c, lam2 = ubar + c;
     // X = (dqn, d(qn u) + g hbar (dh + dz)); g/2 (hR^2 - hL^2) = g hbar dh.
     const T X0 = qnR - qnL;
-    const T X1 = (qnR * uR - qnL * uL) + g * hbar * ((hR - hL) + (zR - zL));
-    const T i2c = T(0.5) * rcp(c);
+    const T X1 = (qnR * uR - qnL * uL) + c2 * ((hR - hL) + (zR - zL));
+    const T i2c = T(0.5) * irc;
     const T a1 = (lam2 * X0 - X1) * i2c;
     const T a2 = (X1 - lam1 * X0) * i2c;
     const T w1 = wminus(lam1), w2 = wminus(lam2);
@@ -106,12 +109,20 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_interior(T hL, T qnL, T qtL, T 
     return o;
 }
 
+template <typename T, bool TRACER>
+__device__ __forceinline__ Flux1<T, TRACER> roe1_interior(T hL, T qnL, T qtL, T cL, T zL,
+                                                           T hR, T qnR, T qtR, T cR, T zR, T g)
+{
+    const T rL = FM<T>::rsq(hL), rR = FM<T>::rsq(hR);
+    return roe1_pre<T, TRACER>(hL, hL * rL, rL * rL, qnL, qtL, cL, zL, hR, hR * rR, rR * rR, qnR, qtR, cR, zR, g);
+}
+
 // One-layer reflective wall seen from side a.
 template <typename T, bool TRACER>
 __device__ __forceinline__ Flux1<T, TRACER> roe1_wall(T h, T qn, T qt, T hc, T g)
 {
     Flux1<T, TRACER> o;
-    const T c = sqrt(g * h);
+    const T c = FM<T>::sqrt(g * h);
     const T ih = rcp(h);
     o.am = -qn;
     o.an = c * qn;
@@ -171,7 +182,7 @@ __device__ __forceinline__ T newton_outer(T mu, T d1, T d2, T c1, T c2, T rc)
         const T f = quartic_q(mu, d1, d2, c1, c2, rc);
         const T df = quartic_dq(mu, d1, d2, c1, c2);
         if (df == T(0)) break;
-        const T step = f / df;
+        const T step = f * rcp(df);
         mu -= step;
         if (fabs(step) <= T(4) * Eps<T>::v * fabs(mu) || !(fabs(step) > T(0))) break;
     }
@@ -183,7 +194,7 @@ __device__ __forceinline__ T newton_polish(T mu, T d1, T d2, T c1, T c2, T rc)
 {
     for (int it = 0; it < 3; ++it) {
         const T df = quartic_dq(mu, d1, d2, c1, c2);
-        if (df != T(0)) mu -= quartic_q(mu, d1, d2, c1, c2, rc) / df;
+        if (df != T(0)) mu -= quartic_q(mu, d1, d2, c1, c2, rc) * rcp(df);
     }
     return mu;
 }
@@ -198,7 +209,7 @@ __device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, 
     const T h1R = R[0], q1R = R[1], t1R = R[2], h2R = R[3], q2R = R[4], t2R = R[5];
     const T i1L = rcp(h1L), i1R = rcp(h1R), i2L = rcp(h2L), i2R = rcp(h2R);
     const T v1L = q1L * i1L, v1R = q1R * i1R, v2L = q2L * i2L, v2R = q2R * i2R;
-    const T s1L = sqrt(h1L), s1R = sqrt(h1R), s2L = sqrt(h2L), s2R = sqrt(h2R);
+    const T s1L = FM<T>::sqrt(h1L), s1R = FM<T>::sqrt(h1R), s2L = FM<T>::sqrt(h2L), s2R = FM<T>::sqrt(h2R);
     const T u1 = (s1L * v1L + s1R * v1R) * rcp(s1L + s1R);
     const T u2 = (s2L * v2L + s2R * v2R) * rcp(s2L + s2R);
     const T c1 = g * T(0.5) * (h1L + h1R); // c1^2
@@ -216,7 +227,7 @@ __device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, 
     // eigenvalues in the shifted variable mu = lambda - m
     const T m = T(0.5) * (u1 + u2);
     const T d1 = u1 - m, d2 = u2 - m;
-    const T bound = sqrt(c1 + c2);
+    const T bound = FM<T>::sqrt(c1 + c2);
     const T muhi = newton_outer(fmax(d1, d2) + bound, d1, d2, c1, c2, rc);
     const T mulo = newton_outer(fmin(d1, d2) - bound, d1, d2, c1, c2, rc);
     // Q(mu) = mu^4 + a3 mu^3 + a2 mu^2 + a1 mu + a0; divide by (mu-muhi)(mu-mulo)
@@ -231,7 +242,7 @@ __device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, 
         o.nonhyp = true;
         disc = T(0);
     }
-    const T sq = sqrt(disc);
+    const T sq = disc > T(0) ? FM<T>::sqrt(disc) : T(0);
     T mid1 = T(-0.5) * (b1 + sq), mid2 = T(-0.5) * (b1 - sq);
     mid1 = newton_polish(mid1, d1, d2, c1, c2, rc);
     mid2 = newton_polish(mid2, d1, d2, c1, c2, rc);
@@ -247,9 +258,9 @@ __device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, 
         const T tau = e2 * e2 - c2;
         const T dq = T(2) * (tau * e1 + rho * e2);
         const T lx = (l - T(2) * u1) * tau * X[0] + tau * X[1] + (l - T(2) * u2) * c1 * X[2] + c1 * X[3];
-        const T alpha = lx / dq;
+        const T alpha = lx * rcp(dq);
         const T w = wminus(l);
-        const T sgm = rho / c1;
+        const T sgm = rho * rcp(c1);
         PX[0] += w * alpha;
         PX[1] += w * alpha * l;
         PX[2] += w * alpha * sgm;

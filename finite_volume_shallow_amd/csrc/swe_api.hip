@@ -1,6 +1,7 @@
 // C ABI of the shallow-water step library (see include/swe.h).
 #include <cmath>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -140,6 +141,9 @@ template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
     };
     c->tb.B = hb.B;
     c->tb.nblocks = hb.nblocks;
+    int upd_max = 0;
+    for (int b = 0; b < hb.nblocks; ++b) upd_max = std::max(upd_max, hb.slot_off[b + 1] - hb.slot_off[b]);
+    c->tb.rounds = (std::max(std::max(hb.lc_max, hb.e_max), upd_max) + 255) / 256;
     c->tb.lc_max = hb.lc_max;
     c->tb.e_max = hb.e_max;
     c->tb.halo_off = ints(hb.halo_off);
@@ -278,7 +282,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= 65536 || B <= 32) break;
                 B /= 2;
             }
-            if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) > 65536) {
+            if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) > 65536 || hb.lc_max > 768 || hb.e_max > 768) {
                 c->err = "triangle blocks do not fit in LDS (mesh too irregular); use SWE_PATH_EDGE";
                 throw Fail{SWE_E_INVAL};
             }

@@ -52,17 +52,18 @@ template <typename T> struct TriArgs {
 };
 
 // Largest |eigenvalue| of the two-layer Roe matrix (the outer roots of the
-// quartic, see roe_device.hpp), edge-frame states L, R.
-template <typename T> __device__ __forceinline__ T roe2_speed(const T *L, const T *R, T g, T r, bool &nonhyp)
+// quartic, see roe_device.hpp), edge-frame states L, R with their per-cell
+// sqrt(h_k), 1/h_k in pL, pR.
+template <typename T>
+__device__ __forceinline__ T roe2_speed(const T *L, const T *pL, const T *R, const T *pR, T g, T r, bool &nonhyp)
 {
-    const T s1L = sqrt(L[0]), s1R = sqrt(R[0]), s2L = sqrt(L[3]), s2R = sqrt(R[3]);
-    const T u1 = (L[1] / s1L + R[1] / s1R) / (s1L + s1R);
-    const T u2 = (L[4] / s2L + R[4] / s2R) / (s2L + s2R);
+    const T u1 = (L[1] * pL[1] * pL[0] + R[1] * pR[1] * pR[0]) * FM<T>::rcp(pL[0] + pR[0]);
+    const T u2 = (L[4] * pL[3] * pL[2] + R[4] * pR[3] * pR[2]) * FM<T>::rcp(pL[2] + pR[2]);
     const T c1 = g * T(0.5) * (L[0] + R[0]);
     const T c2 = g * T(0.5) * (L[3] + R[3]);
     const T rc = r * c1 * c2;
     const T m = T(0.5) * (u1 + u2), d1 = u1 - m, d2 = u2 - m;
-    const T bound = sqrt(c1 + c2);
+    const T bound = FM<T>::sqrt(c1 + c2);
     const T hi = newton_outer(fmax(d1, d2) + bound, d1, d2, c1, c2, rc);
     const T lo = newton_outer(fmin(d1, d2) - bound, d1, d2, c1, c2, rc);
     // inner pair real?  (deflated quadratic discriminant)
@@ -73,10 +74,23 @@ template <typename T> __device__ __forceinline__ T roe2_speed(const T *L, const 
     return fmax(fabs(hi + m), fabs(lo + m));
 }
 
-// Fluctuations of one local edge for its two cells (x/y components, times
-// |G|), from the LDS states.
-// LDS layout of a block: NV state arrays and z ([NV + 1][LCM]), then
-// sqrt(h) and 1/h per layer of every local cell (pre[2 NL][LCM]), then the
+// sqrt(h) and 1/h of local cell l into pre[l], pre[LCM + l] (one layer; the
+// two-layer path keeps its LDS for occupancy and forms them per edge)
+template <typename T, int NL, int NV>
+__device__ __forceinline__ void tri_cellpre(const T *sm, T *pre, int LCM, int l)
+{
+    if (NL != 1) return;
+#pragma unroll
+    for (int k = 0; k < 1; ++k) {
+        const T h = sm[3 * k * LCM + l];
+        const T rq = FM<T>::rsq(h);
+        pre[2 * k * LCM + l] = h * rq;
+        pre[(2 * k + 1) * LCM + l] = rq * rq;
+    }
+}
+
+// LDS layout of a block: NV state arrays and z ([NV + 1][LCM]), then (one
+// layer) sqrt(h) and 1/h of every local cell (pre[2][LCM]), then the
 // per-edge fluctuation slots.
 template <typename T, int NL, bool TR, int NV>
 __device__ __forceinline__ void tri_edge_flux(const T *sm, int LCM, int la, int lb, T nx, T ny, T len, T g, T rr,
@@ -168,6 +182,8 @@ __device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb
             L[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + la] * nx + sm[(3 * l2 + 2) * LCM + la] * ny;
             L[3 * l2 + 2] = T(0);
         }
+        T pa[4], pb[4];
+        roe2_cellpre(L, pa);
         if (lb != 0xFFFF) {
 #pragma unroll
             for (int l2 = 0; l2 < 2; ++l2) {
@@ -175,15 +191,18 @@ __device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb
                 R[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + lb] * nx + sm[(3 * l2 + 2) * LCM + lb] * ny;
                 R[3 * l2 + 2] = T(0);
             }
+            roe2_cellpre(R, pb);
         } else { // mirror state
             R[0] = L[0];
             R[1] = -L[1];
             R[3] = L[3];
             R[4] = -L[4];
             R[2] = R[5] = T(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pb[q] = pa[q];
         }
         bool nh2 = false;
-        sp = roe2_speed<T>(L, R, g, rr, nh2);
+        sp = roe2_speed<T>(L, pa, R, pb, g, rr, nh2);
         if (nh2) bad |= FLAG_NONHYPERBOLIC;
     }
     return len * sp;
@@ -193,15 +212,15 @@ __device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb
 // counts of any block.  Every global load a thread will need in the launch
 // (halo ids, its edges' geometry, its cells' slot lists and 1/|V|) is issued
 // at the start, so the phases after the first barrier only touch LDS.
-template <typename T, int NL, bool TR, bool DT0, int RD>
-__global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
+template <typename T, int NL, bool TR, bool DT0, int RD, int NT>
+__global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
     extern __shared__ double smem_d[];
     T *sm = reinterpret_cast<T *>(smem_d);
     const int LCM = A.lc_max, EM = A.e_max;
-    T *pre = sm + (NV + 1) * LCM;          // sqrt(h), 1/h per layer: pre[(2 k + 0/1) LCM + l]
-    T *fl = pre + 2 * NL * LCM;            // fluctuation slots: side s, var v at fl[(s * NV + v) * EM + e]
+    T *pre = sm + (NV + 1) * LCM;          // one layer: sqrt(h), 1/h at pre[l], pre[LCM + l]
+    T *fl = pre + (NL == 1 ? 2 : 0) * LCM; // fluctuation slots: side s, var v at fl[(s * NV + v) * EM + e]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = blockIdx.x;
@@ -235,14 +254,14 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
     int64_t gid[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int l = tid + m * TRI_THREADS;
+        const int l = tid + m * NT;
         gid[m] = l < B0 ? base + l : (l < LC ? (int64_t)A.halo_ids[h0 + l - B0] : -1);
     }
     uint32_t eab[RD];
     T enx[RD], eny[RD], elen[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int k = tid + m * TRI_THREADS;
+        const int k = tid + m * NT;
         const bool ok = DT0 ? k < es0 : k < ne;
         eab[m] = ok ? A.e_ab[e0 + k] : 0u;
         enx[m] = ok ? A.e_nx[e0 + k] : T(0);
@@ -253,7 +272,7 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
     T cia[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int l = tid + m * TRI_THREADS;
+        const int l = tid + m * NT;
         const bool ok = l < nc;
 #pragma unroll
         for (int j = 0; j < 3; ++j) csl[m][j] = ok ? A.slots[3 * (s0 + l) + j] : (uint16_t)0;
@@ -263,16 +282,12 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
     // ---- 1. W^n and z of the block and its two rings into LDS
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int l = tid + m * TRI_THREADS;
+        const int l = tid + m * NT;
         if (gid[m] >= 0) {
 #pragma unroll
             for (int v = 0; v < NV; ++v) sm[v * LCM + l] = A.in[v][gid[m]];
             sm[NV * LCM + l] = A.z[gid[m]];
-            if (NL == 1) {
-                const T rq = FM<T>::rsq(sm[l]);
-                pre[l] = sm[l] * rq;
-                pre[LCM + l] = rq * rq;
-            }
+            tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
         }
     }
     __syncthreads();
@@ -281,7 +296,7 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
         // ---- 2. every edge touching the block or ring 1, once
 #pragma unroll
         for (int m = 0; m < RD; ++m) {
-            const int k = tid + m * TRI_THREADS;
+            const int k = tid + m * NT;
             if (k < ne) {
                 T Fa[NV], Fb[NV];
                 tri_edge_flux<T, NL, TR, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
@@ -298,7 +313,7 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
         // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
 #pragma unroll
         for (int m = 0; m < RD; ++m) {
-            const int l = tid + m * TRI_THREADS;
+            const int l = tid + m * NT;
             if (l < nc) {
                 T acc[NV];
 #pragma unroll
@@ -312,11 +327,7 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
                 const T fct = (T)dtd * cia[m];
 #pragma unroll
                 for (int v = 0; v < NV; ++v) sm[v * LCM + l] -= fct * acc[v];
-                if (NL == 1) {
-                    const T rq = FM<T>::rsq(sm[l]);
-                    pre[l] = sm[l] * rq;
-                    pre[LCM + l] = rq * rq;
-                }
+                tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
             }
         }
         __syncthreads();
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
     // of W^0 for the prologue), parked in the first slot array
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int k = tid + m * TRI_THREADS;
+        const int k = tid + m * NT;
         if (k < es0)
             fl[k] = tri_edge_speed<T, NL, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
                                               eny[m], elen[m], g, rr, bad);
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(TRI_THREADS) void k_tri_fused(TriArgs<T> A)
     double cand = __builtin_inf();
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int l = tid + m * TRI_THREADS;
+        const int l = tid + m * NT;
         if (l < B0) {
             const T S = fl[csl[m][0] >> 1] + fl[csl[m][1] >> 1] + fl[csl[m][2] >> 1];
             cand = fmin(cand, (double)(T(2) * A.cfl / (cia[m] * S)));
@@ -428,27 +439,30 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     return A;
 }
 
-template <typename T, int NL, bool TR, int RD>
+template <typename T, int NL, bool TR, int RD, int NT>
 static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
     const size_t lds = tri_lds_bytes(NV, sizeof(T), c->tb.lc_max, c->tb.e_max);
     const int per_xcd = (c->tb.nblocks + TRI_XCD - 1) / TRI_XCD;
-    const dim3 grid((unsigned)(per_xcd * TRI_XCD)), block(TRI_THREADS);
+    const dim3 grid((unsigned)(per_xcd * TRI_XCD)), block(NT);
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
-    hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD>), grid, block, lds, c->stream, tri_args<T>(c, 0, cfl));
+    hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
+                       tri_args<T>(c, 0, cfl));
     for (int64_t s = 0; s < nsteps; ++s)
-        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD>), grid, block, lds, c->stream,
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT>), grid, block, lds, c->stream,
                            tri_args<T>(c, s, cfl));
     return hipGetLastError();
 }
 
 template <typename T, int NL, bool TR> static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
-    // rounds of 256 threads that cover the largest block (checked at create)
-    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1>(c, nsteps, cfl);
-    if (c->tb.rounds == 2) return tri_batch_rd<T, NL, TR, 2>(c, nsteps, cfl);
-    return tri_batch_rd<T, NL, TR, 3>(c, nsteps, cfl);
+    // 256 threads per workgroup (four wavefronts keep the CU busy across
+    // the barriers even for 128-cell blocks); rounds of 256 cover the
+    // largest local cell / edge / update counts (checked at create)
+    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 256>(c, nsteps, cfl);
+    if (c->tb.rounds <= 2) return tri_batch_rd<T, NL, TR, 2, 256>(c, nsteps, cfl);
+    return tri_batch_rd<T, NL, TR, 3, 256>(c, nsteps, cfl);
 }
 
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
@@ -462,8 +476,8 @@ hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
 // LDS bytes a block size needs (for choosing B and the launch attribute)
 size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max)
 {
-    const int nl = nv == 6 ? 2 : 1;
-    return ((size_t)(nv + 1 + 2 * nl) * lc_max + (size_t)2 * nv * e_max) * rs;
+    const int npre = nv == 6 ? 0 : 2; // per-cell sqrt(h), 1/h (one layer only)
+    return ((size_t)(nv + 1 + npre) * lc_max + (size_t)2 * nv * e_max) * rs;
 }
 
 } // namespace swe

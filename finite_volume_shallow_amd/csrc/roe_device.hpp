@@ -199,17 +199,19 @@ __device__ __forceinline__ T newton_polish(T mu, T d1, T d2, T c1, T c2, T rc)
     return mu;
 }
 
-// L/R: h1, q1n, q1t, h2, q2n, q2t (edge frame), z.
+// L/R: h1, q1n, q1t, h2, q2n, q2t (edge frame), z; pL/pR: sqrt(h1), 1/h1,
+// sqrt(h2), 1/h2 of each cell.
 template <typename T>
-__device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, T zR, T g, T r)
+__device__ __forceinline__ Flux2<T> roe2_pre(const T *L, const T *pL, T zL, const T *R, const T *pR, T zR, T g,
+                                             T r)
 {
     Flux2<T> o;
     o.nonhyp = false;
     const T h1L = L[0], q1L = L[1], t1L = L[2], h2L = L[3], q2L = L[4], t2L = L[5];
     const T h1R = R[0], q1R = R[1], t1R = R[2], h2R = R[3], q2R = R[4], t2R = R[5];
-    const T i1L = rcp(h1L), i1R = rcp(h1R), i2L = rcp(h2L), i2R = rcp(h2R);
+    const T i1L = pL[1], i1R = pR[1], i2L = pL[3], i2R = pR[3];
     const T v1L = q1L * i1L, v1R = q1R * i1R, v2L = q2L * i2L, v2R = q2R * i2R;
-    const T s1L = FM<T>::sqrt(h1L), s1R = FM<T>::sqrt(h1R), s2L = FM<T>::sqrt(h2L), s2R = FM<T>::sqrt(h2R);
+    const T s1L = pL[0], s1R = pR[0], s2L = pL[2], s2R = pR[2];
     const T u1 = (s1L * v1L + s1R * v1R) * rcp(s1L + s1R);
     const T u2 = (s2L * v2L + s2R * v2R) * rcp(s2L + s2R);
     const T c1 = g * T(0.5) * (h1L + h1R); // c1^2
@@ -296,13 +298,32 @@ __device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, 
     return o;
 }
 
+// Per-cell sqrt(h_k), 1/h_k of a two-layer state.
+template <typename T> __device__ __forceinline__ void roe2_cellpre(const T *W, T *p)
+{
+    const T r1 = FM<T>::rsq(W[0]), r2 = FM<T>::rsq(W[3]);
+    p[0] = W[0] * r1;
+    p[1] = r1 * r1;
+    p[2] = W[3] * r2;
+    p[3] = r2 * r2;
+}
+
+template <typename T>
+__device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, T zR, T g, T r)
+{
+    T pL[4], pR[4];
+    roe2_cellpre(L, pL);
+    roe2_cellpre(R, pR);
+    return roe2_pre<T>(L, pL, zL, R, pR, zR, g, r);
+}
+
 // Two-layer reflective wall seen from side a: the mirror ghost through the
 // 4x4 flux, then both mass fluxes (hence the transverse fluxes) set to zero.
 template <typename T>
-__device__ __forceinline__ Flux2<T> roe2_wall(const T *L, T z, T g, T r)
+__device__ __forceinline__ Flux2<T> roe2_wall_pre(const T *L, const T *pL, T z, T g, T r)
 {
     const T G[6] = {L[0], -L[1], L[2], L[3], -L[4], L[5]};
-    Flux2<T> o = roe2_interior<T>(L, z, G, z, g, r);
+    Flux2<T> o = roe2_pre<T>(L, pL, z, G, pL, z, g, r);
     o.a[0] = -L[1];
     o.a[3] = -L[4];
     o.a[2] = -L[1] * L[2] * rcp(L[0]);
@@ -310,6 +331,13 @@ __device__ __forceinline__ Flux2<T> roe2_wall(const T *L, T z, T g, T r)
 #pragma unroll
     for (int v = 0; v < 6; ++v) o.b[v] = T(0);
     return o;
+}
+
+template <typename T> __device__ __forceinline__ Flux2<T> roe2_wall(const T *L, T z, T g, T r)
+{
+    T p[4];
+    roe2_cellpre(L, p);
+    return roe2_wall_pre<T>(L, p, z, g, r);
 }
 
 } // namespace swe

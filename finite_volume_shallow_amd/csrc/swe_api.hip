@@ -274,17 +274,25 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 for (int k = 0; k < 3; ++k) tri_int[3 * i + k] = d->tri[3 * (int64_t)c->perm_host[i] + k];
             st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, tri_int.data(), he, c->err);
             if (st != SWE_OK) throw Fail{st};
-            // the largest block (cells per workgroup) whose LDS fits in 64 KiB
+            // the largest block (256 or 128 cells per workgroup) whose LDS
+            // fits in 64 KiB and whose local cells and edges fit in three
+            // rounds of the 256 threads
             int B = 256;
+            if (const char *e = std::getenv("SWE_TRI_B")) // tuning override
+                if (std::atoi(e) == 128) B = 128;
             for (;;) {
                 st = build_tri_blocks(he, c->N, B, hb, c->err);
                 if (st != SWE_OK) throw Fail{st};
-                if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= 65536 || B <= 32) break;
-                B /= 2;
-            }
-            if (tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) > 65536 || hb.lc_max > 768 || hb.e_max > 768) {
-                c->err = "triangle blocks do not fit in LDS (mesh too irregular); use SWE_PATH_EDGE";
-                throw Fail{SWE_E_INVAL};
+                int upd = 0;
+                for (int b = 0; b < hb.nblocks; ++b) upd = std::max(upd, hb.slot_off[b + 1] - hb.slot_off[b]);
+                const bool fits = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= 65536 &&
+                                  std::max(std::max(hb.lc_max, hb.e_max), upd) <= 3 * 256;
+                if (fits) break;
+                if (B == 128) {
+                    c->err = "triangle blocks do not fit (mesh too irregular); use SWE_PATH_EDGE";
+                    throw Fail{SWE_E_INVAL};
+                }
+                B = 128;
             }
         }
 

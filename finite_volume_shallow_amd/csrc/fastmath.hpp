@@ -19,6 +19,7 @@ template <> struct FM<float> {
     static __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
     static __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
     static __device__ __forceinline__ float sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+    static __device__ __forceinline__ float rsq_est(float x) { return __builtin_amdgcn_rsqf(x); }
 };
 
 template <> struct FM<double> {
@@ -41,6 +42,8 @@ template <> struct FM<double> {
         return y * e;
     }
     static __device__ __forceinline__ double sqrt(double x) { return x * rsq(x); }
+    // the bare hardware estimate, for starting points only
+    static __device__ __forceinline__ double rsq_est(double x) { return __builtin_amdgcn_rsq(x); }
 };
 
 } // namespace swe

@@ -63,9 +63,8 @@ __device__ __forceinline__ T roe2_speed(const T *L, const T *pL, const T *R, con
     const T c2 = g * T(0.5) * (L[3] + R[3]);
     const T rc = r * c1 * c2;
     const T m = T(0.5) * (u1 + u2), d1 = u1 - m, d2 = u2 - m;
-    const T bound = FM<T>::sqrt(c1 + c2);
-    const T hi = newton_outer(fmax(d1, d2) + bound, d1, d2, c1, c2, rc);
-    const T lo = newton_outer(fmin(d1, d2) - bound, d1, d2, c1, c2, rc);
+    T hi, lo;
+    outer_roots(d1, d2, c1, c2, rc, hi, lo);
     // inner pair real?  (deflated quadratic discriminant)
     const T p1 = d1 * d1 - c1, p2 = d2 * d2 - c2;
     const T a3 = T(-2) * (d1 + d2), a2 = p1 + p2 + T(4) * d1 * d2;
@@ -208,7 +207,7 @@ __device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb
     return len * sp;
 }
 
-// RD: rounds of 256 threads covering the largest local cell / edge / slot
+// RD: rounds of NT threads covering the largest local cell / edge / slot
 // counts of any block.  Every global load a thread will need in the launch
 // (halo ids, its edges' geometry, its cells' slot lists and 1/|V|) is issued
 // at the start, so the phases after the first barrier only touch LDS.
@@ -446,6 +445,12 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     const size_t lds = tri_lds_bytes(NV, sizeof(T), c->tb.lc_max, c->tb.e_max);
     const int per_xcd = (c->tb.nblocks + TRI_XCD - 1) / TRI_XCD;
     const dim3 grid((unsigned)(per_xcd * TRI_XCD)), block(NT);
+    if (lds > 65536) {
+        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, true, RD, NT>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    }
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
     hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
                        tri_args<T>(c, 0, cfl));
@@ -457,9 +462,14 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
 
 template <typename T, int NL, bool TR> static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
-    // 256 threads per workgroup (four wavefronts keep the CU busy across
-    // the barriers even for 128-cell blocks); rounds of 256 cover the
-    // largest local cell / edge / update counts (checked at create)
+    // 512 threads per workgroup (eight wavefronts: the block's latency is
+    // hidden by its own waves as much as by the other blocks on the CU);
+    // rounds of threads cover the largest local cell / edge / update counts
+    // (checked at create)
+    if (c->tb.nt == 512) {
+        if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 512>(c, nsteps, cfl);
+        return tri_batch_rd<T, NL, TR, 2, 512>(c, nsteps, cfl);
+    }
     if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 256>(c, nsteps, cfl);
     if (c->tb.rounds <= 2) return tri_batch_rd<T, NL, TR, 2, 256>(c, nsteps, cfl);
     return tri_batch_rd<T, NL, TR, 3, 256>(c, nsteps, cfl);

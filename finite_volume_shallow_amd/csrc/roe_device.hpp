@@ -37,9 +37,6 @@ namespace swe {
 
 template <typename T> __device__ __forceinline__ T rcp(T x) { return FM<T>::rcp(x); }
 
-template <typename T> struct Eps;
-template <> struct Eps<double> { static constexpr double v = 2.220446049250313e-16; };
-template <> struct Eps<float> { static constexpr float v = 1.1920929e-7f; };
 
 // sgn-weights 1/2 (1 - sgn(lambda)) with sgn(0) = 0
 template <typename T> __device__ __forceinline__ T wminus(T lam)
@@ -145,12 +142,25 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_wall(T h, T qn, T qt, T hc, T g
 // t = (l - u2)^2 - c2^2; the product of a left and its right eigenvector is
 // Q'(l).  So alpha_k = l_k . X / Q'(l_k) needs no matrix inversion.
 //
-// Roots: the two outer roots by Newton from outside bounds (Q is convex and
-// increasing beyond its largest root when all four roots are real, so the
-// iteration decreases monotonically onto it; likewise from the left), the
-// two inner roots from the deflated quadratic, each polished by Newton on
-// the factored form of Q.  A negative discriminant of the deflated
-// quadratic means complex speeds: the state is flagged non-hyperbolic.
+// Roots: the two outer roots by Newton, the two inner roots from the
+// deflated quadratic, each polished by one Newton step on the factored form
+// of Q.  A negative discriminant of the deflated quadratic means complex
+// speeds: the state is flagged non-hyperbolic.
+//
+// Newton starts for the outer roots.  Write P for the product term alone
+// (no coupling): its roots are d_k -/+ c_k, and Q = P - r c1^2 c2^2 < P,
+// so the largest root of Q lies above the largest root p4 of P, where P
+// (and Q) is already increasing and convex; Newton started anywhere at or
+// beyond p4 converges to it monotonically after at most one overshoot.
+// The start is the outer root of the motionless pair (d1 = d2 = 0, a
+// biquadratic: mu^2 = (c1^2 + c2^2 + sqrt((c1^2 - c2^2)^2 + 4 r c1^2 c2^2))/2)
+// shifted by the c^2-weighted mean of d1, d2, raised to p4 if below it;
+// mirrored for the smallest root.  That start is within a few 1e-5 of the
+// root for the flows of interest, so one or two steps suffice.  Iteration
+// stops once a step is below sqrt-epsilon of the root: Newton's quadratic
+// convergence leaves the iterate after such a step accurate to rounding.
+// ---------------------------------------------------------------------------
+
 // ---------------------------------------------------------------------------
 
 template <typename T> struct Flux2 {
@@ -174,29 +184,48 @@ __device__ __forceinline__ T quartic_dq(T mu, T d1, T d2, T c1, T c2)
     return T(2) * (e1 * (e2 * e2 - c2) + e2 * (e1 * e1 - c1));
 }
 
-template <typename T>
-__device__ __forceinline__ T newton_outer(T mu, T d1, T d2, T c1, T c2, T rc)
+template <typename T> struct NewtonStop;
+template <> struct NewtonStop<double> { static constexpr double v = 1e-8; };
+template <> struct NewtonStop<float> { static constexpr float v = 1e-4f; };
+
+// square root good enough for a starting point (hardware estimate, 0 for 0)
+template <typename T> __device__ __forceinline__ T sqrt_start(T x)
 {
-    // monotone from outside; bounded iteration count
+    return x > T(0) ? x * FM<T>::rsq_est(x) : T(0);
+}
+
+// Largest (hi) and smallest (lo) root of Q in the shifted variable.
+template <typename T>
+__device__ __forceinline__ void outer_roots(T d1, T d2, T c1, T c2, T rc, T &hi, T &lo)
+{
+    const T s1 = sqrt_start(c1), s2 = sqrt_start(c2);
+    const T dc = c1 - c2;
+    const T w = sqrt_start(T(0.5) * ((c1 + c2) + sqrt_start(dc * dc + T(4) * rc)));
+    const T um = (d1 * c1 + d2 * c2) * rcp(c1 + c2);
+    // p4 / p1 from estimated square roots: moved out by a margin that covers
+    // their error (and keeps Q' > 0 off a double root of P)
+    const T mg = T(1e-4) * (s1 + s2);
+    hi = fmax(um + w, fmax(d1 + s1, d2 + s2) + mg);
+    lo = fmin(um - w, fmin(d1 - s1, d2 - s2) - mg);
+    bool dh = false, dl = false;
     for (int it = 0; it < 40; ++it) {
-        const T f = quartic_q(mu, d1, d2, c1, c2, rc);
-        const T df = quartic_dq(mu, d1, d2, c1, c2);
-        if (df == T(0)) break;
-        const T step = f * rcp(df);
-        mu -= step;
-        if (fabs(step) <= T(4) * Eps<T>::v * fabs(mu) || !(fabs(step) > T(0))) break;
+        const T fh = quartic_q(hi, d1, d2, c1, c2, rc), gh = quartic_dq(hi, d1, d2, c1, c2);
+        const T fl = quartic_q(lo, d1, d2, c1, c2, rc), gl = quartic_dq(lo, d1, d2, c1, c2);
+        const T sh = fh == T(0) ? T(0) : fh * rcp(gh);
+        const T sl = fl == T(0) ? T(0) : fl * rcp(gl);
+        if (!dh) hi -= sh;
+        if (!dl) lo -= sl;
+        dh = dh || !(fabs(sh) > NewtonStop<T>::v * fabs(hi));
+        dl = dl || !(fabs(sl) > NewtonStop<T>::v * fabs(lo));
+        if (dh && dl) break;
     }
-    return mu;
 }
 
 template <typename T>
 __device__ __forceinline__ T newton_polish(T mu, T d1, T d2, T c1, T c2, T rc)
 {
-    for (int it = 0; it < 3; ++it) {
-        const T df = quartic_dq(mu, d1, d2, c1, c2);
-        if (df != T(0)) mu -= quartic_q(mu, d1, d2, c1, c2, rc) * rcp(df);
-    }
-    return mu;
+    const T df = quartic_dq(mu, d1, d2, c1, c2);
+    return df != T(0) ? mu - quartic_q(mu, d1, d2, c1, c2, rc) * rcp(df) : mu;
 }
 
 // L/R: h1, q1n, q1t, h2, q2n, q2t (edge frame), z; pL/pR: sqrt(h1), 1/h1,
@@ -229,9 +258,8 @@ __device__ __forceinline__ Flux2<T> roe2_pre(const T *L, const T *pL, T zL, cons
     // eigenvalues in the shifted variable mu = lambda - m
     const T m = T(0.5) * (u1 + u2);
     const T d1 = u1 - m, d2 = u2 - m;
-    const T bound = FM<T>::sqrt(c1 + c2);
-    const T muhi = newton_outer(fmax(d1, d2) + bound, d1, d2, c1, c2, rc);
-    const T mulo = newton_outer(fmin(d1, d2) - bound, d1, d2, c1, c2, rc);
+    T muhi, mulo;
+    outer_roots(d1, d2, c1, c2, rc, muhi, mulo);
     // Q(mu) = mu^4 + a3 mu^3 + a2 mu^2 + a1 mu + a0; divide by (mu-muhi)(mu-mulo)
     const T p1 = d1 * d1 - c1, p2 = d2 * d2 - c2;
     const T a3 = T(-2) * (d1 + d2);

@@ -143,7 +143,7 @@ template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
     c->tb.nblocks = hb.nblocks;
     int upd_max = 0;
     for (int b = 0; b < hb.nblocks; ++b) upd_max = std::max(upd_max, hb.slot_off[b + 1] - hb.slot_off[b]);
-    c->tb.rounds = (std::max(std::max(hb.lc_max, hb.e_max), upd_max) + 255) / 256;
+    c->tb.rounds = (std::max(std::max(hb.lc_max, hb.e_max), upd_max) + c->tb.nt - 1) / c->tb.nt;
     c->tb.lc_max = hb.lc_max;
     c->tb.e_max = hb.e_max;
     c->tb.halo_off = ints(hb.halo_off);
@@ -274,25 +274,34 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 for (int k = 0; k < 3; ++k) tri_int[3 * i + k] = d->tri[3 * (int64_t)c->perm_host[i] + k];
             st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, tri_int.data(), he, c->err);
             if (st != SWE_OK) throw Fail{st};
-            // the largest block (256 or 128 cells per workgroup) whose LDS
-            // fits in 64 KiB and whose local cells and edges fit in three
-            // rounds of the 256 threads
-            int B = 256;
-            if (const char *e = std::getenv("SWE_TRI_B")) // tuning override
-                if (std::atoi(e) == 128) B = 128;
+            // 512 threads per workgroup; blocks of 288 cells (one layer) or
+            // 192 (two layers, whose per-cell and per-edge LDS is twice as
+            // large), fewer if the LDS of a block would exceed 64 KiB or its
+            // local cells and edges two rounds of the threads
+            c->tb.nt = 512;
+            int B = c->nv == 6 ? 192 : 288;
+            size_t lds_cap = 65536;
+            if (const char *e = std::getenv("SWE_TRI_B")) { // tuning overrides
+                const int v = std::atoi(e);
+                if (v >= 64 && v <= 512 && v % 32 == 0) B = v;
+            }
+            if (const char *e = std::getenv("SWE_TRI_LDS")) lds_cap = (size_t)std::atol(e);
+            if (const char *e = std::getenv("SWE_TRI_NT"))
+                if (std::atoi(e) == 256) c->tb.nt = 256;
             for (;;) {
                 st = build_tri_blocks(he, c->N, B, hb, c->err);
                 if (st != SWE_OK) throw Fail{st};
                 int upd = 0;
                 for (int b = 0; b < hb.nblocks; ++b) upd = std::max(upd, hb.slot_off[b + 1] - hb.slot_off[b]);
-                const bool fits = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= 65536 &&
-                                  std::max(std::max(hb.lc_max, hb.e_max), upd) <= 3 * 256;
+                const int cap = (c->tb.nt == 256 ? 3 : 2) * c->tb.nt;
+                const bool fits = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= lds_cap &&
+                                  std::max(std::max(hb.lc_max, hb.e_max), upd) <= cap;
                 if (fits) break;
-                if (B == 128) {
+                if (B <= 128) {
                     c->err = "triangle blocks do not fit (mesh too irregular); use SWE_PATH_EDGE";
                     throw Fail{SWE_E_INVAL};
                 }
-                B = 128;
+                B = B > 192 ? 192 : 128;
             }
         }
 

@@ -142,8 +142,7 @@ __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, 
     const T X1 = (qR * uR - qL * uL) + c2 * ((hR - hL) + (zR - zL));
     const T a1 = (lam2 * X0 - X1) * i2c;
     const T a2 = (X1 - lam1 * X0) * i2c;
-    const T w1 = lam1 < T(0) ? T(1) : (lam1 > T(0) ? T(0) : T(0.5));
-    const T w2 = lam2 < T(0) ? T(1) : (lam2 > T(0) ? T(0) : T(0.5));
+    const T w1 = wminus(lam1), w2 = wminus(lam2);
     const T pm0 = w1 * a1 + w2 * a2;
     const T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
     o.am = pm0;
@@ -222,8 +221,8 @@ __device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int 
 template <typename T> struct Carry {
     PC<T> prev;                  // W^n of row r-1
     bool prevrow;                // row r-1 inside the domain (uniform)
-    T ax_m, ax_x, ax_y, ax_c;    // x-edge fluctuation sums of row r-1 (times |G|)
-    T yb_m, yb_x, yb_y, yb_c;    // its bottom y-edge part
+    T ax_m, ax_x, ax_y, ax_c;    // x-edge fluctuation sums of row r-1
+    T yb_m, yb_n, yb_t, yb_c;    // its bottom y-edge part (edge frame)
     T np_h, np_s, np_b;          // W^{n+1} of row r-2: h, sqrt(h), qy / sqrt(h)
     bool nprow;                  // row r-2 inside the domain
     T sx_prev, sybot_prev;       // Eq. (5) speed sums of row r-2 (x-edges, bottom edge)
@@ -239,7 +238,7 @@ template <typename T> struct Ld {
 template <typename T> struct TileC {
     int i, col, j0, rlast, rstore_end;
     bool colok, xwall_lane, wlane;
-    T f, g, lx, ly, g_half;
+    T fx, fy, g, lx, ly, g_half;
 };
 
 // Rows of W^n a wavefront keeps in flight ahead of the row it computes.
@@ -280,10 +279,10 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
             ex.bc = c;
         }
     }
-    O.ax_m = lx * (ex.am + prv(ex.bm));
-    O.ax_x = lx * (ex.an + prv(ex.bn));
-    O.ax_y = lx * (ex.at + prv(ex.bt));
-    O.ax_c = TR ? lx * (ex.ac + prv(ex.bc)) : T(0);
+    O.ax_m = ex.am + prv(ex.bm);
+    O.ax_x = ex.an + prv(ex.bn);
+    O.ax_y = ex.at + prv(ex.bt);
+    O.ax_c = TR ? ex.ac + prv(ex.bc) : T(0);
 
     // ---- y-edge (row r-1, row r): normal (0, 1), qn = qy, ut = -u;
     // back-rotation (m, n, t, c) -> (m, -t, n, c)
@@ -313,16 +312,18 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     O.sx_prev = I.sx_prev;
     O.sybot_prev = I.sybot_prev;
     if (r >= K.j0) {
-        // ---- complete row r-1: W^{n+1} = W^n - dt/|V| sum |G| fluct
-        const T am = I.ax_m + I.yb_m + ly * ey.am;
-        const T ax = I.ax_x + I.yb_x + ly * (-ey.at);
-        const T ay = I.ax_y + I.yb_y + ly * ey.an;
-        const T ac = I.ax_c + I.yb_c + ly * ey.ac;
-        const T f = K.f;
-        const T h1 = prev.h - f * am;
-        const T qx1 = prev.qx - f * ax;
-        const T qy1 = prev.qy - f * ay;
-        const T c1 = TR ? prev.c - f * ac : T(0);
+        // ---- complete row r-1: W^{n+1} = W^n - dt/|V| sum |G| fluct, the
+        // x- and y-edge sums scaled by dt |G_x| / |V| and dt |G_y| / |V|;
+        // y-edge fluctuations map back as (m, n, t, c) -> (m, -t, n, c)
+        const T ym = I.yb_m + ey.am;
+        const T yt = I.yb_t + ey.at;
+        const T yn = I.yb_n + ey.an;
+        const T yc = I.yb_c + ey.ac;
+        const T fx = K.fx, fy = K.fy;
+        const T h1 = prev.h - fx * I.ax_m - fy * ym;
+        const T qx1 = prev.qx - fx * I.ax_x + fy * yt;
+        const T qy1 = prev.qy - fx * I.ax_y - fy * yn;
+        const T c1 = TR ? prev.c - fx * I.ax_c - fy * yc : T(0);
         // ---- Eq. (5) speeds of W^{n+1}
         const T rq = FM<T>::rsq(h1);
         const T s1 = h1 * rq, a1 = qx1 * rq, b1 = qy1 * rq;
@@ -357,11 +358,11 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         O.nprow = I.prevrow;
         O.sx_prev = sx_cur;
     }
-    // bottom part of the y-edge for row r: (m, n, t, c) -> (m, -t, n, c)
-    O.yb_m = ly * ey.bm;
-    O.yb_x = ly * (-ey.bt);
-    O.yb_y = ly * ey.bn;
-    O.yb_c = ly * ey.bc;
+    // bottom part of the y-edge for row r (edge frame)
+    O.yb_m = ey.bm;
+    O.yb_t = ey.bt;
+    O.yb_n = ey.bn;
+    O.yb_c = ey.bc;
     O.prev = cur;
     O.prevrow = currow;
 }
@@ -394,7 +395,8 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     K.wlane = lane >= 2 && lane < 2 + CART_COLS && K.i >= 0 && K.i < A.nx;
     K.rlast = K.j0 + A.ty + 1; // last row loaded
     K.rstore_end = min(K.j0 + A.ty, A.ny);
-    K.f = (T)dtd / (A.dx * A.dy);
+    K.fx = (T)(dtd / (double)A.dx); // dt |G_x| / |V|, |G_x| = dy
+    K.fy = (T)(dtd / (double)A.dy); // dt |G_y| / |V|, |G_y| = dx
     K.g = A.g;
     K.lx = A.dy; // length of an x-edge
     K.ly = A.dx; // length of a y-edge
@@ -409,7 +411,7 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
         c0.prev = prep(p.h, p.qx, p.qy, p.c, p.z);
         c0.prevrow = p.rowok;
         c0.ax_m = c0.ax_x = c0.ax_y = c0.ax_c = T(0);
-        c0.yb_m = c0.yb_x = c0.yb_y = c0.yb_c = T(0);
+        c0.yb_m = c0.yb_n = c0.yb_t = c0.yb_c = T(0);
         c0.np_h = T(1);
         c0.np_s = T(1);
         c0.np_b = T(0);

@@ -38,10 +38,20 @@ namespace swe {
 template <typename T> __device__ __forceinline__ T rcp(T x) { return FM<T>::rcp(x); }
 
 
-// sgn-weights 1/2 (1 - sgn(lambda)) with sgn(0) = 0
-template <typename T> __device__ __forceinline__ T wminus(T lam)
+// sgn-weights 1/2 (1 - sgn(lambda)) with sgn(0) = 0, branch-free:
+// clamp(1/2 - lambda 2^K, 0, 1) is exactly 1, 0, 1/2 for lambda < 0, > 0,
+// = 0 whenever |lambda| >= 2^-(K+1) or lambda = 0.  A wave speed is a sum
+// u +- c with c = sqrt(g h) > 0, so a nonzero one is at least an ulp of c,
+// far above 2^-101 (float) or 2^-601 (double); the product overflowing to
+// +-inf clamps correctly.
+template <typename T> __device__ __forceinline__ T wminus(T lam);
+template <> __device__ __forceinline__ float wminus(float lam)
 {
-    return lam < T(0) ? T(1) : (lam > T(0) ? T(0) : T(0.5));
+    return __builtin_amdgcn_fmed3f(__builtin_fmaf(lam, -0x1p100f, 0.5f), 0.0f, 1.0f);
+}
+template <> __device__ __forceinline__ double wminus(double lam)
+{
+    return fmin(fmax(__builtin_fma(lam, -0x1p600, 0.5), 0.0), 1.0);
 }
 
 // One-layer interior edge.  Inputs are edge-frame states: depth h, normal

@@ -42,7 +42,7 @@ template <typename T> struct TriArgs {
     int B, nblocks, per_xcd, lc_max, e_max;
     const int32_t *halo_off, *halo_ids, *n1, *edge_off, *e_s0, *slot_off;
     const uint32_t *e_ab;
-    const T *e_nx, *e_ny, *e_len;
+    const T *e_gx, *e_gy; // |G| eta of the local edges
     const uint16_t *slots;
     const T *iarea;
     T g, r, cfl;
@@ -263,9 +263,8 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
         const int k = tid + m * NT;
         const bool ok = DT0 ? k < es0 : k < ne;
         eab[m] = ok ? A.e_ab[e0 + k] : 0u;
-        enx[m] = ok ? A.e_nx[e0 + k] : T(0);
-        eny[m] = ok ? A.e_ny[e0 + k] : T(0);
-        elen[m] = ok ? A.e_len[e0 + k] : T(0);
+        enx[m] = ok ? A.e_gx[e0 + k] : T(1); // |G| eta until the loads land
+        eny[m] = ok ? A.e_gy[e0 + k] : T(0);
     }
     uint16_t csl[RD][3];
     T cia[RD];
@@ -288,6 +287,15 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
             sm[NV * LCM + l] = A.z[gid[m]];
             tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
         }
+    }
+    // unit normal and length of each of this thread's edges from |G| eta
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+        const T q = enx[m] * enx[m] + eny[m] * eny[m];
+        const T rq = FM<T>::rsq(q);
+        elen[m] = q * rq;
+        enx[m] *= rq;
+        eny[m] *= rq;
     }
     __syncthreads();
 
@@ -424,9 +432,8 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     A.e_s0 = c->tb.e_s0;
     A.slot_off = c->tb.slot_off;
     A.e_ab = c->tb.e_ab;
-    A.e_nx = (const T *)c->tb.e_nx;
-    A.e_ny = (const T *)c->tb.e_ny;
-    A.e_len = (const T *)c->tb.e_len;
+    A.e_gx = (const T *)c->tb.e_gx;
+    A.e_gy = (const T *)c->tb.e_gy;
     A.slots = c->tb.slots;
     A.iarea = (const T *)c->tb.iarea;
     A.g = (T)c->g;

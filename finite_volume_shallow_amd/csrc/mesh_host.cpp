@@ -278,9 +278,8 @@ int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std
             const uint32_t la = (uint32_t)cloc[he.a[e]];
             const uint32_t lb = he.b[e] >= 0 ? (uint32_t)cloc[he.b[e]] : 0xFFFFu;
             out.e_ab.push_back(la | (lb << 16));
-            out.e_nx.push_back(he.nx[e]);
-            out.e_ny.push_back(he.ny[e]);
-            out.e_len.push_back(he.len[e]);
+            out.e_gx.push_back(he.len[e] * he.nx[e]);
+            out.e_gy.push_back(he.len[e] * he.ny[e]);
         }
         auto add_slots_of = [&](int64_t c) {
             if (he.off[c + 1] - he.off[c] != 3) return false;

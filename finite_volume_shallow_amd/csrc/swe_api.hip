@@ -154,9 +154,8 @@ template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
     c->tb.slot_off = ints(hb.slot_off);
     c->tb.e_ab = (uint32_t *)dev_alloc(c, hb.e_ab.size() * sizeof(uint32_t));
     upload_raw(c, c->tb.e_ab, hb.e_ab.data(), hb.e_ab.size() * sizeof(uint32_t));
-    c->tb.e_nx = reals(hb.e_nx);
-    c->tb.e_ny = reals(hb.e_ny);
-    c->tb.e_len = reals(hb.e_len);
+    c->tb.e_gx = reals(hb.e_gx);
+    c->tb.e_gy = reals(hb.e_gy);
     c->tb.iarea = reals(hb.iarea);
     c->tb.slots = (uint16_t *)dev_alloc(c, hb.slots.size() * sizeof(uint16_t));
     upload_raw(c, c->tb.slots, hb.slots.data(), hb.slots.size() * sizeof(uint16_t));

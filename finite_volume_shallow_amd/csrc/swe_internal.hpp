@@ -38,7 +38,7 @@ struct HostBlocks {
     std::vector<int32_t> n1;                 // ring-1 size per block
     std::vector<int32_t> edge_off, e_s0;     // local edges; leading edges touching the block
     std::vector<uint32_t> e_ab;              // local a | local b << 16 (b = 0xFFFF: wall)
-    std::vector<double> e_nx, e_ny, e_len;
+    std::vector<double> e_gx, e_gy;          // |G| eta: length times unit normal
     std::vector<int32_t> slot_off;           // per block: first slot row (block + ring 1 cells)
     std::vector<uint16_t> slots;             // 3 per cell: local edge << 1 | side
     std::vector<double> iarea;               // 1/|V| per slot row
@@ -114,7 +114,7 @@ struct swe_ctx {
         int32_t *halo_off = nullptr, *halo_ids = nullptr, *n1 = nullptr, *edge_off = nullptr,
                 *e_s0 = nullptr, *slot_off = nullptr;
         uint32_t *e_ab = nullptr;
-        void *e_nx = nullptr, *e_ny = nullptr, *e_len = nullptr, *iarea = nullptr;
+        void *e_gx = nullptr, *e_gy = nullptr, *iarea = nullptr;
         uint16_t *slots = nullptr;
     } tb;
 

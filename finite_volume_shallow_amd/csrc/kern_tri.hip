@@ -207,6 +207,19 @@ __device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb
     return len * sp;
 }
 
+// Per-step bookkeeping by workgroup 0: clear the partial-minimum bank the
+// launch after next will fill, record dt^n and advance the time.
+template <typename T> __device__ __forceinline__ void tri_book(const TriArgs<T> &A, int bank, int tid, double dtd)
+{
+    if (tid < 64) {
+        A.part[((bank + 2) % 3) * TRI_NPART + tid] = __builtin_inf();
+        if (tid == 0) {
+            A.book.hist[A.step] = dtd;
+            A.book.t[0] += dtd;
+        }
+    }
+}
+
 // RD: rounds of NT threads covering the largest local cell / edge / slot
 // counts of any block.  Every global load a thread will need in the launch
 // (halo ids, its edges' geometry, its cells' slot lists and 1/|V|) is issued
@@ -225,18 +238,13 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     const int w = blockIdx.x;
     const int blk = (w % TRI_XCD) * A.per_xcd + w / TRI_XCD;
     const int bank = (int)(A.step % 3);
-    double dtd = 0.0;
-    if (!DT0) {
-        dtd = wave_min(A.part[bank * TRI_NPART + lane]);
-        if (w == 0 && tid < 64) {
-            A.part[((bank + 2) % 3) * TRI_NPART + lane] = __builtin_inf();
-            if (lane == 0) {
-                A.book.hist[A.step] = dtd;
-                A.book.t[0] += dtd;
-            }
-        }
+    // the partial minima of dt^n: loaded now, reduced when the update needs
+    // them, so their latency overlaps the block's own loads
+    const double dpart = DT0 ? 0.0 : A.part[bank * TRI_NPART + lane];
+    if (blk >= A.nblocks) { // uniform over the workgroup
+        if (!DT0 && w == 0) tri_book(A, bank, tid, wave_min(dpart));
+        return;
     }
-    if (blk >= A.nblocks) return; // uniform over the workgroup
 
     const int64_t base = (int64_t)blk * A.B;
     const int B0 = (int)min((int64_t)A.B, A.N - base);
@@ -249,42 +257,63 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     const T g = A.g, rr = A.r;
     unsigned bad = 0;
 
-    // ---- all global reads of the launch, issued up front
-    int64_t gid[RD];
+    // ---- all global reads of the launch, issued up front.  The loads are
+    // unconditional (indices clamped into the block's ranges, which are never
+    // empty, and the halo list ends with a padding entry) and out-of-range
+    // lanes are masked afterwards, so no load waits on a branch.
+    const int nh1 = max(nh - 1, 0);
+    const int ne1 = (DT0 ? es0 : ne) - 1, nc1 = nc - 1;
+    int32_t hid[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
-        gid[m] = l < B0 ? base + l : (l < LC ? (int64_t)A.halo_ids[h0 + l - B0] : -1);
+        hid[m] = A.halo_ids[h0 + min(max(l - B0, 0), nh1)];
     }
     uint32_t eab[RD];
     T enx[RD], eny[RD], elen[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int k = tid + m * NT;
-        const bool ok = DT0 ? k < es0 : k < ne;
-        eab[m] = ok ? A.e_ab[e0 + k] : 0u;
-        enx[m] = ok ? A.e_gx[e0 + k] : T(1); // |G| eta until the loads land
-        eny[m] = ok ? A.e_gy[e0 + k] : T(0);
+        const int k = min(tid + m * NT, ne1);
+        eab[m] = A.e_ab[e0 + k];
+        enx[m] = A.e_gx[e0 + k]; // |G| eta until the loads land
+        eny[m] = A.e_gy[e0 + k];
     }
-    uint16_t csl[RD][3];
+    uint64_t csl4[RD];
     T cia[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int l = tid + m * NT;
-        const bool ok = l < nc;
+        const int l = min(tid + m * NT, nc1);
+        csl4[m] = reinterpret_cast<const uint64_t *>(A.slots)[s0 + l];
+        cia[m] = A.iarea[s0 + l];
+    }
+    // (an empty asm use pins the halo-id loads here, ahead of the branchy
+    // selection below, which would otherwise pull them into a branch and
+    // wait on each)
 #pragma unroll
-        for (int j = 0; j < 3; ++j) csl[m][j] = ok ? A.slots[3 * (s0 + l) + j] : (uint16_t)0;
-        cia[m] = ok ? A.iarea[s0 + l] : T(0);
+    for (int m = 0; m < RD; ++m) asm volatile("" ::"v"(hid[m]));
+    int64_t gid[RD];
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+        const int l = tid + m * NT;
+        gid[m] = l < B0 ? base + l : (l < LC ? (int64_t)hid[m] : -1);
     }
 
-    // ---- 1. W^n and z of the block and its two rings into LDS
+    // ---- 1. W^n and z of the block and its two rings into LDS (all rounds
+    // loaded before the first LDS write)
+    T st[RD][NV + 1];
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+        const int64_t gm = gid[m] >= 0 ? gid[m] : base;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) st[m][v] = A.in[v][gm];
+        st[m][NV] = A.z[gm];
+    }
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
         if (gid[m] >= 0) {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) sm[v * LCM + l] = A.in[v][gid[m]];
-            sm[NV * LCM + l] = A.z[gid[m]];
+            for (int v = 0; v <= NV; ++v) sm[v * LCM + l] = st[m][v];
             tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
         }
     }
@@ -299,6 +328,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     }
     __syncthreads();
 
+    double dtd = 0.0;
     if (!DT0) {
         // ---- 2. every edge touching the block or ring 1, once
 #pragma unroll
@@ -317,6 +347,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
         }
         __syncthreads();
 
+        dtd = wave_min(dpart);
         // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
 #pragma unroll
         for (int m = 0; m < RD; ++m) {
@@ -327,7 +358,8 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
                 for (int v = 0; v < NV; ++v) acc[v] = T(0);
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
-                    const int e = csl[m][j] >> 1, side = csl[m][j] & 1;
+                    const unsigned sj = (unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu;
+                    const int e = (int)(sj >> 1), side = (int)(sj & 1u);
 #pragma unroll
                     for (int v = 0; v < NV; ++v) acc[v] += fl[(side * NV + v) * EM + e];
                 }
@@ -357,7 +389,8 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
         if (l < B0) {
-            const T S = fl[csl[m][0] >> 1] + fl[csl[m][1] >> 1] + fl[csl[m][2] >> 1];
+            const T S = fl[(unsigned)(csl4[m] >> 1) & 0x7FFFu] + fl[(unsigned)(csl4[m] >> 17) & 0x7FFFu] +
+                        fl[(unsigned)(csl4[m] >> 33) & 0x7FFFu];
             cand = fmin(cand, (double)(T(2) * A.cfl / (cia[m] * S)));
             if (!DT0) {
                 bool badv = false;
@@ -375,6 +408,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     const int slot_bank = DT0 ? 0 : (bank + 1) % 3;
     block_min_to_slot(cand, A.part + slot_bank * TRI_NPART + (w % TRI_NPART));
     if (bad) atomicOr(A.book.flags, bad);
+    if (!DT0 && w == 0) tri_book(A, bank, tid, dtd);
 }
 
 __global__ void k_tri_init(double *part, StepBook book)

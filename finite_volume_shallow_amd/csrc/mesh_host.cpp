@@ -287,6 +287,7 @@ int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std
                 const int32_t e = he.ce[k] >> 1, side = he.ce[k] & 1;
                 out.slots.push_back((uint16_t)((eloc[e] << 1) | side));
             }
+            out.slots.push_back(0); // padding: one 8-byte load per cell
             out.iarea.push_back(1.0 / he.area[c]);
             return true;
         };
@@ -301,6 +302,7 @@ int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std
         out.e_s0.push_back(es0);
         out.edge_off.push_back((int32_t)out.e_ab.size());
         out.slot_off.push_back(out.slot_off.back() + B0 + n1);
+        if (b == nb - 1) out.halo_ids.push_back(0); // padding: in-range clamped loads
         out.lc_max = std::max(out.lc_max, lc);
         out.e_max = std::max(out.e_max, ne);
     }

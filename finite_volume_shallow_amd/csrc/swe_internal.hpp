@@ -34,13 +34,13 @@ struct HostEdges {
 struct HostBlocks {
     int B = 0, nblocks = 0;
     int lc_max = 0, e_max = 0;              // largest local cell / edge counts
-    std::vector<int32_t> halo_off, halo_ids; // global ids of ring 1 then ring 2
+    std::vector<int32_t> halo_off, halo_ids; // global ids of ring 1 then ring 2 (one padding entry at the end)
     std::vector<int32_t> n1;                 // ring-1 size per block
     std::vector<int32_t> edge_off, e_s0;     // local edges; leading edges touching the block
     std::vector<uint32_t> e_ab;              // local a | local b << 16 (b = 0xFFFF: wall)
     std::vector<double> e_gx, e_gy;          // |G| eta: length times unit normal
     std::vector<int32_t> slot_off;           // per block: first slot row (block + ring 1 cells)
-    std::vector<uint16_t> slots;             // 3 per cell: local edge << 1 | side
+    std::vector<uint16_t> slots;             // 4 per cell: 3 x (local edge << 1 | side), padding
     std::vector<double> iarea;               // 1/|V| per slot row
 };
 

@@ -207,6 +207,18 @@ __device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb
     return len * sp;
 }
 
+// Element i of an array through a 32-bit byte offset (scalar base plus
+// vector offset addressing; every array of this path is below 4 GiB: cells
+// and local edges < 2^29).
+template <typename T> __device__ __forceinline__ const T &ld32(const T *base, uint32_t i)
+{
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + (uint32_t)(i * (uint32_t)sizeof(T)));
+}
+template <typename T> __device__ __forceinline__ T &st32(T *base, uint32_t i)
+{
+    return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + (uint32_t)(i * (uint32_t)sizeof(T)));
+}
+
 // Per-step bookkeeping by workgroup 0: clear the partial-minimum bank the
 // launch after next will fill, record dt^n and advance the time.
 template <typename T> __device__ __forceinline__ void tri_book(const TriArgs<T> &A, int bank, int tid, double dtd)
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     T *sm = reinterpret_cast<T *>(smem_d);
     const int LCM = A.lc_max, EM = A.e_max;
     T *pre = sm + (NV + 1) * LCM;          // one layer: sqrt(h), 1/h at pre[l], pre[LCM + l]
-    T *fl = pre + (NL == 1 ? 2 : 0) * LCM; // fluctuation slots: side s, var v at fl[(s * NV + v) * EM + e]
+    T *fl = pre + (NL == 1 ? 2 : 0) * LCM; // fluctuation slots: side s, var v of edge e at fl[(s * NV + v) * EM + e]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = blockIdx.x;
@@ -261,41 +273,41 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     // unconditional (indices clamped into the block's ranges, which are never
     // empty, and the halo list ends with a padding entry) and out-of-range
     // lanes are masked afterwards, so no load waits on a branch.
+    const uint32_t ubase = (uint32_t)base;
     const int nh1 = max(nh - 1, 0);
     const int ne1 = (DT0 ? es0 : ne) - 1, nc1 = nc - 1;
     int32_t hid[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
-        hid[m] = A.halo_ids[h0 + min(max(l - B0, 0), nh1)];
+        hid[m] = ld32(A.halo_ids, (uint32_t)(h0 + min(max(l - B0, 0), nh1)));
     }
     uint32_t eab[RD];
     T enx[RD], eny[RD], elen[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int k = min(tid + m * NT, ne1);
-        eab[m] = A.e_ab[e0 + k];
-        enx[m] = A.e_gx[e0 + k]; // |G| eta until the loads land
-        eny[m] = A.e_gy[e0 + k];
+        const uint32_t k = (uint32_t)(e0 + min(tid + m * NT, ne1));
+        eab[m] = ld32(A.e_ab, k);
+        enx[m] = ld32(A.e_gx, k); // |G| eta until the loads land
+        eny[m] = ld32(A.e_gy, k);
     }
     uint64_t csl4[RD];
     T cia[RD];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int l = min(tid + m * NT, nc1);
-        csl4[m] = reinterpret_cast<const uint64_t *>(A.slots)[s0 + l];
-        cia[m] = A.iarea[s0 + l];
+        const uint32_t r = (uint32_t)(s0 + min(tid + m * NT, nc1));
+        csl4[m] = ld32(reinterpret_cast<const uint64_t *>(A.slots), r);
+        cia[m] = ld32(A.iarea, r);
     }
-    // (an empty asm use pins the halo-id loads here, ahead of the branchy
-    // selection below, which would otherwise pull them into a branch and
-    // wait on each)
+    // (an empty asm use pins the halo-id loads here, ahead of the selection
+    // below, which would otherwise pull them into a branch and wait on each)
 #pragma unroll
     for (int m = 0; m < RD; ++m) asm volatile("" ::"v"(hid[m]));
-    int64_t gid[RD];
+    uint32_t gidx[RD]; // a valid cell for every lane; only l < LC are local cells
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
-        gid[m] = l < B0 ? base + l : (l < LC ? (int64_t)hid[m] : -1);
+        gidx[m] = l < B0 ? ubase + (uint32_t)l : (uint32_t)hid[m];
     }
 
     // ---- 1. W^n and z of the block and its two rings into LDS (all rounds
@@ -303,15 +315,14 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     T st[RD][NV + 1];
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
-        const int64_t gm = gid[m] >= 0 ? gid[m] : base;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) st[m][v] = A.in[v][gm];
-        st[m][NV] = A.z[gm];
+        for (int v = 0; v < NV; ++v) st[m][v] = ld32(A.in[v], gidx[m]);
+        st[m][NV] = ld32(A.z, gidx[m]);
     }
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
-        if (gid[m] >= 0) {
+        if (l < LC) {
 #pragma unroll
             for (int v = 0; v <= NV; ++v) sm[v * LCM + l] = st[m][v];
             tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
@@ -349,6 +360,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 
         dtd = wave_min(dpart);
         // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
+        // (a slot is side * NV * EM + edge: variable v of it sits v * EM on)
 #pragma unroll
         for (int m = 0; m < RD; ++m) {
             const int l = tid + m * NT;
@@ -358,10 +370,9 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
                 for (int v = 0; v < NV; ++v) acc[v] = T(0);
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
-                    const unsigned sj = (unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu;
-                    const int e = (int)(sj >> 1), side = (int)(sj & 1u);
+                    const T *f = fl + ((unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu);
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) acc[v] += fl[(side * NV + v) * EM + e];
+                    for (int v = 0; v < NV; ++v) acc[v] += f[v * EM];
                 }
                 const T fct = (T)dtd * cia[m];
 #pragma unroll
@@ -373,31 +384,37 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     }
 
     // ---- 4. Eq. (5) speeds on the edges touching the block (of W^{n+1}, or
-    // of W^0 for the prologue), parked in the first slot array
+    // of W^0 for the prologue), parked at both sides' first slot so that the
+    // cells' slots address them directly
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int k = tid + m * NT;
-        if (k < es0)
-            fl[k] = tri_edge_speed<T, NL, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
-                                              eny[m], elen[m], g, rr, bad);
+        if (k < es0) {
+            const T sp = tri_edge_speed<T, NL, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
+                                                   eny[m], elen[m], g, rr, bad);
+            fl[k] = sp;
+            fl[NV * EM + k] = sp;
+        }
     }
     __syncthreads();
 
-    // ---- 5. dt candidates of the block cells, W^{n+1} out
-    double cand = __builtin_inf();
+    // ---- 5. dt candidates of the block cells, W^{n+1} out.  dt_i =
+    // 2 gamma / (S_i / |V_i|) and a correctly rounded quotient is monotone in
+    // its divisor, so the smallest dt_i is 2 gamma over the largest S_i / |V_i|.
+    T rate = T(0);
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
         if (l < B0) {
-            const T S = fl[(unsigned)(csl4[m] >> 1) & 0x7FFFu] + fl[(unsigned)(csl4[m] >> 17) & 0x7FFFu] +
-                        fl[(unsigned)(csl4[m] >> 33) & 0x7FFFu];
-            cand = fmin(cand, (double)(T(2) * A.cfl / (cia[m] * S)));
+            const T S = fl[(unsigned)csl4[m] & 0xFFFFu] + fl[(unsigned)(csl4[m] >> 16) & 0xFFFFu] +
+                        fl[(unsigned)(csl4[m] >> 32) & 0xFFFFu];
+            rate = fmax(rate, cia[m] * S);
             if (!DT0) {
                 bool badv = false;
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                     const T x = sm[v * LCM + l];
-                    A.out[v][base + l] = x;
+                    st32(A.out[v], ubase + (uint32_t)l) = x;
                     badv |= !isfinite(x);
                 }
                 if (!(sm[l] > T(0)) || (NL == 2 && !(sm[3 * LCM + l] > T(0)))) bad |= FLAG_DEPTH;
@@ -405,6 +422,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
             }
         }
     }
+    const double cand = rate > T(0) ? (double)(T(2) * A.cfl / rate) : __builtin_inf();
     const int slot_bank = DT0 ? 0 : (bank + 1) % 3;
     block_min_to_slot(cand, A.part + slot_bank * TRI_NPART + (w % TRI_NPART));
     if (bad) atomicOr(A.book.flags, bad);

@@ -157,8 +157,13 @@ template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
     c->tb.e_gx = reals(hb.e_gx);
     c->tb.e_gy = reals(hb.e_gy);
     c->tb.iarea = reals(hb.iarea);
-    c->tb.slots = (uint16_t *)dev_alloc(c, hb.slots.size() * sizeof(uint16_t));
-    upload_raw(c, c->tb.slots, hb.slots.data(), hb.slots.size() * sizeof(uint16_t));
+    // slots as the kernel addresses its fluctuation LDS: side * nv * e_max + edge
+    std::vector<uint16_t> enc(hb.slots.size(), 0);
+    for (size_t i = 0; i < hb.slots.size(); ++i)
+        if (i % 4 != 3)
+            enc[i] = (uint16_t)((hb.slots[i] & 1u) * (unsigned)(c->nv * hb.e_max) + (hb.slots[i] >> 1));
+    c->tb.slots = (uint16_t *)dev_alloc(c, enc.size() * sizeof(uint16_t));
+    upload_raw(c, c->tb.slots, enc.data(), enc.size() * sizeof(uint16_t));
 }
 
 void free_all(swe_ctx *c)
@@ -294,6 +299,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 for (int b = 0; b < hb.nblocks; ++b) upd = std::max(upd, hb.slot_off[b + 1] - hb.slot_off[b]);
                 const int cap = (c->tb.nt == 256 ? 3 : 2) * c->tb.nt;
                 const bool fits = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= lds_cap &&
+                                  2 * c->nv * hb.e_max <= 0xFFFF &&
                                   std::max(std::max(hb.lc_max, hb.e_max), upd) <= cap;
                 if (fits) break;
                 if (B <= 128) {

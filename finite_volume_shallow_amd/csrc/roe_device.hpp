@@ -221,8 +221,8 @@ __device__ __forceinline__ void outer_roots(T d1, T d2, T c1, T c2, T rc, T &hi,
     for (int it = 0; it < 40; ++it) {
         const T fh = quartic_q(hi, d1, d2, c1, c2, rc), gh = quartic_dq(hi, d1, d2, c1, c2);
         const T fl = quartic_q(lo, d1, d2, c1, c2, rc), gl = quartic_dq(lo, d1, d2, c1, c2);
-        const T sh = fh == T(0) ? T(0) : fh * rcp(gh);
-        const T sl = fl == T(0) ? T(0) : fl * rcp(gl);
+        const T sh = fh == T(0) ? T(0) : fh * FM<T>::rcp_est(gh);
+        const T sl = fl == T(0) ? T(0) : fl * FM<T>::rcp_est(gl);
         if (!dh) hi -= sh;
         if (!dl) lo -= sl;
         dh = dh || !(fabs(sh) > NewtonStop<T>::v * fabs(hi));
@@ -235,7 +235,7 @@ template <typename T>
 __device__ __forceinline__ T newton_polish(T mu, T d1, T d2, T c1, T c2, T rc)
 {
     const T df = quartic_dq(mu, d1, d2, c1, c2);
-    return df != T(0) ? mu - quartic_q(mu, d1, d2, c1, c2, rc) * rcp(df) : mu;
+    return df != T(0) ? mu - quartic_q(mu, d1, d2, c1, c2, rc) * FM<T>::rcp_est(df) : mu;
 }
 
 // L/R: h1, q1n, q1t, h2, q2n, q2t (edge frame), z; pL/pR: sqrt(h1), 1/h1,

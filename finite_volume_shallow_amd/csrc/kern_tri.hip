@@ -73,40 +73,61 @@ __device__ __forceinline__ T roe2_speed(const T *L, const T *pL, const T *R, con
     return fmax(fabs(hi + m), fabs(lo + m));
 }
 
-// sqrt(h) and 1/h of local cell l into pre[l], pre[LCM + l] (one layer; the
-// two-layer path keeps its LDS for occupancy and forms them per edge)
-template <typename T, int NL, int NV>
-__device__ __forceinline__ void tri_cellpre(const T *sm, T *pre, int LCM, int l)
+// LDS records.  LDS has 32 four-byte banks: a wave whose lanes read
+// consecutive records of an odd number of 8-byte reals touches every bank
+// once, so every record stride here is odd (in reals) and field offsets are
+// constants (neighbouring fields load and store as one instruction).
+//   cell state: the NV conserved variables (two layers: and z), SA reals;
+//   cell aux (one layer): z, sqrt(h), 1/h, 3 reals, after all state records;
+//   edge fluctuations: side a of every edge, then side b, ER reals each.
+template <int NL, int NV> struct TriRec {
+    static constexpr int SA = NL == 1 ? (NV | 1) : ((NV + 1) | 1);
+    static constexpr int AX = NL == 1 ? 3 : 0;
+    static constexpr int ER = NV | 1;
+};
+
+// View of local cell l: its state record and (one layer) its aux record.
+template <typename T, int NL, int NV> struct TriCell {
+    T *s, *x;
+    __device__ __forceinline__ TriCell(T *sm, int lcm, int l)
+        : s(sm + l * TriRec<NL, NV>::SA), x(sm + lcm * TriRec<NL, NV>::SA + l * TriRec<NL, NV>::AX)
+    {
+    }
+    __device__ __forceinline__ T &z() const { return NL == 1 ? x[0] : s[NV]; }
+    __device__ __forceinline__ T &sq() const { return x[1]; } // sqrt(h), one layer
+    __device__ __forceinline__ T &ih() const { return x[2]; } // 1/h, one layer
+};
+
+// sqrt(h) and 1/h of a one-layer cell (the two-layer path keeps its LDS for
+// occupancy and forms them per edge)
+template <typename T, int NL, int NV> __device__ __forceinline__ void tri_cellpre(const TriCell<T, NL, NV> &c)
 {
-    if (NL != 1) return;
-#pragma unroll
-    for (int k = 0; k < 1; ++k) {
-        const T h = sm[3 * k * LCM + l];
-        const T rq = FM<T>::rsq(h);
-        pre[2 * k * LCM + l] = h * rq;
-        pre[(2 * k + 1) * LCM + l] = rq * rq;
+    if constexpr (NL == 1) {
+        const T rq = FM<T>::rsq(c.s[0]);
+        c.sq() = c.s[0] * rq;
+        c.ih() = rq * rq;
     }
 }
 
-// LDS layout of a block: NV state arrays and z ([NV + 1][LCM]), then (one
-// layer) sqrt(h) and 1/h of every local cell (pre[2][LCM]), then the
-// per-edge fluctuation slots.
+// Fluctuations |G| T^-1 (...) of both sides of a local edge between the
+// cell records A and B (B == nullptr: a wall), in the x-y frame.
 template <typename T, int NL, bool TR, int NV>
-__device__ __forceinline__ void tri_edge_flux(const T *sm, int LCM, int la, int lb, T nx, T ny, T len, T g, T rr,
-                                              T (&Fa)[NV], T (&Fb)[NV], unsigned &bad)
+__device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, const TriCell<T, NL, NV> &CB, bool wall,
+                                              T nx, T ny, T len, T g, T rr, T (&Fa)[NV], T (&Fb)[NV],
+                                              unsigned &bad)
 {
-    const T *pre = sm + (NV + 1) * LCM;
+    const T *A = CA.s, *B = CB.s;
     if constexpr (NL == 1) {
-        const T ha = sm[la], qxa = sm[LCM + la], qya = sm[2 * LCM + la];
-        const T ca = TR ? sm[3 * LCM + la] : T(0);
+        const T ha = A[0], qxa = A[1], qya = A[2];
+        const T ca = TR ? A[3] : T(0);
         const T qna = qxa * nx + qya * ny, qta = -qxa * ny + qya * nx;
         Flux1<T, TR> f;
-        if (lb != 0xFFFF) {
-            const T hb = sm[lb], qxb = sm[LCM + lb], qyb = sm[2 * LCM + lb];
-            const T cb = TR ? sm[3 * LCM + lb] : T(0);
+        if (!wall) {
+            const T hb = B[0], qxb = B[1], qyb = B[2];
+            const T cb = TR ? B[3] : T(0);
             const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-            f = roe1_pre<T, TR>(ha, pre[la], pre[LCM + la], qna, qta, ca, sm[NV * LCM + la], hb, pre[lb],
-                                pre[LCM + lb], qnb, qtb, cb, sm[NV * LCM + lb], g);
+            f = roe1_pre<T, TR>(ha, CA.sq(), CA.ih(), qna, qta, ca, CA.z(), hb, CB.sq(), CB.ih(), qnb, qtb, cb,
+                                CB.z(), g);
         } else {
             f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
         }
@@ -121,26 +142,26 @@ __device__ __forceinline__ void tri_edge_flux(const T *sm, int LCM, int la, int 
             Fb[3] = len * f.bc;
         }
     } else {
-        T L[6], R[6];
+        T L[6], Rs[6];
 #pragma unroll
         for (int l2 = 0; l2 < 2; ++l2) {
-            const T qx = sm[(3 * l2 + 1) * LCM + la], qy = sm[(3 * l2 + 2) * LCM + la];
-            L[3 * l2] = sm[3 * l2 * LCM + la];
+            const T qx = A[3 * l2 + 1], qy = A[3 * l2 + 2];
+            L[3 * l2] = A[3 * l2];
             L[3 * l2 + 1] = qx * nx + qy * ny;
             L[3 * l2 + 2] = -qx * ny + qy * nx;
         }
         Flux2<T> f;
-        if (lb != 0xFFFF) {
+        if (!wall) {
 #pragma unroll
             for (int l2 = 0; l2 < 2; ++l2) {
-                const T qx = sm[(3 * l2 + 1) * LCM + lb], qy = sm[(3 * l2 + 2) * LCM + lb];
-                R[3 * l2] = sm[3 * l2 * LCM + lb];
-                R[3 * l2 + 1] = qx * nx + qy * ny;
-                R[3 * l2 + 2] = -qx * ny + qy * nx;
+                const T qx = B[3 * l2 + 1], qy = B[3 * l2 + 2];
+                Rs[3 * l2] = B[3 * l2];
+                Rs[3 * l2 + 1] = qx * nx + qy * ny;
+                Rs[3 * l2 + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T>(L, sm[NV * LCM + la], R, sm[NV * LCM + lb], g, rr);
+            f = roe2_interior<T>(L, CA.z(), Rs, CB.z(), g, rr);
         } else {
-            f = roe2_wall<T>(L, sm[NV * LCM + la], g, rr);
+            f = roe2_wall<T>(L, CA.z(), g, rr);
         }
         if (f.nonhyp) bad |= FLAG_NONHYPERBOLIC;
 #pragma unroll
@@ -155,53 +176,53 @@ __device__ __forceinline__ void tri_edge_flux(const T *sm, int LCM, int la, int 
     }
 }
 
-// Eq. (5) speed |G| ||D||_inf of a local edge from the LDS states.
+// Eq. (5) speed |G| ||D||_inf of a local edge between cells CA and CB.
 template <typename T, int NL, int NV>
-__device__ __forceinline__ T tri_edge_speed(const T *sm, int LCM, int la, int lb, T nx, T ny, T len, T g, T rr,
-                                            unsigned &bad)
+__device__ __forceinline__ T tri_edge_speed(const TriCell<T, NL, NV> &CA, const TriCell<T, NL, NV> &CB, bool wall,
+                                            T nx, T ny, T len, T g, T rr, unsigned &bad)
 {
+    const T *A = CA.s, *B = CB.s;
     T sp;
     if constexpr (NL == 1) {
-        const T *pre = sm + (NV + 1) * LCM;
-        const T ha = sm[la], qna = sm[LCM + la] * nx + sm[2 * LCM + la] * ny;
-        if (lb != 0xFFFF) {
-            const T hb = sm[lb], qnb = sm[LCM + lb] * nx + sm[2 * LCM + lb] * ny;
-            const T sa = pre[la], sb = pre[lb];
+        const T ha = A[0], qna = A[1] * nx + A[2] * ny;
+        if (!wall) {
+            const T hb = B[0], qnb = B[1] * nx + B[2] * ny;
+            const T sa = CA.sq(), sb = CB.sq();
             // u_Roe = (sa ua + sb ub) / (sa + sb), s u = qn sqrt(h) / h
-            const T ubar = (qna * sa * pre[LCM + la] + qnb * sb * pre[LCM + lb]) * FM<T>::rcp(sa + sb);
+            const T ubar = (qna * sa * CA.ih() + qnb * sb * CB.ih()) * FM<T>::rcp(sa + sb);
             sp = fabs(ubar) + FM<T>::sqrt(g * T(0.5) * (ha + hb));
         } else {
             sp = FM<T>::sqrt(g * ha);
         }
     } else {
-        T L[6], R[6];
+        T L[6], Rs[6];
 #pragma unroll
         for (int l2 = 0; l2 < 2; ++l2) {
-            L[3 * l2] = sm[3 * l2 * LCM + la];
-            L[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + la] * nx + sm[(3 * l2 + 2) * LCM + la] * ny;
+            L[3 * l2] = A[3 * l2];
+            L[3 * l2 + 1] = A[3 * l2 + 1] * nx + A[3 * l2 + 2] * ny;
             L[3 * l2 + 2] = T(0);
         }
         T pa[4], pb[4];
         roe2_cellpre(L, pa);
-        if (lb != 0xFFFF) {
+        if (!wall) {
 #pragma unroll
             for (int l2 = 0; l2 < 2; ++l2) {
-                R[3 * l2] = sm[3 * l2 * LCM + lb];
-                R[3 * l2 + 1] = sm[(3 * l2 + 1) * LCM + lb] * nx + sm[(3 * l2 + 2) * LCM + lb] * ny;
-                R[3 * l2 + 2] = T(0);
+                Rs[3 * l2] = B[3 * l2];
+                Rs[3 * l2 + 1] = B[3 * l2 + 1] * nx + B[3 * l2 + 2] * ny;
+                Rs[3 * l2 + 2] = T(0);
             }
-            roe2_cellpre(R, pb);
+            roe2_cellpre(Rs, pb);
         } else { // mirror state
-            R[0] = L[0];
-            R[1] = -L[1];
-            R[3] = L[3];
-            R[4] = -L[4];
-            R[2] = R[5] = T(0);
+            Rs[0] = L[0];
+            Rs[1] = -L[1];
+            Rs[3] = L[3];
+            Rs[4] = -L[4];
+            Rs[2] = Rs[5] = T(0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) pb[q] = pa[q];
         }
         bool nh2 = false;
-        sp = roe2_speed<T>(L, pa, R, pb, g, rr, nh2);
+        sp = roe2_speed<T>(L, pa, Rs, pb, g, rr, nh2);
         if (nh2) bad |= FLAG_NONHYPERBOLIC;
     }
     return len * sp;
@@ -240,11 +261,13 @@ template <typename T, int NL, bool TR, bool DT0, int RD, int NT>
 __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
+    using Rec = TriRec<NL, NV>;
+    using Cell = TriCell<T, NL, NV>;
+    constexpr int ER = Rec::ER;
     extern __shared__ double smem_d[];
-    T *sm = reinterpret_cast<T *>(smem_d);
+    T *sm = reinterpret_cast<T *>(smem_d); // cell records
     const int LCM = A.lc_max, EM = A.e_max;
-    T *pre = sm + (NV + 1) * LCM;          // one layer: sqrt(h), 1/h at pre[l], pre[LCM + l]
-    T *fl = pre + (NL == 1 ? 2 : 0) * LCM; // fluctuation slots: side s, var v of edge e at fl[(s * NV + v) * EM + e]
+    T *fl = sm + (Rec::SA + Rec::AX) * LCM; // side s, var v of edge e at fl[s ER EM + ER e + v]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = blockIdx.x;
@@ -323,9 +346,11 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
         if (l < LC) {
+            const Cell c(sm, LCM, l);
 #pragma unroll
-            for (int v = 0; v <= NV; ++v) sm[v * LCM + l] = st[m][v];
-            tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
+            for (int v = 0; v < NV; ++v) c.s[v] = st[m][v];
+            c.z() = st[m][NV];
+            tri_cellpre<T, NL, NV>(c);
         }
     }
     // unit normal and length of each of this thread's edges from |G| eta
@@ -346,13 +371,16 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
         for (int m = 0; m < RD; ++m) {
             const int k = tid + m * NT;
             if (k < ne) {
+                const unsigned lb = eab[m] >> 16;
+                const bool wall = lb == 0xFFFFu;
                 T Fa[NV], Fb[NV];
-                tri_edge_flux<T, NL, TR, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
-                                             eny[m], elen[m], g, rr, Fa, Fb, bad);
+                tri_edge_flux<T, NL, TR, NV>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)), Cell(sm, LCM, wall ? 0 : (int)lb),
+                                             wall, enx[m], eny[m], elen[m], g, rr, Fa, Fb, bad);
+                T *fa = fl + ER * k, *fb = fl + ER * (EM + k);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    fl[v * EM + k] = Fa[v];
-                    fl[(NV + v) * EM + k] = Fb[v];
+                    fa[v] = Fa[v];
+                    fb[v] = Fb[v];
                 }
             }
         }
@@ -360,7 +388,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 
         dtd = wave_min(dpart);
         // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
-        // (a slot is side * NV * EM + edge: variable v of it sits v * EM on)
+        // (a slot is the offset of a side's record: (side EM + edge) ER)
 #pragma unroll
         for (int m = 0; m < RD; ++m) {
             const int l = tid + m * NT;
@@ -372,12 +400,13 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
                 for (int j = 0; j < 3; ++j) {
                     const T *f = fl + ((unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu);
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) acc[v] += f[v * EM];
+                    for (int v = 0; v < NV; ++v) acc[v] += f[v];
                 }
                 const T fct = (T)dtd * cia[m];
+                const Cell c(sm, LCM, l);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) sm[v * LCM + l] -= fct * acc[v];
-                tri_cellpre<T, NL, NV>(sm, pre, LCM, l);
+                for (int v = 0; v < NV; ++v) c.s[v] -= fct * acc[v];
+                tri_cellpre<T, NL, NV>(c);
             }
         }
         __syncthreads();
@@ -390,10 +419,13 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     for (int m = 0; m < RD; ++m) {
         const int k = tid + m * NT;
         if (k < es0) {
-            const T sp = tri_edge_speed<T, NL, NV>(sm, LCM, (int)(eab[m] & 0xFFFFu), (int)(eab[m] >> 16), enx[m],
-                                                   eny[m], elen[m], g, rr, bad);
-            fl[k] = sp;
-            fl[NV * EM + k] = sp;
+            const unsigned lb = eab[m] >> 16;
+            const bool wall = lb == 0xFFFFu;
+            const T sp = tri_edge_speed<T, NL, NV>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)),
+                                                   Cell(sm, LCM, wall ? 0 : (int)lb), wall, enx[m], eny[m], elen[m],
+                                                   g, rr, bad);
+            fl[ER * k] = sp;
+            fl[ER * (EM + k)] = sp;
         }
     }
     __syncthreads();
@@ -411,13 +443,14 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
             rate = fmax(rate, cia[m] * S);
             if (!DT0) {
                 bool badv = false;
+                const T *c = sm + l * Rec::SA;
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    const T x = sm[v * LCM + l];
+                    const T x = c[v];
                     st32(A.out[v], ubase + (uint32_t)l) = x;
                     badv |= !isfinite(x);
                 }
-                if (!(sm[l] > T(0)) || (NL == 2 && !(sm[3 * LCM + l] > T(0)))) bad |= FLAG_DEPTH;
+                if (!(c[0] > T(0)) || (NL == 2 && !(c[3] > T(0)))) bad |= FLAG_DEPTH;
                 if (badv) bad |= FLAG_NONFINITE;
             }
         }
@@ -542,11 +575,20 @@ hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
     return f32 ? tri_batch_t<float, 1, false>(c, nsteps, cfl) : tri_batch_t<double, 1, false>(c, nsteps, cfl);
 }
 
-// LDS bytes a block size needs (for choosing B and the launch attribute)
+// LDS bytes a block size needs (for choosing B and the launch attribute):
+// the cell records, then two fluctuation records per edge (TriRec)
+template <int NL, int NV> static size_t tri_lds_rec(size_t rs, int lc_max, int e_max)
+{
+    using R = TriRec<NL, NV>;
+    return ((size_t)(R::SA + R::AX) * lc_max + (size_t)2 * R::ER * e_max) * rs;
+}
 size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max)
 {
-    const int npre = nv == 6 ? 0 : 2; // per-cell sqrt(h), 1/h (one layer only)
-    return ((size_t)(nv + 1 + npre) * lc_max + (size_t)2 * nv * e_max) * rs;
+    return nv == 6 ? tri_lds_rec<2, 6>(rs, lc_max, e_max)
+                   : nv == 4 ? tri_lds_rec<1, 4>(rs, lc_max, e_max) : tri_lds_rec<1, 3>(rs, lc_max, e_max);
 }
+
+// Reals per edge fluctuation record (the host encodes slots with it).
+int tri_edge_rec(int nv) { return nv | 1; }
 
 } // namespace swe

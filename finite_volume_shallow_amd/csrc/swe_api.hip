@@ -157,11 +157,13 @@ template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
     c->tb.e_gx = reals(hb.e_gx);
     c->tb.e_gy = reals(hb.e_gy);
     c->tb.iarea = reals(hb.iarea);
-    // slots as the kernel addresses its fluctuation LDS: side * nv * e_max + edge
+    // slots as the kernel addresses its fluctuation records:
+    // (side e_max + edge) er, er = reals per record
+    const unsigned er = (unsigned)tri_edge_rec(c->nv);
     std::vector<uint16_t> enc(hb.slots.size(), 0);
     for (size_t i = 0; i < hb.slots.size(); ++i)
         if (i % 4 != 3)
-            enc[i] = (uint16_t)((hb.slots[i] & 1u) * (unsigned)(c->nv * hb.e_max) + (hb.slots[i] >> 1));
+            enc[i] = (uint16_t)(((hb.slots[i] & 1u) * (unsigned)hb.e_max + (hb.slots[i] >> 1)) * er);
     c->tb.slots = (uint16_t *)dev_alloc(c, enc.size() * sizeof(uint16_t));
     upload_raw(c, c->tb.slots, enc.data(), enc.size() * sizeof(uint16_t));
 }
@@ -280,11 +282,12 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             if (st != SWE_OK) throw Fail{st};
             // 512 threads per workgroup; blocks of 288 cells (one layer) or
             // 192 (two layers, whose per-cell and per-edge LDS is twice as
-            // large), fewer if the LDS of a block would exceed 64 KiB or its
-            // local cells and edges two rounds of the threads
+            // large), fewer if the LDS of a block would exceed 64 KiB (80 KiB
+            // for two layers, whose registers allow two blocks per CU
+            // anyway) or its local cells and edges two rounds of the threads
             c->tb.nt = 512;
             int B = c->nv == 6 ? 192 : 288;
-            size_t lds_cap = 65536;
+            size_t lds_cap = c->nv == 6 ? 81920 : 65536;
             if (const char *e = std::getenv("SWE_TRI_B")) { // tuning overrides
                 const int v = std::atoi(e);
                 if (v >= 64 && v <= 512 && v % 32 == 0) B = v;
@@ -299,7 +302,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 for (int b = 0; b < hb.nblocks; ++b) upd = std::max(upd, hb.slot_off[b + 1] - hb.slot_off[b]);
                 const int cap = (c->tb.nt == 256 ? 3 : 2) * c->tb.nt;
                 const bool fits = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= lds_cap &&
-                                  2 * c->nv * hb.e_max <= 0xFFFF &&
+                                  2 * tri_edge_rec(c->nv) * hb.e_max <= 0xFFFF &&
                                   std::max(std::max(hb.lc_max, hb.e_max), upd) <= cap;
                 if (fits) break;
                 if (B <= 128) {

@@ -135,5 +135,6 @@ hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl);
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl);
 hipError_t launch_permute(swe_ctx *c, const void *src, void *dst, int to_internal);
 size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max);
+int tri_edge_rec(int nv);
 
 } // namespace swe

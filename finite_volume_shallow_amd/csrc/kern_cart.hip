@@ -63,6 +63,7 @@ template <typename T, bool TR> struct CartArgs {
     int nx, ny, perx, pery;
     T dx, dy, g, cfl;
     int ty;        // rows per tile
+    int alt;       // odd row blocks march downward
     int nstrips;   // tiles across x
     int ntiles;    // tiles in total
     int per_xcd;   // tiles per XCD band
@@ -195,9 +196,10 @@ template <typename T> __device__ __forceinline__ T &at(T *base, uint32_t k)
 
 // Load a row of W^n for this lane.  CHECK: the row or the column may lie
 // outside the domain (walls); such cells get benign placeholder values.
+// `row` is the grid row; sy = -1 loads the y-mirrored state (qy negated).
 template <bool CHECK, typename T, bool TR>
-__device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int col, bool colok, T &h, T &qx,
-                                         T &qy, T &c, T &z, bool &rowok)
+__device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int col, bool colok, T sy, T &h,
+                                         T &qx, T &qy, T &c, T &z, bool &rowok)
 {
     rowok = true;
     if (row < 0 || row >= A.ny) {
@@ -208,7 +210,7 @@ __device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int 
         const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
         h = at(A.h, k);
         qx = at(A.qx, k);
-        qy = at(A.qy, k);
+        qy = sy * at(A.qy, k);
         c = TR ? at(A.hc, k) : T(0);
         z = at(A.z, k);
     } else {
@@ -234,9 +236,14 @@ template <typename T> struct Ld {
     bool rowok;
 };
 
-// Per-tile constants.
+// Per-tile constants.  A tile marches over "march rows" r = j0-2 ..
+// j0+TY+1; an upward tile visits grid rows in that order (grid row = r), a
+// downward tile in the opposite order (grid row = rbase - r) and works on
+// the y-mirrored state (qy negated on load and store, walls and periodic
+// wrap unchanged), so one code path serves both.  Rows rs0 .. rs1-1 (march
+// numbering) are the tile's own rows that exist in the grid.
 template <typename T> struct TileC {
-    int i, col, j0, rlast, rstore_end;
+    int i, col, j0, rlast, rs0, rs1, rbase;
     bool colok, xwall_lane, wlane;
     T fx, fy, g, lx, ly, g_half;
 };
@@ -247,7 +254,7 @@ constexpr int PREFETCH = 2;
 // One row step of a tile: row r of W^n arrives (cur), row r+PREFETCH is
 // requested into nxt_ld, row r-1 of W^{n+1} is completed and stored, and
 // the Eq. (5) speed sum of row r-2 is closed.  XW / YW: walls in x / y.
-template <typename T, bool TR, bool XW, bool YW>
+template <typename T, bool TR, bool XW, bool YW, bool DN>
 __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
                                          bool &bad_depth, bool &bad_val)
@@ -255,8 +262,8 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     const PC<T> cur = prep(cur_ld.h, cur_ld.qx, cur_ld.qy, cur_ld.c, cur_ld.z);
     const bool currow = cur_ld.rowok; // uniform across the wavefront
     if (r + PREFETCH <= K.rlast)
-        load_row<XW || YW>(A, r + PREFETCH, K.col, K.colok, nxt_ld.h, nxt_ld.qx, nxt_ld.qy, nxt_ld.c, nxt_ld.z,
-                           nxt_ld.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - (r + PREFETCH) : r + PREFETCH, K.col, K.colok, DN ? T(-1) : T(1), nxt_ld.h,
+                           nxt_ld.qx, nxt_ld.qy, nxt_ld.c, nxt_ld.z, nxt_ld.rowok);
     const PC<T> &prev = I.prev;
     const T g = K.g, lx = K.lx, ly = K.ly;
 
@@ -338,16 +345,16 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
             else eys = FM<T>::sqrt(g * (I.nprow ? I.np_h : h1));
             eys *= ly;
             const int rr = r - 2;
-            if (rr >= K.j0 && rr < K.rstore_end && K.wlane) smax = fmax(smax, I.sx_prev + I.sybot_prev + eys);
+            if (rr >= K.rs0 && rr < K.rs1 && K.wlane) smax = fmax(smax, I.sx_prev + I.sybot_prev + eys);
             O.sybot_prev = eys;
         }
         // ---- store row r-1 of the tile
         const int wr = r - 1;
-        if (wr >= K.j0 && wr < K.rstore_end && K.wlane) {
-            const uint32_t k = (uint32_t)wr * (uint32_t)A.nx + (uint32_t)K.i;
+        if (wr >= K.rs0 && wr < K.rs1 && K.wlane) {
+            const uint32_t k = (uint32_t)(DN ? K.rbase - wr : wr) * (uint32_t)A.nx + (uint32_t)K.i;
             at(A.oh, k) = h1;
             at(A.oqx, k) = qx1;
-            at(A.oqy, k) = qy1;
+            at(A.oqy, k) = DN ? -qy1 : qy1;
             if (TR) at(A.ohc, k) = c1;
             bad_depth |= !(h1 > T(0));
             bad_val |= !isfinite(h1 + qx1 + qy1 + c1);
@@ -371,7 +378,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 // tile's rows reach a wall in y.  Tiles with neither (almost all of them)
 // run without any wall code.  Returns the tile's largest Eq. (5) speed sum
 // sum |G| ||D|| (the smallest dt candidate is 2 gamma |V| over it).
-template <typename T, bool TR, bool XW, bool YW>
+template <typename T, bool TR, bool XW, bool YW, bool DN>
 __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, int lane, double dtd, T &smax_out,
                                           unsigned &bad_out)
 {
@@ -394,7 +401,10 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     K.xwall_lane = K.colok != nxtok;
     K.wlane = lane >= 2 && lane < 2 + CART_COLS && K.i >= 0 && K.i < A.nx;
     K.rlast = K.j0 + A.ty + 1; // last row loaded
-    K.rstore_end = min(K.j0 + A.ty, A.ny);
+    K.rbase = 2 * K.j0 + A.ty - 1; // DN: grid row = rbase - march row
+    const int jtop = min(K.j0 + A.ty, A.ny);
+    K.rs0 = DN ? K.rbase - jtop + 1 : K.j0;
+    K.rs1 = DN ? K.j0 + A.ty : jtop;
     K.fx = (T)(dtd / (double)A.dx); // dt |G_x| / |V|, |G_x| = dy
     K.fy = (T)(dtd / (double)A.dy); // dt |G_y| / |V|, |G_y| = dx
     K.g = A.g;
@@ -407,7 +417,7 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     Ld<T> l0, l1, l2, l3;
     {
         Ld<T> p;
-        load_row<XW || YW>(A, K.j0 - 2, K.col, K.colok, p.h, p.qx, p.qy, p.c, p.z, p.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 2) : K.j0 - 2, K.col, K.colok, DN ? T(-1) : T(1), p.h, p.qx, p.qy, p.c, p.z, p.rowok);
         c0.prev = prep(p.h, p.qx, p.qy, p.c, p.z);
         c0.prevrow = p.rowok;
         c0.ax_m = c0.ax_x = c0.ax_y = c0.ax_c = T(0);
@@ -417,24 +427,35 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
         c0.np_b = T(0);
         c0.nprow = false;
         c0.sx_prev = c0.sybot_prev = T(0);
-        load_row<XW || YW>(A, K.j0 - 1, K.col, K.colok, l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
-        load_row<XW || YW>(A, K.j0, K.col, K.colok, l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 1) : K.j0 - 1, K.col, K.colok, DN ? T(-1) : T(1), l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - K.j0 : K.j0, K.col, K.colok, DN ? T(-1) : T(1), l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
     }
     // Four rows per trip: the carried registers alternate between c0 and c1
     // and the four row buffers rotate (row r in one, row r+2 requested into
     // another), so no register is copied between rows.
     int r = K.j0 - 1;
     for (; r + 3 <= K.rlast; r += 4) {
-        row_step<T, TR, XW, YW>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
     }
-    if (r <= K.rlast) row_step<T, TR, XW, YW>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+    if (r <= K.rlast) row_step<T, TR, XW, YW, DN>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
     smax_out = smax;
     bad_out = (bad_depth ? FLAG_DEPTH : 0u) | (bad_val ? FLAG_NONFINITE : 0u);
+}
+
+// The tile variant for its walls (x, y) and march direction.
+template <typename T, bool TR, bool DN>
+__device__ __forceinline__ void cart_tile_dispatch(const CartArgs<T, TR> &A, int tile, int lane, double dtd, bool xw,
+                                                   bool yw, T &smax, unsigned &bad)
+{
+    if (!xw && !yw) cart_tile<T, TR, false, false, DN>(A, tile, lane, dtd, smax, bad);
+    else if (!yw) cart_tile<T, TR, true, false, DN>(A, tile, lane, dtd, smax, bad);
+    else if (!xw) cart_tile<T, TR, false, true, DN>(A, tile, lane, dtd, smax, bad);
+    else cart_tile<T, TR, true, true, DN>(A, tile, lane, dtd, smax, bad);
 }
 
 template <typename T, bool TR>
@@ -464,10 +485,11 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     const bool yw = !A.pery && (j0 - 2 < 0 || j0 + A.ty + 1 >= A.ny);
     T smax;
     unsigned bad;
-    if (!xw && !yw) cart_tile<T, TR, false, false>(A, tile, lane, dtd, smax, bad);
-    else if (!yw) cart_tile<T, TR, true, false>(A, tile, lane, dtd, smax, bad);
-    else if (!xw) cart_tile<T, TR, false, true>(A, tile, lane, dtd, smax, bad);
-    else cart_tile<T, TR, true, true>(A, tile, lane, dtd, smax, bad);
+    // on large grids odd row blocks march downward: neighbouring blocks then
+    // reach the rows they share (each other's halo) at about the same time,
+    // while those rows are still in L2
+    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true>(A, tile, lane, dtd, xw, yw, smax, bad);
+    else cart_tile_dispatch<T, TR, false>(A, tile, lane, dtd, xw, yw, smax, bad);
 
     // the tile's dt candidate 2 gamma |V| / max sum |G| ||D|| (Eq. (5))
     const double dmin = wave_min(smax > T(0) ? (double)(T(2) * A.cfl * A.dx * A.dy / smax) : __builtin_inf());
@@ -560,6 +582,7 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     A.g = (T)c->g;
     A.cfl = (T)cfl;
     A.ty = c->cart_ty;
+    A.alt = c->cart_alt;
     A.nstrips = (int)((c->nx + CART_COLS - 1) / CART_COLS);
     const int nrb = (int)((c->ny + A.ty - 1) / A.ty);
     A.ntiles = A.nstrips * nrb;

@@ -114,16 +114,28 @@ template <typename T> void upload_geometry(swe_ctx *c, const HostEdges &h)
 // the 4096^2 grid: taller tiles lose latency hiding, shorter ones add halo
 // rows), reduced until the grid gives at least 2048 wavefronts (two per SIMD
 // of the 1024 SIMDs), never below 8 rows.  SWE_CART_TY overrides it (tuning).
-int cart_tile_rows(int64_t nx, int64_t ny)
+// Rows per tile of the fused Cartesian kernel (one 64-lane wavefront per
+// tile of 60 columns) and whether odd row blocks march downward.  Large
+// grids: 12 rows, alternating (measured on 4096^2: the halo rows two
+// neighbouring tiles share are then read close together and served from
+// L2).  Smaller grids: 10 rows, halved while there are fewer than 1024
+// tiles, down to 4.
+void cart_tiling(int64_t nx, int64_t ny, int &ty, int &alt)
 {
-    if (const char *e = std::getenv("SWE_CART_TY")) {
-        const int v = std::atoi(e);
-        if (v >= 4 && v <= 4096) return v;
-    }
     const int64_t strips = (nx + 59) / 60;
-    int ty = 32;
-    while (ty > 8 && strips * ((ny + ty - 1) / ty) < 2048) ty /= 2;
-    return ty;
+    if (strips * ((ny + 11) / 12) >= 8192) {
+        ty = 12;
+        alt = 1;
+    } else {
+        ty = 10;
+        while (ty > 4 && strips * ((ny + ty - 1) / ty) < 1024) ty = std::max(4, ty / 2);
+        alt = 0;
+    }
+    if (const char *e = std::getenv("SWE_CART_TY")) { // tuning overrides
+        const int v = std::atoi(e);
+        if (v >= 4 && v <= 4096) ty = v;
+    }
+    if (const char *e = std::getenv("SWE_CART_ALT")) alt = std::atoi(e) != 0;
 }
 
 template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
@@ -336,7 +348,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
         } else if (d->mesh_kind == SWE_MESH_CART) {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
-            c->cart_ty = cart_tile_rows(d->nx, d->ny);
+            cart_tiling(d->nx, d->ny, c->cart_ty, c->cart_alt);
         } else {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             if (c->prec == SWE_F32) upload_blocks<float>(c, hb);

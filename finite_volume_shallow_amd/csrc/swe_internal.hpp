@@ -102,6 +102,7 @@ struct swe_ctx {
 
     // fused Cartesian path
     int cart_ty = 64;            // rows per tile
+    int cart_alt = 0;            // odd row blocks of tiles march downward
     double *cart_part = nullptr; // [3][64] partial dt minima (both fused paths)
 
     // fused triangle path: cells in internal (Morton) order

@@ -28,6 +28,14 @@ def _shuffled_tri(nq, seed=77):
     return w
 
 
+def _periodic_xy(nx, ny):
+    """the 4096^2-style flow on a small grid, periodic in both directions"""
+    w = inputs.config3(nx=nx, ny=ny)
+    w.bc_y = "periodic"
+    w.precision = "f64"
+    return w
+
+
 CASES = {
     # name: (workload factory, steps, precision)
     "c1-dam-break-64x64": (lambda: inputs.config1(), 100, "f64"),
@@ -43,7 +51,38 @@ CASES = {
     "c5-two-layer-13": (lambda: inputs.config5(nq=13), 100, "f64"),
     "c4-tri-shuffled-30": (lambda: _shuffled_tri(30), 60, "f64"),
     "c4-tri-40-f32": (lambda: inputs.config4(nq=40), 100, "f32"),
+    "c3-periodic-xy-67x40-f64": (lambda: _periodic_xy(67, 40), 60, "f64"),
 }
+
+
+# Cartesian tilings the size heuristic picks only on large grids, forced on
+# small ones: (rows per tile, alternate march direction)
+TILINGS = {
+    "c1-dam-break-64x64": [(8, 1), (12, 1)],
+    "c2-hump-96-f64": [(8, 1), (5, 1)],
+    "c3-flow-160x96-f32": [(12, 1), (8, 0)],
+    "c3-ragged-67x33-f64": [(4, 1), (12, 1)],
+    "c1-ragged-131x5": [(4, 1)],
+    "c3-periodic-xy-67x40-f64": [(4, 1), (8, 1), (12, 1)],
+}
+
+
+@pytest.mark.parametrize("tiling", [f"{n}@ty{t}alt{a}" for n, v in TILINGS.items() for t, a in v])
+def test_parity_cart_tilings(tiling, monkeypatch):
+    name, rest = tiling.split("@")
+    ty, alt = rest[2:].split("alt")
+    monkeypatch.setenv("SWE_CART_TY", ty)
+    monkeypatch.setenv("SWE_CART_ALT", alt)
+    make, nsteps, prec = CASES[name]
+    w = make()
+    say(f"[tiling] {name} rows/tile={ty} alternate={alt} steps={nsteps} prec={prec}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    errs = field_errors(got, ref, w.g)
+    assert max(errs) <= tol, errs
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
 
 
 @pytest.mark.parametrize("path", list(PATHS))

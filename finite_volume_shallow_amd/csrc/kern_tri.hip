@@ -462,6 +462,218 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     if (!DT0 && w == 0) tri_book(A, bank, tid, dtd);
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined variant: a persistent workgroup walks a band of blocks
+// and, while it evaluates block i, already has block i+1's global reads in
+// flight (its scalars, halo ids, edge data and slot rows during the flux
+// phase; its cell states during the update and speed phases).  One round of
+// threads covers a block (local cells, edges and updated cells <= NT).
+// ---------------------------------------------------------------------------
+
+// Scalars of one block.
+struct TriBlk {
+    int base, B0, h0, nh, n1, e0, ne, es0, s0;
+};
+
+template <typename T> __device__ __forceinline__ TriBlk tri_blk(const TriArgs<T> &A, int blk)
+{
+    TriBlk b;
+    b.base = blk * A.B; // cells < 2^29
+    b.B0 = min(A.B, (int)A.N - b.base);
+    b.h0 = A.halo_off[blk];
+    b.nh = A.halo_off[blk + 1] - b.h0;
+    b.n1 = A.n1[blk];
+    b.e0 = A.edge_off[blk];
+    b.ne = A.edge_off[blk + 1] - b.e0;
+    b.es0 = A.e_s0[blk];
+    b.s0 = A.slot_off[blk];
+    return b;
+}
+
+// One thread's reads of a block's mesh data: its halo id, its edge (local
+// id pair, |G| eta), its cell's slot row and 1/|V| (indices clamped into the
+// block's ranges; out-of-range threads are masked where the values are used).
+template <typename T> struct TriPre {
+    int32_t hid;
+    uint32_t eab;
+    T gx, gy;
+    uint64_t csl4;
+    T cia;
+};
+
+template <typename T> __device__ __forceinline__ TriPre<T> tri_pre(const TriArgs<T> &A, const TriBlk &b, int tid)
+{
+    TriPre<T> p;
+    p.hid = ld32(A.halo_ids, (uint32_t)(b.h0 + min(max(tid - b.B0, 0), max(b.nh - 1, 0))));
+    const uint32_t k = (uint32_t)(b.e0 + min(tid, b.ne - 1));
+    p.eab = ld32(A.e_ab, k);
+    p.gx = ld32(A.e_gx, k);
+    p.gy = ld32(A.e_gy, k);
+    const uint32_t r = (uint32_t)(b.s0 + min(tid, b.B0 + b.n1 - 1));
+    p.csl4 = ld32(reinterpret_cast<const uint64_t *>(A.slots), r);
+    p.cia = ld32(A.iarea, r);
+    return p;
+}
+
+// The thread's local cell of a block: W^n and z (a valid cell for every
+// thread; only tid < B0 + nh are local cells).
+template <typename T, int NV>
+__device__ __forceinline__ void tri_state(const TriArgs<T> &A, const TriBlk &b, const TriPre<T> &p, int tid,
+                                          T (&st)[NV + 1])
+{
+    const uint32_t gi = tid < b.B0 ? (uint32_t)(b.base + tid) : (uint32_t)p.hid;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) st[v] = ld32(A.in[v], gi);
+    st[NV] = ld32(A.z, gi);
+}
+
+template <typename T, int NL, bool TR, int NT>
+__global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
+{
+    constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
+    using Rec = TriRec<NL, NV>;
+    using Cell = TriCell<T, NL, NV>;
+    constexpr int ER = Rec::ER;
+    extern __shared__ double smem_d[];
+    T *sm = reinterpret_cast<T *>(smem_d);
+    const int LCM = A.lc_max, EM = A.e_max;
+    T *fl = sm + (Rec::SA + Rec::AX) * LCM;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = blockIdx.x;
+    // XCD-aware: the workgroups of XCD w % 8 share its band of consecutive
+    // (Morton-neighbouring) blocks, dealt round-robin
+    const int xcd = w % TRI_XCD, G = (int)gridDim.x / TRI_XCD;
+    const int bend = min((xcd + 1) * A.per_xcd, A.nblocks);
+    int blk = xcd * A.per_xcd + w / TRI_XCD;
+    const int bank = (int)(A.step % 3);
+    const double dpart = A.part[bank * TRI_NPART + lane];
+    const T g = A.g, rr = A.r;
+    unsigned bad = 0;
+    T rate = T(0);
+
+    TriBlk cb{};
+    TriPre<T> cp{};
+    T cst[NV + 1];
+#pragma unroll
+    for (int v = 0; v <= NV; ++v) cst[v] = T(1);
+    if (blk < bend) {
+        cb = tri_blk(A, blk);
+        cp = tri_pre(A, cb, tid);
+        asm volatile("" ::"v"(cp.hid));
+        tri_state<T, NV>(A, cb, cp, tid, cst);
+    }
+    const double dtd = wave_min(dpart);
+
+    while (blk < bend) { // uniform over the workgroup
+        const int nblk = blk + G;
+        const bool more = nblk < bend;
+        const int LC = cb.B0 + cb.nh, nc = cb.B0 + cb.n1;
+
+        // ---- 1. W^n and z into LDS; this thread's edge geometry
+        if (tid < LC) {
+            const Cell c(sm, LCM, tid);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) c.s[v] = cst[v];
+            c.z() = cst[NV];
+            tri_cellpre<T, NL, NV>(c);
+        }
+        const T q = cp.gx * cp.gx + cp.gy * cp.gy;
+        const T rq = FM<T>::rsq(q);
+        const T elen = q * rq, enx = cp.gx * rq, eny = cp.gy * rq;
+        const unsigned la = cp.eab & 0xFFFFu, lb = cp.eab >> 16;
+        const bool wall = lb == 0xFFFFu;
+        __syncthreads();
+
+        // next block's scalars and mesh data
+        TriBlk nb{};
+        TriPre<T> np{};
+        if (more) {
+            nb = tri_blk(A, nblk);
+            np = tri_pre(A, nb, tid);
+        }
+
+        // ---- 2. every edge touching the block or ring 1, once
+        if (tid < cb.ne) {
+            T Fa[NV], Fb[NV];
+            tri_edge_flux<T, NL, TR, NV>(Cell(sm, LCM, (int)la), Cell(sm, LCM, wall ? 0 : (int)lb), wall, enx, eny,
+                                         elen, g, rr, Fa, Fb, bad);
+            T *fa = fl + ER * tid, *fb = fl + ER * (EM + tid);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                fa[v] = Fa[v];
+                fb[v] = Fb[v];
+            }
+        }
+        __syncthreads();
+
+        // next block's cell states (its halo ids have arrived)
+        T nst[NV + 1];
+#pragma unroll
+        for (int v = 0; v <= NV; ++v) nst[v] = T(1);
+        if (more) tri_state<T, NV>(A, nb, np, tid, nst);
+
+        // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
+        if (tid < nc) {
+            T acc[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[v] = T(0);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const T *f = fl + ((unsigned)(cp.csl4 >> (16 * j)) & 0xFFFFu);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[v] += f[v];
+            }
+            const T fct = (T)dtd * cp.cia;
+            const Cell c(sm, LCM, tid);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) c.s[v] -= fct * acc[v];
+            tri_cellpre<T, NL, NV>(c);
+        }
+        __syncthreads();
+
+        // ---- 4. Eq. (5) speeds of W^{n+1} on the edges touching the block
+        if (tid < cb.es0) {
+            const T sp = tri_edge_speed<T, NL, NV>(Cell(sm, LCM, (int)la), Cell(sm, LCM, wall ? 0 : (int)lb), wall,
+                                                   enx, eny, elen, g, rr, bad);
+            fl[ER * tid] = sp;
+            fl[ER * (EM + tid)] = sp;
+        }
+        __syncthreads();
+
+        // ---- 5. the block cells' S_i / |V_i| and W^{n+1} out
+        if (tid < cb.B0) {
+            const T S = fl[(unsigned)cp.csl4 & 0xFFFFu] + fl[(unsigned)(cp.csl4 >> 16) & 0xFFFFu] +
+                        fl[(unsigned)(cp.csl4 >> 32) & 0xFFFFu];
+            rate = fmax(rate, cp.cia * S);
+            const T *c = sm + tid * Rec::SA;
+            bool badv = false;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const T x = c[v];
+                st32(A.out[v], (uint32_t)(cb.base + tid)) = x;
+                badv |= !isfinite(x);
+            }
+            if (!(c[0] > T(0)) || (NL == 2 && !(c[3] > T(0)))) bad |= FLAG_DEPTH;
+            if (badv) bad |= FLAG_NONFINITE;
+        }
+        __syncthreads(); // the LDS is the next block's
+
+        cb = nb;
+        cp = np;
+#pragma unroll
+        for (int v = 0; v <= NV; ++v) cst[v] = nst[v];
+        blk = nblk;
+    }
+
+    // dt candidate of everything this workgroup updated: 2 gamma over the
+    // largest S_i / |V_i| (a correctly rounded quotient is monotone)
+    const double cand = rate > T(0) ? (double)(T(2) * A.cfl / rate) : __builtin_inf();
+    block_min_to_slot(cand, A.part + ((bank + 1) % 3) * TRI_NPART + (w % TRI_NPART));
+    if (bad) atomicOr(A.book.flags, bad);
+    if (w == 0) tri_book(A, bank, tid, dtd);
+}
+
 __global__ void k_tri_init(double *part, StepBook book)
 {
     const int t = threadIdx.x;
@@ -546,6 +758,25 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
     hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
                        tri_args<T>(c, 0, cfl));
+    if constexpr (RD == 1) {
+        if (c->tb.pipe_wgs != 0) {
+            if (lds > 65536)
+                hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (c->tb.pipe_wgs < 0) { // as many workgroups as can be resident at once
+                int per_cu = 0, cus = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT>, NT, lds) !=
+                        hipSuccess ||
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess)
+                    return hipErrorUnknown;
+                c->tb.pipe_wgs = std::max(1, per_cu) * std::max(1, cus);
+            }
+            const dim3 pgrid((unsigned)(TRI_XCD * std::max(1, std::min(c->tb.pipe_wgs / TRI_XCD, per_xcd))));
+            for (int64_t s = 0; s < nsteps; ++s)
+                hipLaunchKernelGGL((k_tri_pipe<T, NL, TR, NT>), pgrid, block, lds, c->stream, tri_args<T>(c, s, cfl));
+            return hipGetLastError();
+        }
+    }
     for (int64_t s = 0; s < nsteps; ++s)
         hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT>), grid, block, lds, c->stream,
                            tri_args<T>(c, s, cfl));

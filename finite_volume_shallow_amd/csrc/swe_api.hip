@@ -292,13 +292,16 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 for (int k = 0; k < 3; ++k) tri_int[3 * i + k] = d->tri[3 * (int64_t)c->perm_host[i] + k];
             st = build_tri_edges(d->nnodes, d->node_xy, d->ncells, tri_int.data(), he, c->err);
             if (st != SWE_OK) throw Fail{st};
-            // 512 threads per workgroup; blocks of 288 cells (one layer) or
-            // 192 (two layers, whose per-cell and per-edge LDS is twice as
-            // large), fewer if the LDS of a block would exceed 64 KiB (80 KiB
-            // for two layers, whose registers allow two blocks per CU
-            // anyway) or its local cells and edges two rounds of the threads
+            // 512 threads per workgroup.  One layer: blocks of 224 cells,
+            // which one round of the threads covers (local cells and edges
+            // <= 512), run by the software-pipelined persistent kernel;
+            // failing that (irregular meshes) 288, 192 or 128 cells with one
+            // workgroup per block.  Two layers (twice the LDS per cell and
+            // edge, registers for two blocks per CU): 192, else 128 cells.
+            // Blocks keep their LDS within 64 KiB (80 KiB for two layers).
             c->tb.nt = 512;
-            int B = c->nv == 6 ? 192 : 288;
+            int B = c->nv == 6 ? 192 : 224;
+            bool pipe = c->nv != 6;
             size_t lds_cap = c->nv == 6 ? 81920 : 65536;
             if (const char *e = std::getenv("SWE_TRI_B")) { // tuning overrides
                 const int v = std::atoi(e);
@@ -307,22 +310,30 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             if (const char *e = std::getenv("SWE_TRI_LDS")) lds_cap = (size_t)std::atol(e);
             if (const char *e = std::getenv("SWE_TRI_NT"))
                 if (std::atoi(e) == 256) c->tb.nt = 256;
+            if (const char *e = std::getenv("SWE_TRI_PIPE")) pipe = std::atoi(e) != 0;
             for (;;) {
                 st = build_tri_blocks(he, c->N, B, hb, c->err);
                 if (st != SWE_OK) throw Fail{st};
                 int upd = 0;
                 for (int b = 0; b < hb.nblocks; ++b) upd = std::max(upd, hb.slot_off[b + 1] - hb.slot_off[b]);
+                const int need = std::max(std::max(hb.lc_max, hb.e_max), upd);
+                const bool lds_ok = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= lds_cap &&
+                                    2 * tri_edge_rec(c->nv) * hb.e_max <= 0xFFFF;
+                if (pipe) {
+                    if (lds_ok && need <= c->tb.nt) break;
+                    pipe = false; // this mesh: one workgroup per block
+                    B = 288;
+                    continue;
+                }
                 const int cap = (c->tb.nt == 256 ? 3 : 2) * c->tb.nt;
-                const bool fits = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= lds_cap &&
-                                  2 * tri_edge_rec(c->nv) * hb.e_max <= 0xFFFF &&
-                                  std::max(std::max(hb.lc_max, hb.e_max), upd) <= cap;
-                if (fits) break;
+                if (lds_ok && need <= cap) break;
                 if (B <= 128) {
                     c->err = "triangle blocks do not fit (mesh too irregular); use SWE_PATH_EDGE";
                     throw Fail{SWE_E_INVAL};
                 }
                 B = B > 192 ? 192 : 128;
             }
+            c->tb.pipe_wgs = pipe ? -1 : 0; // -1: size the persistent grid at the first launch
         }
 
         HIPTRY(hipGetDevice(&c->device));

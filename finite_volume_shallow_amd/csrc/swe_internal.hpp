@@ -112,6 +112,7 @@ struct swe_ctx {
         int B = 0, nblocks = 0, lc_max = 0, e_max = 0;
         int nt = 512;   // threads per workgroup (256 or 512)
         int rounds = 1; // ceil(max(local cells, local edges, updated cells) / nt), <= 3
+        int pipe_wgs = 0; // persistent pipelined workgroups (0: one workgroup per block, -1: not sized yet)
         int32_t *halo_off = nullptr, *halo_ids = nullptr, *n1 = nullptr, *edge_off = nullptr,
                 *e_s0 = nullptr, *slot_off = nullptr;
         uint32_t *e_ab = nullptr;

@@ -85,6 +85,31 @@ def test_parity_cart_tilings(tiling, monkeypatch):
     assert np.abs(dts - rdts).max() <= dtol * rdts.max()
 
 
+# One-layer triangle meshes run the software-pipelined persistent kernel by
+# default; these force the one-workgroup-per-block kernel (and its larger
+# blocks) on them, and the pipelined kernel with a small persistent grid.
+TRI_KERNELS = {"per-block-288": {"SWE_TRI_PIPE": "0", "SWE_TRI_B": "288"},
+               "per-block-128": {"SWE_TRI_PIPE": "0", "SWE_TRI_B": "128"},
+               "pipelined-128": {"SWE_TRI_B": "128"}}
+
+
+@pytest.mark.parametrize("kernel", list(TRI_KERNELS))
+@pytest.mark.parametrize("name", ["c4-tri-36", "c4-tri-ragged-19", "c4-tri-shuffled-30", "c4-tri-40-f32"])
+def test_parity_tri_kernels(name, kernel, monkeypatch):
+    for k, v in TRI_KERNELS[kernel].items():
+        monkeypatch.setenv(k, v)
+    make, nsteps, prec = CASES[name]
+    w = make()
+    say(f"[tri kernel] {name} {kernel} steps={nsteps} prec={prec}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    errs = field_errors(got, ref, w.g)
+    assert max(errs) <= tol, errs
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("name", list(CASES))
 def test_parity(name, path):

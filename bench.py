@@ -233,7 +233,8 @@ def main():
         E = int(np.unique(e, axis=0).shape[0])
     bpc = alg_bytes_per_cell(w, prec, E)
     if used_path == "fused":
-        kernel = "k_cart_fused" if w.kind == "cart" else "k_tri_fused"
+        # one-layer triangle meshes of regular size run the pipelined kernel
+        kernel = "k_cart_fused" if w.kind == "cart" else ("k_tri_pipe" if w.nlayers == 1 else "k_tri_fused")
     else:
         kernel = "k_edge_flux+k_cell_dt+k_cell_update"
     # one fused launch per step: the average launch duration is the time per

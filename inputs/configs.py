@@ -51,6 +51,8 @@ class Workload:
     # triangle meshes
     node_xy: np.ndarray | None = None
     tri: np.ndarray | None = None
+    # "ir" (the IR-Roe scheme) or "classical" (full Roe matrix, one layer)
+    scheme: str = "ir"
 
     @property
     def ncells(self) -> int:

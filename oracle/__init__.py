@@ -40,16 +40,17 @@ def lib():
             _build.build()
         L = ctypes.CDLL(_build.LIB)
         L.or_roe1_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
+        L.or_roe1c_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
         L.or_roe1_wall.argtypes = [_D, ctypes.c_double, _D, _D]
         L.or_roe2_edge.argtypes = [_D, _D, ctypes.c_double, ctypes.c_double, _D, _D, _D]
         L.or_roe2_wall.argtypes = [_D, ctypes.c_double, ctypes.c_double, _D, _D]
         L.or_run_cart.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_int,
-                                  _D, _D, _D, _D, _D, _D, ctypes.c_int]
+                                  _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int]
         L.or_run_tri.argtypes = [ctypes.c_int64, _D, ctypes.c_int64, _I32,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_int,
-                                 _D, _D, _D, _D, _D, _D, ctypes.c_int]
+                                 _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int]
         L.or_run_tri2.argtypes = [ctypes.c_int64, _D, ctypes.c_int64, _I32,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                   ctypes.c_int, _D, _D, _D, _D, _D, _D, _D, _D,
@@ -79,6 +80,17 @@ def roe1_edge(L, R, g=9.81):
     L = _f64(L); R = _f64(R)
     phi = np.zeros(4); sp = ctypes.c_double()
     st = lib().or_roe1_edge(_dp(L), _dp(R), g, _dp(phi), ctypes.byref(sp))
+    if st:
+        raise OracleError(st)
+    return phi, sp.value
+
+
+def roe1c_edge(L, R, g=9.81):
+    """Classical Roe flux (four waves, contact waves for the transverse
+    momentum and the pollutant) leaving L for one-layer edge states."""
+    L = _f64(L); R = _f64(R)
+    phi = np.zeros(4); sp = ctypes.c_double()
+    st = lib().or_roe1c_edge(_dp(L), _dp(R), g, _dp(phi), ctypes.byref(sp))
     if st:
         raise OracleError(st)
     return phi, sp.value
@@ -141,12 +153,15 @@ def run(w, nsteps=None, nthreads=None, check=True):
     z = _f64(w.z)
     dts = np.zeros(max(nsteps, 1))
     L = lib()
+    classical = int(getattr(w, "scheme", "ir") == "classical")
+    if classical and w.nlayers != 1:
+        raise ValueError("the classical Roe variant is one-layer only")
     if w.kind == "cart":
         hc = st_arrays[3] if w.ntracers else None
         status = L.or_run_cart(w.nx, w.ny, w.dx, w.dy, int(w.bc_x == "periodic"),
                                int(w.bc_y == "periodic"), w.g, w.cfl, nsteps,
                                _dp(z), _dp(st_arrays[0]), _dp(st_arrays[1]),
-                               _dp(st_arrays[2]), _dp(hc), _dp(dts), nthreads)
+                               _dp(st_arrays[2]), _dp(hc), _dp(dts), nthreads, classical)
     elif w.nlayers == 1:
         xy = _f64(w.node_xy).ravel()
         t = np.ascontiguousarray(w.tri, dtype=np.int32).ravel()
@@ -154,7 +169,7 @@ def run(w, nsteps=None, nthreads=None, check=True):
         status = L.or_run_tri(xy.size // 2, _dp(xy), t.size // 3, t.ctypes.data_as(_I32),
                               w.g, w.cfl, nsteps, _dp(z), _dp(st_arrays[0]),
                               _dp(st_arrays[1]), _dp(st_arrays[2]), _dp(hc), _dp(dts),
-                              nthreads)
+                              nthreads, classical)
     else:
         xy = _f64(w.node_xy).ravel()
         t = np.ascontiguousarray(w.tri, dtype=np.int32).ravel()

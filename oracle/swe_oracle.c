@@ -43,6 +43,14 @@
  *    wave speeds come from the same edge pass as the fluxes), dt = min_i of
  *    2 gamma |V_i| / sum_j |G_ij| ||D_ij||_inf over all cells.
  *
+ * Classical Roe variant (one layer, selected per run): the full Roe matrix
+ * of the edge-normal system in (h, q_n, q_t, hc) -- its transverse momentum
+ * and pollutant rows carry contact waves of speed u_Roe -- upwinded with
+ * P^- = K (1/2 (I - sgn D)) K^-1 on all four waves, in place of the IR-Roe
+ * step 3 (transverse momentum and pollutant upwinded by the sign of the mass
+ * flux).  The pages contrast the two schemes; the classical one is the
+ * reference the IR-Roe method improves on.  Same walls and same Eq. (5).
+ *
  * The flux is evaluated per cell from that cell's own side, literally as in
  * Eq. (4): every interior edge is therefore computed twice, once from each
  * side, with the outward normal of the cell being updated.
@@ -120,6 +128,56 @@ int or_roe1_edge(const double *L, const double *R, double g, double *phi,
     phi[2] = f0 * ustar;
     phi[3] = f0 * cstar;
     *speed = fmax(fabs(lam1), fabs(lam2));
+    return OR_OK;
+}
+
+/* Classical Roe flux for the same edge states.  Roe matrix of the system
+ * (h, q_n, q_t, hc) with flux (q_n, q_n^2/h + g h^2/2, q_n q_t/h, q_n hc/h)
+ * at the Roe state (u, v, C Roe averages of the normal and transverse
+ * velocities and the concentration, c^2 = g hbar):
+ *   A = [[0, 1, 0, 0], [c^2 - u^2, 2u, 0, 0], [-u v, v, u, 0], [-u C, C, 0, u]]
+ * eigenvalues u - c, u, u, u + c with right eigenvectors
+ *   r1 = (1, u - c, v, C), r2 = (0, 0, 1, 0), r3 = (0, 0, 0, 1), r4 = (1, u + c, v, C).
+ * X = F(W_R) - F(W_L) - S (H_R - H_L); alpha = K^-1 X; Phi = F(W_L) + P^- X. */
+int or_roe1c_edge(const double *L, const double *R, double g, double *phi,
+                  double *speed)
+{
+    double hL = L[0], qL = L[1], tL = L[2], cL = L[3], HL = L[4];
+    double hR = R[0], qR = R[1], tR = R[2], cR = R[3], HR = R[4];
+    if (!(hL > 0.0) || !(hR > 0.0)) return OR_DEPTH;
+
+    double uL = qL / hL, uR = qR / hR, vL = tL / hL, vR = tR / hR;
+    double kL = cL / hL, kR = cR / hR; /* concentrations */
+    double sL = sqrt(hL), sR = sqrt(hR);
+    double ubar = (sL * uL + sR * uR) / (sL + sR);
+    double vbar = (sL * vL + sR * vR) / (sL + sR);
+    double Cbar = (sL * kL + sR * kR) / (sL + sR);
+    double hbar = 0.5 * (hL + hR);
+    double c = sqrt(g * hbar);
+    double lam[4] = {ubar - c, ubar, ubar, ubar + c};
+
+    double FL[4] = {qL, qL * qL / hL + 0.5 * g * hL * hL, qL * vL, qL * kL};
+    double FR[4] = {qR, qR * qR / hR + 0.5 * g * hR * hR, qR * vR, qR * kR};
+    double X[4];
+    for (int v = 0; v < 4; ++v) X[v] = FR[v] - FL[v];
+    X[1] -= g * hbar * (HR - HL);
+
+    /* alpha = K^-1 X for K = [r1 r2 r3 r4] */
+    double al[4];
+    al[0] = (lam[3] * X[0] - X[1]) / (lam[3] - lam[0]);
+    al[3] = (X[1] - lam[0] * X[0]) / (lam[3] - lam[0]);
+    al[1] = X[2] - vbar * X[0]; /* rows 3, 4 of K alpha = X: alpha1 + alpha4 = X0 */
+    al[2] = X[3] - Cbar * X[0];
+    double r[4][4] = {{1.0, lam[0], vbar, Cbar},
+                      {0.0, 0.0, 1.0, 0.0},
+                      {0.0, 0.0, 0.0, 1.0},
+                      {1.0, lam[3], vbar, Cbar}};
+    for (int v = 0; v < 4; ++v) phi[v] = FL[v];
+    for (int k = 0; k < 4; ++k) {
+        double w = 0.5 * (1.0 - sgn(lam[k]));
+        for (int v = 0; v < 4; ++v) phi[v] += w * al[k] * r[k][v];
+    }
+    *speed = fmax(fabs(lam[0]), fabs(lam[3]));
     return OR_OK;
 }
 
@@ -402,7 +460,7 @@ static int check_state(int64_t n, int nv, double *const *W)
 int or_run_cart(int nx, int ny, double dx, double dy, int periodic_x,
                 int periodic_y, double g, double cfl, int nsteps,
                 const double *z, double *h, double *qx, double *qy, double *hc,
-                double *dts, int nthreads)
+                double *dts, int nthreads, int classical)
 {
     int64_t N = (int64_t)nx * ny;
     double area = dx * dy;
@@ -443,7 +501,8 @@ int or_run_cart(int nx, int ny, double dx, double dy, int periodic_x,
                     double Rst[5] = {h[m], qx[m] * ex[sd] + qy[m] * ey[sd],
                                      -qx[m] * ey[sd] + qy[m] * ex[sd],
                                      hc ? hc[m] : 0.0, -z[m]};
-                    st = or_roe1_edge(Lst, Rst, g, phi, &sp);
+                    st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)
+                                   : or_roe1_edge(Lst, Rst, g, phi, &sp);
                 }
                 if (st > err) err = st;
                 /* back-rotation T^-1 and accumulation of |G| F^- */
@@ -560,7 +619,7 @@ static int build_tri_cells(int64_t nnodes, const double *xy, int64_t ncells,
 int or_run_tri(int64_t nnodes, const double *xy, int64_t ncells,
                const int32_t *tri, double g, double cfl, int nsteps,
                const double *z, double *h, double *qx, double *qy, double *hc,
-               double *dts, int nthreads)
+               double *dts, int nthreads, int classical)
 {
     or_tri_cell *cells = malloc(sizeof(or_tri_cell) * ncells);
     double *acc = malloc(sizeof(double) * 4 * ncells);
@@ -587,7 +646,8 @@ int or_run_tri(int64_t nnodes, const double *xy, int64_t ncells,
                 } else {
                     double Rst[5] = {h[m], qx[m] * ex + qy[m] * ey, -qx[m] * ey + qy[m] * ex,
                                      hc ? hc[m] : 0.0, -z[m]};
-                    st = or_roe1_edge(Lst, Rst, g, phi, &sp);
+                    st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)
+                                   : or_roe1_edge(Lst, Rst, g, phi, &sp);
                 }
                 if (st > err) err = st;
                 a[0] += C->len[k] * phi[0];

@@ -294,3 +294,103 @@ def test_depth_failure_is_reported():
     with pytest.raises(oracle.OracleError) as e:
         oracle.run(w, nsteps=1)
     assert e.value.code == 2
+
+
+# ------------------------------------------- the classical Roe variant (one layer)
+# The same whole-run properties hold for the classical Roe scheme: its 2x2
+# part and walls equal the IR-Roe scheme's, its contact waves carry the
+# transverse momentum and the pollutant.
+
+def _classical(w):
+    w.scheme = "classical"
+    return w
+
+
+def test_classical_lake_at_rest():
+    w = _classical(inputs.config2(n=64, nsteps=400, hump=False, blob=False))
+    st, _, _ = oracle.run(w)
+    assert np.abs(st[1] / st[0]).max() <= 1e-12 and np.abs(st[2] / st[0]).max() <= 1e-12
+    assert np.abs(st[0] + w.z - 5.0).max() <= 1e-12
+    w = _classical(inputs.config4(nq=20, nsteps=150, still=True))
+    st, _, _ = oracle.run(w)
+    assert np.abs(st[1] / st[0]).max() <= 1e-12 and np.abs(st[2] / st[0]).max() <= 1e-12
+    assert np.abs(st[0] + w.z - 5.0).max() <= 1e-12
+
+
+@pytest.mark.parametrize("case", ["c3", "c4tracer"])
+def test_classical_mass_and_pollutant_conservation(case):
+    if case == "c3":
+        w = _classical(inputs.config3(nx=64, ny=48, nsteps=100))
+        area = np.full(w.ncells, w.dx * w.dy)
+    else:
+        w = _classical(inputs.config4(nq=30, nsteps=60))
+        area = _tri_areas(w)
+        rng = np.random.default_rng(2)
+        w.ntracers = 1
+        w.state.append(w.state[0] * rng.uniform(0, 1, w.ncells))
+    m0 = [_fsum(w.state[v] * area) for v in (0, 3)]
+    st, _, _ = oracle.run(w)
+    for a, v in zip(m0, (0, 3)):
+        assert abs(_fsum(st[v] * area) - a) <= 1e-12 * abs(a)
+
+
+def test_classical_x_momentum_in_flat_periodic_channel():
+    w = _classical(inputs.config3(nx=64, ny=32, nsteps=100, flat=True))
+    scale = _fsum(np.abs(w.state[1]))
+    p0 = _fsum(w.state[1])
+    st, _, _ = oracle.run(w)
+    assert abs(_fsum(st[1]) - p0) <= 1e-12 * scale
+
+
+def test_classical_dam_break_rows_identical_and_equal_to_ir_roe():
+    # no transverse flow: depth and momenta of the two schemes coincide up to
+    # rounding (the 2x2 part is the same); the pollutant differs, carried by
+    # the contact wave (Roe velocity) instead of by the mass flux
+    w = inputs.config1(nsteps=60)
+    a, da, _ = oracle.run(w)
+    b, db, _ = oracle.run(_classical(w.copy()))
+    for x in b:
+        g2 = x.reshape(64, 64)
+        assert (g2 == g2[0]).all()
+    assert (b[2] == 0.0).all()
+    assert np.abs(da - db).max() <= 1e-14 * da.max()
+    for x, y in zip(a[:3], b[:3]):
+        assert np.abs(x - y).max() <= 1e-12 * max(np.abs(x).max(), 1.0)
+    assert np.abs(a[3] - b[3]).max() > 1e-6
+
+
+def test_classical_rotation_invariance_triangles():
+    th = 0.3
+    c, s = math.cos(th), math.sin(th)
+    w = _classical(inputs.config4(nq=16, nsteps=60))
+    rng = np.random.default_rng(9)
+    w.state[1] = rng.uniform(-0.05, 0.05, w.ncells) * w.state[0]
+    w.state[2] = rng.uniform(-0.05, 0.05, w.ncells) * w.state[0]
+    rw = w.copy()
+    x, y = w.node_xy[:, 0], w.node_xy[:, 1]
+    rw.node_xy = np.stack([c * x - s * y + 3.0, s * x + c * y - 1.0], axis=1)
+    rw.state[1] = c * w.state[1] - s * w.state[2]
+    rw.state[2] = s * w.state[1] + c * w.state[2]
+    sa, da, _ = oracle.run(w)
+    sb, db, _ = oracle.run(rw)
+    assert np.abs(da - db).max() <= 1e-12 * da.max()
+    qx, qy = sb[1], sb[2]
+    sb[1], sb[2] = c * qx + s * qy, -s * qx + c * qy
+    for v in range(3):
+        assert np.abs(sa[v] - sb[v]).max() <= 1e-12 * max(np.abs(sa[v]).max(), 1.0)
+
+
+def test_classical_constant_concentration_is_preserved_exactly():
+    w = _classical(inputs.config2(n=48, nsteps=120))
+    w.state[3] = w.state[0].copy()
+    st, _, _ = oracle.run(w)
+    assert (st[3] == st[0]).all()
+
+
+def test_classical_differs_from_ir_roe_with_transverse_flow():
+    # a sheared flow: the contact waves change the transverse momentum
+    w = inputs.config3(nx=48, ny=40, nsteps=40)
+    a, _, _ = oracle.run(w)
+    b, _, _ = oracle.run(_classical(w.copy()))
+    rel = np.abs(a[2] - b[2]).max() / np.abs(a[2]).max()
+    assert 1e-8 < rel < 1e-1

@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
     ap.add_argument("--precision", choices=["f32", "f64"], default=None)
     ap.add_argument("--path", choices=["auto", "edge"], default="auto")
+    ap.add_argument("--scheme", choices=["ir", "classical"], default="ir",
+                    help="numerical flux: IR-Roe (default) or the classical Roe flux (one layer only)")
     ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,6 +195,10 @@ def main():
                           "GBps_read_plus_write": 8 * n / (ms / 1e3) / 1e9}), flush=True)
         return
     w = inputs.make_config(args.config)
+    if args.scheme == "classical" and w.nlayers != 1:
+        print("the classical Roe flux is one-layer only", file=sys.stderr)
+        sys.exit(2)
+    w.scheme = args.scheme
     prec = args.precision or w.precision
     K = args.steps or w.nsteps
     stream = torch.cuda.Stream()
@@ -241,7 +247,9 @@ def main():
     # step (the batch also holds one small dt-prologue launch)
     achieved = bpc * N / (ms_step / 1e3) / 1e9
     src_hash = kernel_source_hash(ROOT)
-    traffic = measured_traffic(kernel, args.config, src_hash)
+    # counters are recorded per kernel instance: the classical-flux kernel is
+    # another instance (its own name in the traffic table)
+    traffic = measured_traffic(kernel + ("-classical" if args.scheme == "classical" else ""), args.config, src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": kernel, "alg_bytes_per_cell": bpc, "src_hash": src_hash}
@@ -258,7 +266,9 @@ def main():
         "vs_baseline": None,
         "dtype": prec,
         "data": "synthetic",
-        "config": {"workload": f"config {args.config}: {WORKLOADS[args.config]}", "cells": N,
+        "config": {"workload": f"config {args.config}: {WORKLOADS[args.config]}"
+                               + (" (classical Roe flux)" if args.scheme == "classical" else ""), "cells": N,
+                   "scheme": args.scheme,
                    "precision": prec, "path": used_path, "simulated_seconds": t_adv},
         "roofline": roofline,
     }

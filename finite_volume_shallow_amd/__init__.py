@@ -18,13 +18,14 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libswe.so")
 
-SWE_ABI_VERSION = 1
+SWE_ABI_VERSION = 2
 SWE_OK, SWE_E_INVAL, SWE_E_NOMEM, SWE_E_HIP, SWE_E_NOSTATE = 0, -1, -2, -3, -4
 SWE_E_DEPTH, SWE_E_NONFINITE, SWE_E_NONHYPERBOLIC = -5, -6, -7
 SWE_MESH_CART, SWE_MESH_TRI = 0, 1
 SWE_F64, SWE_F32 = 0, 1
 SWE_BC_WALL, SWE_BC_PERIODIC = 0, 1
 SWE_PATH_AUTO, SWE_PATH_EDGE, SWE_PATH_FUSED = 0, 1, 2
+SWE_SCHEME_IR_ROE, SWE_SCHEME_ROE = 0, 1
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I32 = ctypes.POINTER(ctypes.c_int32)
@@ -35,6 +36,7 @@ class swe_mesh_desc(ctypes.Structure):
         ("abi_version", ctypes.c_int32), ("mesh_kind", ctypes.c_int32),
         ("nlayers", ctypes.c_int32), ("ntracers", ctypes.c_int32),
         ("precision", ctypes.c_int32), ("path", ctypes.c_int32),
+        ("scheme", ctypes.c_int32),
         ("g", ctypes.c_double), ("r", ctypes.c_double),
         ("nx", ctypes.c_int64), ("ny", ctypes.c_int64),
         ("dx", ctypes.c_double), ("dy", ctypes.c_double),
@@ -181,7 +183,7 @@ def swe_path(ctx):
 # ------------------------------------------------------------------ helpers
 
 def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUTO,
-              g=9.81, r=0.0, nx=0, ny=0, dx=0.0, dy=0.0, bc_x="wall", bc_y="wall",
+              scheme="ir", g=9.81, r=0.0, nx=0, ny=0, dx=0.0, dy=0.0, bc_x="wall", bc_y="wall",
               node_xy=None, tri=None, stream=None):
     """Fill a swe_mesh_desc.  Returns (desc, keepalive) - keep the second
     value referenced until swe_create_mesh returned."""
@@ -192,6 +194,9 @@ def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUT
     d.ntracers = ntracers
     d.precision = SWE_F32 if precision == "f32" else SWE_F64
     d.path = path
+    if scheme not in ("ir", "classical"):
+        raise ValueError(f"unknown scheme {scheme!r}")
+    d.scheme = SWE_SCHEME_ROE if scheme == "classical" else SWE_SCHEME_IR_ROE
     d.g = g
     d.r = r
     keep = []
@@ -215,9 +220,10 @@ def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUT
 def desc_from_workload(w, path=SWE_PATH_AUTO, stream=None, precision=None):
     """Mesh description of an object with the fields of a workload record
     (kind, nlayers, ntracers, precision, g, r, nx, ny, dx, dy, bc_x, bc_y,
-    node_xy, tri)."""
+    node_xy, tri, and optionally scheme)."""
     return mesh_desc(kind=w.kind, nlayers=w.nlayers, ntracers=w.ntracers,
-                     precision=precision or w.precision, path=path, g=w.g, r=w.r,
+                     precision=precision or w.precision, path=path,
+                     scheme=getattr(w, "scheme", "ir"), g=w.g, r=w.r,
                      nx=w.nx, ny=w.ny, dx=w.dx, dy=w.dy, bc_x=w.bc_x, bc_y=w.bc_y,
                      node_xy=w.node_xy, tri=w.tri, stream=stream)
 

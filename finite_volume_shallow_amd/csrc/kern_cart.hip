@@ -128,12 +128,17 @@ template <typename T> struct EF {
 // transverse).  [IR] Sec. 2.2 steps 1-3 with one layer: Roe averages,
 // X = F(W_b) - F(W_a) - S dH, P^- X by the 2x2 eigen-decomposition,
 // the transverse momentum and the pollutant upwinded by the mass flux.
-template <typename T, bool TR>
+// CL: the classical Roe flux of the whole system instead, whose transverse
+// momentum and pollutant rows are contact waves of speed ubar (Roe averages
+// vbar, Cbar of the transverse velocity and the concentration, weighted by
+// sqrt(h) like ubar).
+template <typename T, bool TR, bool CL>
 __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, T hR, T sR, T qR, T uR, T tR,
                                       T cR, T zR, T g)
 {
     EF<T> o;
-    const T ubar = (sL * uL + sR * uR) * FM<T>::rcp(sL + sR);
+    const T isum = FM<T>::rcp(sL + sR);
+    const T ubar = (sL * uL + sR * uR) * isum;
     const T c2 = g * T(0.5) * (hL + hR);
     const T irc = FM<T>::rsq(c2);
     const T c = c2 * irc;
@@ -150,6 +155,22 @@ __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, 
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
+    if (CL) {
+        const T wu = wminus(ubar);
+        const T vbar = (sL * tL + sR * tR) * isum;
+        const T Xt = qR * tR - qL * tL;
+        o.at = vbar * pm0 + wu * (Xt - vbar * X0);
+        o.bt = Xt - o.at;
+        if (TR) {
+            const T cbar = (sL * cL + sR * cR) * isum;
+            const T Xc = qR * cR - qL * cL;
+            o.ac = cbar * pm0 + wu * (Xc - cbar * X0);
+            o.bc = Xc - o.ac;
+        } else {
+            o.ac = o.bc = T(0);
+        }
+        return o;
+    }
     const T phi0 = qL + pm0;
     const bool up = phi0 > T(0);
     o.at = up ? pm0 * tL : phi0 * tR - qL * tL;
@@ -254,7 +275,7 @@ constexpr int PREFETCH = 2;
 // One row step of a tile: row r of W^n arrives (cur), row r+PREFETCH is
 // requested into nxt_ld, row r-1 of W^{n+1} is completed and stored, and
 // the Eq. (5) speed sum of row r-2 is closed.  XW / YW: walls in x / y.
-template <typename T, bool TR, bool XW, bool YW, bool DN>
+template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL>
 __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
                                          bool &bad_depth, bool &bad_val)
@@ -270,7 +291,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     // ---- x-edge (lane, lane+1) of row r
     const T Rh = nxt(cur.h), Rs = nxt(cur.s), Ru = nxt(cur.u), Rv = nxt(cur.v), Rc = nxt(cur.cc),
             Rz = nxt(cur.z), Rq = nxt(cur.qx);
-    EF<T> ex = flux<T, TR>(cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, Rh, Rs, Rq, Ru, Rv, Rc, Rz, g);
+    EF<T> ex = flux<T, TR, CL>(cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, Rh, Rs, Rq, Ru, Rv, Rc, Rz, g);
     if (XW && K.xwall_lane) {
         if (K.colok) { // wall on the right of this lane's cell
             wall(cur.h, cur.qx, cur.v, cur.cc, g, ex.am, ex.an, ex.at, ex.ac);
@@ -293,7 +314,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 
     // ---- y-edge (row r-1, row r): normal (0, 1), qn = qy, ut = -u;
     // back-rotation (m, n, t, c) -> (m, -t, n, c)
-    EF<T> ey = flux<T, TR>(prev.h, prev.s, prev.qy, prev.v, -prev.u, prev.cc, prev.z, cur.h, cur.s, cur.qy, cur.v,
+    EF<T> ey = flux<T, TR, CL>(prev.h, prev.s, prev.qy, prev.v, -prev.u, prev.cc, prev.z, cur.h, cur.s, cur.qy, cur.v,
                            -cur.u, cur.cc, cur.z, g);
     if (YW && I.prevrow != currow) {
         if (I.prevrow) { // wall above row r-1
@@ -378,7 +399,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 // tile's rows reach a wall in y.  Tiles with neither (almost all of them)
 // run without any wall code.  Returns the tile's largest Eq. (5) speed sum
 // sum |G| ||D|| (the smallest dt candidate is 2 gamma |V| over it).
-template <typename T, bool TR, bool XW, bool YW, bool DN>
+template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL>
 __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, int lane, double dtd, T &smax_out,
                                           unsigned &bad_out)
 {
@@ -435,30 +456,30 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     // another), so no register is copied between rows.
     int r = K.j0 - 1;
     for (; r + 3 <= K.rlast; r += 4) {
-        row_step<T, TR, XW, YW, DN>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
     }
-    if (r <= K.rlast) row_step<T, TR, XW, YW, DN>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, CL>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, CL>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, CL>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
     smax_out = smax;
     bad_out = (bad_depth ? FLAG_DEPTH : 0u) | (bad_val ? FLAG_NONFINITE : 0u);
 }
 
 // The tile variant for its walls (x, y) and march direction.
-template <typename T, bool TR, bool DN>
+template <typename T, bool TR, bool DN, bool CL>
 __device__ __forceinline__ void cart_tile_dispatch(const CartArgs<T, TR> &A, int tile, int lane, double dtd, bool xw,
                                                    bool yw, T &smax, unsigned &bad)
 {
-    if (!xw && !yw) cart_tile<T, TR, false, false, DN>(A, tile, lane, dtd, smax, bad);
-    else if (!yw) cart_tile<T, TR, true, false, DN>(A, tile, lane, dtd, smax, bad);
-    else if (!xw) cart_tile<T, TR, false, true, DN>(A, tile, lane, dtd, smax, bad);
-    else cart_tile<T, TR, true, true, DN>(A, tile, lane, dtd, smax, bad);
+    if (!xw && !yw) cart_tile<T, TR, false, false, DN, CL>(A, tile, lane, dtd, smax, bad);
+    else if (!yw) cart_tile<T, TR, true, false, DN, CL>(A, tile, lane, dtd, smax, bad);
+    else if (!xw) cart_tile<T, TR, false, true, DN, CL>(A, tile, lane, dtd, smax, bad);
+    else cart_tile<T, TR, true, true, DN, CL>(A, tile, lane, dtd, smax, bad);
 }
 
-template <typename T, bool TR>
+template <typename T, bool TR, bool CL = false>
 __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
 {
     const int lane = threadIdx.x;
@@ -488,8 +509,8 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     // on large grids odd row blocks march downward: neighbouring blocks then
     // reach the rows they share (each other's halo) at about the same time,
     // while those rows are still in L2
-    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true>(A, tile, lane, dtd, xw, yw, smax, bad);
-    else cart_tile_dispatch<T, TR, false>(A, tile, lane, dtd, xw, yw, smax, bad);
+    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, CL>(A, tile, lane, dtd, xw, yw, smax, bad);
+    else cart_tile_dispatch<T, TR, false, CL>(A, tile, lane, dtd, xw, yw, smax, bad);
 
     // the tile's dt candidate 2 gamma |V| / max sum |G| ||D|| (Eq. (5))
     const double dmin = wave_min(smax > T(0) ? (double)(T(2) * A.cfl * A.dx * A.dy / smax) : __builtin_inf());
@@ -593,7 +614,8 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     return A;
 }
 
-template <typename T, bool TR> static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
+template <typename T, bool TR, bool CL = false>
+static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
     hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
     const T *src = (const T *)c->state[c->cur];
@@ -606,7 +628,7 @@ template <typename T, bool TR> static hipError_t cart_batch_t(swe_ctx *c, int32_
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
         const unsigned grid = (unsigned)(A.per_xcd * NUM_XCD);
-        hipLaunchKernelGGL((k_cart_fused<T, TR>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
+        hipLaunchKernelGGL((k_cart_fused<T, TR, CL>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
     }
     return hipGetLastError();
 }
@@ -614,6 +636,11 @@ template <typename T, bool TR> static hipError_t cart_batch_t(swe_ctx *c, int32_
 hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
+    if (c->classical) {
+        if (c->ntracers)
+            return f32 ? cart_batch_t<float, true, true>(c, nsteps, cfl) : cart_batch_t<double, true, true>(c, nsteps, cfl);
+        return f32 ? cart_batch_t<float, false, true>(c, nsteps, cfl) : cart_batch_t<double, false, true>(c, nsteps, cfl);
+    }
     if (c->ntracers) return f32 ? cart_batch_t<float, true>(c, nsteps, cfl) : cart_batch_t<double, true>(c, nsteps, cfl);
     return f32 ? cart_batch_t<float, false>(c, nsteps, cfl) : cart_batch_t<double, false>(c, nsteps, cfl);
 }

@@ -24,7 +24,8 @@ template <typename T> struct EdgeArrays {
     const T *nx, *ny, *len;
 };
 
-template <typename T, int NL, bool TR>
+// CL: classical Roe flux (one layer) instead of IR-Roe.
+template <typename T, int NL, bool TR, bool CL>
 __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, StatePtrs<T> W,
                                                    const T *__restrict__ z, T g, T r,
                                                    T *__restrict__ out, unsigned *flags)
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, 
             const T hb = W.v[0][b], qxb = W.v[1][b], qyb = W.v[2][b];
             const T cb = TR ? W.v[3][b] : T(0);
             const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-            f = roe1_interior<T, TR>(ha, qna, qta, ca, z[a], hb, qnb, qtb, cb, z[b], g);
+            f = roe1_interior<T, TR, CL>(ha, qna, qta, ca, z[a], hb, qnb, qtb, cb, z[b], g);
         } else {
             f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
         }
@@ -182,7 +183,8 @@ template <typename T> static StatePtrs<T> state_ptrs(swe_ctx *c)
     return p;
 }
 
-template <typename T, int NL, bool TR> static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
+template <typename T, int NL, bool TR, bool CL = false>
+static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
     const int bs = 256;
@@ -190,7 +192,7 @@ template <typename T, int NL, bool TR> static hipError_t edge_step_t(swe_ctx *c,
     StatePtrs<T> W = state_ptrs<T>(c);
     T *out = (T *)c->e_out;
     const dim3 ge((unsigned)((c->E + bs - 1) / bs)), gc((unsigned)((c->N + bs - 1) / bs));
-    hipLaunchKernelGGL((k_edge_flux<T, NL, TR>), ge, dim3(bs), 0, c->stream, c->E, ed, W,
+    hipLaunchKernelGGL((k_edge_flux<T, NL, TR, CL>), ge, dim3(bs), 0, c->stream, c->E, ed, W,
                        (const T *)c->zbed, (T)c->g, (T)c->r, out, c->book.flags);
     hipLaunchKernelGGL((k_cell_dt<T, NV>), gc, dim3(bs), 0, c->stream, c->N, c->E, c->c_off, c->c_edge,
                        (const T *)c->c_area, (const T *)out, (T)cfl, c->book.slots + (step % 3));
@@ -203,6 +205,11 @@ hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
     if (c->nlayers == 2) return f32 ? edge_step_t<float, 2, false>(c, step, cfl) : edge_step_t<double, 2, false>(c, step, cfl);
+    if (c->classical) {
+        if (c->ntracers)
+            return f32 ? edge_step_t<float, 1, true, true>(c, step, cfl) : edge_step_t<double, 1, true, true>(c, step, cfl);
+        return f32 ? edge_step_t<float, 1, false, true>(c, step, cfl) : edge_step_t<double, 1, false, true>(c, step, cfl);
+    }
     if (c->ntracers) return f32 ? edge_step_t<float, 1, true>(c, step, cfl) : edge_step_t<double, 1, true>(c, step, cfl);
     return f32 ? edge_step_t<float, 1, false>(c, step, cfl) : edge_step_t<double, 1, false>(c, step, cfl);
 }

@@ -110,8 +110,9 @@ template <typename T, int NL, int NV> __device__ __forceinline__ void tri_cellpr
 }
 
 // Fluctuations |G| T^-1 (...) of both sides of a local edge between the
-// cell records A and B (B == nullptr: a wall), in the x-y frame.
-template <typename T, int NL, bool TR, int NV>
+// cell records A and B (B == nullptr: a wall), in the x-y frame.  CL: the
+// classical Roe flux (one layer) instead of IR-Roe.
+template <typename T, int NL, bool TR, int NV, bool CL = false>
 __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, const TriCell<T, NL, NV> &CB, bool wall,
                                               T nx, T ny, T len, T g, T rr, T (&Fa)[NV], T (&Fb)[NV],
                                               unsigned &bad)
@@ -126,7 +127,7 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
             const T hb = B[0], qxb = B[1], qyb = B[2];
             const T cb = TR ? B[3] : T(0);
             const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-            f = roe1_pre<T, TR>(ha, CA.sq(), CA.ih(), qna, qta, ca, CA.z(), hb, CB.sq(), CB.ih(), qnb, qtb, cb,
+            f = roe1_pre<T, TR, CL>(ha, CA.sq(), CA.ih(), qna, qta, ca, CA.z(), hb, CB.sq(), CB.ih(), qnb, qtb, cb,
                                 CB.z(), g);
         } else {
             f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
@@ -257,7 +258,7 @@ template <typename T> __device__ __forceinline__ void tri_book(const TriArgs<T> 
 // counts of any block.  Every global load a thread will need in the launch
 // (halo ids, its edges' geometry, its cells' slot lists and 1/|V|) is issued
 // at the start, so the phases after the first barrier only touch LDS.
-template <typename T, int NL, bool TR, bool DT0, int RD, int NT>
+template <typename T, int NL, bool TR, bool DT0, int RD, int NT, bool CL = false>
 __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
                 const unsigned lb = eab[m] >> 16;
                 const bool wall = lb == 0xFFFFu;
                 T Fa[NV], Fb[NV];
-                tri_edge_flux<T, NL, TR, NV>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)), Cell(sm, LCM, wall ? 0 : (int)lb),
+                tri_edge_flux<T, NL, TR, NV, CL>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)), Cell(sm, LCM, wall ? 0 : (int)lb),
                                              wall, enx[m], eny[m], elen[m], g, rr, Fa, Fb, bad);
                 T *fa = fl + ER * k, *fb = fl + ER * (EM + k);
 #pragma unroll
@@ -527,7 +528,7 @@ __device__ __forceinline__ void tri_state(const TriArgs<T> &A, const TriBlk &b, 
     st[NV] = ld32(A.z, gi);
 }
 
-template <typename T, int NL, bool TR, int NT>
+template <typename T, int NL, bool TR, int NT, bool CL = false>
 __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         // ---- 2. every edge touching the block or ring 1, once
         if (tid < cb.ne) {
             T Fa[NV], Fb[NV];
-            tri_edge_flux<T, NL, TR, NV>(Cell(sm, LCM, (int)la), Cell(sm, LCM, wall ? 0 : (int)lb), wall, enx, eny,
+            tri_edge_flux<T, NL, TR, NV, CL>(Cell(sm, LCM, (int)la), Cell(sm, LCM, wall ? 0 : (int)lb), wall, enx, eny,
                                          elen, g, rr, Fa, Fb, bad);
             T *fa = fl + ER * tid, *fb = fl + ER * (EM + tid);
 #pragma unroll
@@ -742,7 +743,9 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     return A;
 }
 
-template <typename T, int NL, bool TR, int RD, int NT>
+// CL: classical Roe flux.  The initial-state dt prologue computes speeds
+// only, which both fluxes share, so it is the IR-Roe instance.
+template <typename T, int NL, bool TR, int RD, int NT, bool CL>
 static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -752,7 +755,7 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     if (lds > 65536) {
         hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, true, RD, NT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT>,
+        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, CL>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     }
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
@@ -761,11 +764,11 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     if constexpr (RD == 1) {
         if (c->tb.pipe_wgs != 0) {
             if (lds > 65536)
-                hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT>,
+                hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT, CL>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (c->tb.pipe_wgs < 0) { // as many workgroups as can be resident at once
                 int per_cu = 0, cus = 0;
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT>, NT, lds) !=
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT, CL>, NT, lds) !=
                         hipSuccess ||
                     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess)
                     return hipErrorUnknown;
@@ -773,35 +776,41 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
             }
             const dim3 pgrid((unsigned)(TRI_XCD * std::max(1, std::min(c->tb.pipe_wgs / TRI_XCD, per_xcd))));
             for (int64_t s = 0; s < nsteps; ++s)
-                hipLaunchKernelGGL((k_tri_pipe<T, NL, TR, NT>), pgrid, block, lds, c->stream, tri_args<T>(c, s, cfl));
+                hipLaunchKernelGGL((k_tri_pipe<T, NL, TR, NT, CL>), pgrid, block, lds, c->stream, tri_args<T>(c, s, cfl));
             return hipGetLastError();
         }
     }
     for (int64_t s = 0; s < nsteps; ++s)
-        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT>), grid, block, lds, c->stream,
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT, CL>), grid, block, lds, c->stream,
                            tri_args<T>(c, s, cfl));
     return hipGetLastError();
 }
 
-template <typename T, int NL, bool TR> static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
+template <typename T, int NL, bool TR, bool CL = false>
+static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
     // 512 threads per workgroup (eight wavefronts: the block's latency is
     // hidden by its own waves as much as by the other blocks on the CU);
     // rounds of threads cover the largest local cell / edge / update counts
     // (checked at create)
     if (c->tb.nt == 512) {
-        if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 512>(c, nsteps, cfl);
-        return tri_batch_rd<T, NL, TR, 2, 512>(c, nsteps, cfl);
+        if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 512, CL>(c, nsteps, cfl);
+        return tri_batch_rd<T, NL, TR, 2, 512, CL>(c, nsteps, cfl);
     }
-    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 256>(c, nsteps, cfl);
-    if (c->tb.rounds <= 2) return tri_batch_rd<T, NL, TR, 2, 256>(c, nsteps, cfl);
-    return tri_batch_rd<T, NL, TR, 3, 256>(c, nsteps, cfl);
+    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 256, CL>(c, nsteps, cfl);
+    if (c->tb.rounds <= 2) return tri_batch_rd<T, NL, TR, 2, 256, CL>(c, nsteps, cfl);
+    return tri_batch_rd<T, NL, TR, 3, 256, CL>(c, nsteps, cfl);
 }
 
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
     if (c->nlayers == 2) return f32 ? tri_batch_t<float, 2, false>(c, nsteps, cfl) : tri_batch_t<double, 2, false>(c, nsteps, cfl);
+    if (c->classical) {
+        if (c->ntracers)
+            return f32 ? tri_batch_t<float, 1, true, true>(c, nsteps, cfl) : tri_batch_t<double, 1, true, true>(c, nsteps, cfl);
+        return f32 ? tri_batch_t<float, 1, false, true>(c, nsteps, cfl) : tri_batch_t<double, 1, false, true>(c, nsteps, cfl);
+    }
     if (c->ntracers) return f32 ? tri_batch_t<float, 1, true>(c, nsteps, cfl) : tri_batch_t<double, 1, true>(c, nsteps, cfl);
     return f32 ? tri_batch_t<float, 1, false>(c, nsteps, cfl) : tri_batch_t<double, 1, false>(c, nsteps, cfl);
 }

@@ -65,13 +65,23 @@ template <typename T, bool TRACER> struct Flux1 {
 };
 
 // As roe1_interior, with sqrt(h) and 1/h of both cells supplied.
-template <typename T, bool TRACER>
+//
+// CL selects the classical Roe flux of the whole edge system
+// (h, qn, qt, hc): its Roe matrix adds to the 2x2 block two contact waves of
+// speed ubar, with eigenvectors e_qt and e_hc, while the acoustic
+// eigenvectors carry the Roe averages vbar, Cbar (sqrt(h)-weighted, like
+// ubar) in those rows.  With alpha_t = X_t - vbar X_0 and
+// alpha_c = X_c - Cbar X_0, the side-a fluctuation of those rows is
+// vbar (P^- X)_0 + w(ubar) alpha_t, and the same with Cbar; mass and normal
+// momentum are those of the IR-Roe flux.
+template <typename T, bool TRACER, bool CL = false>
 __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T qtL, T cL, T zL, T hR, T sR,
                                                       T ihR, T qnR, T qtR, T cR, T zR, T g)
 {
     Flux1<T, TRACER> o;
     const T uL = qnL * ihL, uR = qnR * ihR;
-    const T ubar = (sL * uL + sR * uR) * rcp(sL + sR);
+    const T isum = rcp(sL + sR);
+    const T ubar = (sL * uL + sR * uR) * isum;
     const T hbar = T(0.5) * (hL + hR);
     const T c2 = g * hbar;
     const T irc = FM<T>::rsq(c2);
@@ -90,8 +100,27 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
-    const T phi0 = qnL + pm0; // mass flux through the edge
     const T utL = qtL * ihL, utR = qtR * ihR;
+    if (CL) {
+        const T wu = wminus(ubar);
+        const T vbar = (sL * utL + sR * utR) * isum;
+        const T Xt = qnR * utR - qnL * utL;
+        o.at = vbar * pm0 + wu * (Xt - vbar * X0);
+        o.bt = Xt - o.at;
+        if (TRACER) {
+            const T ccL = cL * ihL, ccR = cR * ihR;
+            const T cbar = (sL * ccL + sR * ccR) * isum;
+            const T Xc = qnR * ccR - qnL * ccL;
+            o.ac = cbar * pm0 + wu * (Xc - cbar * X0);
+            o.bc = Xc - o.ac;
+        } else {
+            o.ac = T(0);
+            o.bc = T(0);
+        }
+        o.speed = fabs(ubar) + c;
+        return o;
+    }
+    const T phi0 = qnL + pm0; // mass flux through the edge
     if (phi0 > T(0)) {
         o.at = pm0 * utL;                    // phi0 utL - qnL utL
         o.bt = qnR * utR - phi0 * utL;       // -(phi0 utL - qnR utR)
@@ -116,12 +145,12 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     return o;
 }
 
-template <typename T, bool TRACER>
+template <typename T, bool TRACER, bool CL = false>
 __device__ __forceinline__ Flux1<T, TRACER> roe1_interior(T hL, T qnL, T qtL, T cL, T zL,
                                                            T hR, T qnR, T qtR, T cR, T zR, T g)
 {
     const T rL = FM<T>::rsq(hL), rR = FM<T>::rsq(hR);
-    return roe1_pre<T, TRACER>(hL, hL * rL, rL * rL, qnL, qtL, cL, zL, hR, hR * rR, rR * rR, qnR, qtR, cR, zR, g);
+    return roe1_pre<T, TRACER, CL>(hL, hL * rL, rL * rL, qnL, qtL, cL, zL, hR, hR * rR, rR * rR, qnR, qtR, cR, zR, g);
 }
 
 // One-layer reflective wall seen from side a.

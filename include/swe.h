@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define SWE_ABI_VERSION 1
+#define SWE_ABI_VERSION 2
 
 typedef struct swe_ctx swe_ctx; /* opaque; owns every device allocation */
 
@@ -57,6 +57,17 @@ enum swe_bc { SWE_BC_WALL = 0, SWE_BC_PERIODIC = 1 };
  * (two layers on a Cartesian grid are rejected anyway). */
 enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2 };
 
+/* Numerical flux.  SWE_SCHEME_IR_ROE: the IR-Roe scheme of [IR] Sec. 2.2 --
+ * the Roe matrix of the normal subsystem (2x2 for one layer, 4x4 for two),
+ * with the transverse momentum and the pollutant carried by the mass flux
+ * and upwinded by its sign.  SWE_SCHEME_ROE: the classical Roe scheme that
+ * [IR] contrasts it with -- the Roe matrix of the whole one-layer edge
+ * system (h, q_n, q_t, hc), whose transverse momentum and pollutant rows are
+ * contact waves of the Roe velocity, upwinded like the other waves.  The
+ * classical scheme is available for one layer only; both use the same walls
+ * and the same Eq. (5) time step. */
+enum swe_scheme { SWE_SCHEME_IR_ROE = 0, SWE_SCHEME_ROE = 1 };
+
 typedef struct swe_mesh_desc {
     int32_t abi_version; /* must be SWE_ABI_VERSION                          */
     int32_t mesh_kind;   /* SWE_MESH_CART or SWE_MESH_TRI                    */
@@ -64,6 +75,7 @@ typedef struct swe_mesh_desc {
     int32_t ntracers;    /* 0 or 1 pollutant (one layer only)                */
     int32_t precision;   /* SWE_F64 or SWE_F32: storage and arithmetic type  */
     int32_t path;        /* enum swe_path                                    */
+    int32_t scheme;      /* enum swe_scheme (classical Roe: one layer only)  */
     double g;            /* gravity, > 0                                     */
     double r;            /* density ratio rho1/rho2 in (0, 1) (two layers)   */
 

@@ -34,9 +34,20 @@ def test_every_declared_symbol_is_exported():
 def test_struct_layout_matches_header():
     # offsets follow the C layout of swe_mesh_desc on x86-64
     d = swe.swe_mesh_desc
-    assert d.g.offset == 24 and d.nx.offset == 40 and d.bc_x.offset == 72
-    assert d.nnodes.offset == 80 and d.node_xy.offset == 96 and d.hip_stream.offset == 112
-    assert ctypes.sizeof(d) == 120
+    assert d.scheme.offset == 24 and d.g.offset == 32 and d.nx.offset == 48
+    assert d.bc_x.offset == 80 and d.nnodes.offset == 88 and d.node_xy.offset == 104
+    assert d.hip_stream.offset == 120 and ctypes.sizeof(d) == 128
+
+
+def test_binding_constants_match_header():
+    # every enum value and the ABI version the binding uses is the header's
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "swe.h")).read()
+    assert int(re.search(r"#define SWE_ABI_VERSION (\d+)", hdr).group(1)) == swe.SWE_ABI_VERSION
+    consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SWE_[A-Z0-9_]+) = (-?\d+)", hdr)}
+    for name in ["SWE_MESH_CART", "SWE_MESH_TRI", "SWE_F64", "SWE_F32", "SWE_BC_WALL", "SWE_BC_PERIODIC",
+                 "SWE_PATH_AUTO", "SWE_PATH_EDGE", "SWE_PATH_FUSED", "SWE_SCHEME_IR_ROE", "SWE_SCHEME_ROE"]:
+        assert consts[name] == getattr(swe, name), name
 
 
 def test_strerror_covers_all_codes():
@@ -85,7 +96,18 @@ def _square_mesh():
     return xy, tri
 
 
-@pytest.mark.parametrize("case", ["clockwise", "node-range", "triple-edge", "two-layer-tracer", "bad-r"])
+def test_create_rejects_bad_scheme():
+    d, keep = _cart()
+    d.scheme = 5
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL and "scheme" in str(e.value)
+    with pytest.raises(ValueError):
+        swe.mesh_desc(kind="cart", nx=4, ny=4, dx=1.0, dy=1.0, scheme="hllc")
+
+
+@pytest.mark.parametrize("case", ["clockwise", "node-range", "triple-edge", "two-layer-tracer", "bad-r",
+                                  "two-layer-classical"])
 def test_create_rejects_bad_triangles(case):
     xy, tri = _square_mesh()
     kw = {}
@@ -102,6 +124,8 @@ def test_create_rejects_bad_triangles(case):
         kw = dict(nlayers=2, ntracers=1, r=0.9)
     elif case == "bad-r":
         kw = dict(nlayers=2, r=1.0)
+    elif case == "two-layer-classical":
+        kw = dict(nlayers=2, r=0.9, scheme="classical")
     d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, **kw)
     with pytest.raises(swe.SweError) as e:
         swe.swe_create_mesh(d)

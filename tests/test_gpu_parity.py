@@ -128,6 +128,86 @@ def test_parity(name, path):
     assert abs(t - rdts.sum()) <= dtol * rdts.sum()
 
 
+def _tri_pollutant(nq, seed=91):
+    """the triangle dam break with a pollutant: concentration a seeded
+    smooth field in [0.2, 1] (no triangle workload carries one)"""
+    w = inputs.config4(nq=nq)
+    rng = np.random.default_rng(seed)
+    xy = w.node_xy[w.tri].mean(axis=1)
+    kx, ky, ph = rng.uniform(1.0, 4.0), rng.uniform(1.0, 4.0), rng.uniform(0, 2 * np.pi)
+    conc = 0.6 + 0.4 * np.sin(2 * np.pi * (kx * xy[:, 0] + ky * xy[:, 1]) / 1000.0 + ph)
+    w.ntracers = 1
+    w.state = w.state + [w.state[0] * conc]
+    return w
+
+
+# The classical Roe flux (contact waves of the Roe velocity for the
+# transverse momentum and the pollutant) on every one-layer case, both paths.
+CLASSICAL = {n: CASES[n] for n in CASES if not n.startswith("c5")}
+CLASSICAL["c4-tri-pollutant-23"] = (lambda: _tri_pollutant(23), 80, "f64")
+CLASSICAL["c4-tri-pollutant-33-f32"] = (lambda: _tri_pollutant(33), 80, "f32")
+
+
+def _classical(make):
+    w = make()
+    w.scheme = "classical"
+    return w
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("name", list(CLASSICAL))
+def test_parity_classical(name, path):
+    make, nsteps, prec = CLASSICAL[name]
+    w = _classical(make)
+    say(f"[classical] {name} path={path} steps={nsteps} prec={prec} cells={w.ncells}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, path=PATHS[path], precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    errs = field_errors(got, ref, w.g)
+    say(f"    field errors {['%.2e' % e for e in errs]}")
+    assert max(errs) <= tol, errs
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+    assert abs(t - rdts.sum()) <= dtol * rdts.sum()
+
+
+@pytest.mark.parametrize("kernel", list(TRI_KERNELS))
+@pytest.mark.parametrize("name", ["c4-tri-pollutant-23", "c4-tri-40-f32"])
+def test_parity_classical_tri_kernels(name, kernel, monkeypatch):
+    for k, v in TRI_KERNELS[kernel].items():
+        monkeypatch.setenv(k, v)
+    make, nsteps, prec = CLASSICAL[name]
+    w = _classical(make)
+    say(f"[classical tri kernel] {name} {kernel} steps={nsteps} prec={prec}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    assert max(field_errors(got, ref, w.g)) <= tol
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+
+
+def test_parity_ir_pollutant_triangles():
+    # the IR-Roe pollutant on triangle meshes (both paths)
+    for path in PATHS:
+        w = _tri_pollutant(23)
+        say(f"[ir pollutant tri] path={path}")
+        got, dts, t = gpu_run(w, nsteps=80, path=PATHS[path])
+        ref, rdts = oracle_reference(w, nsteps=80)
+        assert max(field_errors(got, ref, w.g)) <= FP64_TOL
+        assert np.abs(dts - rdts).max() <= 1e-12 * rdts.max()
+
+
+def test_classical_and_ir_differ_on_gpu():
+    # the two schemes share mass and normal momentum fluxes but not the
+    # pollutant's: after a few steps of a sheared flow they must differ
+    w = inputs.config3(nx=64, ny=40)
+    w.precision = "f64"
+    ir, _, _ = gpu_run(w, nsteps=20)
+    cl, _, _ = gpu_run(_classical(lambda: w.copy()), nsteps=20)
+    assert np.abs(ir[3] - cl[3]).max() > 1e-8 * np.abs(ir[3]).max()
+
+
 def test_config1_symmetry_on_gpu():
     w = inputs.config1()
     say("[sym] config1 rows identical, qy == 0")

@@ -44,6 +44,7 @@ def lib():
         L.or_roe1_wall.argtypes = [_D, ctypes.c_double, _D, _D]
         L.or_roe2_edge.argtypes = [_D, _D, ctypes.c_double, ctypes.c_double, _D, _D, _D]
         L.or_roe2_wall.argtypes = [_D, ctypes.c_double, ctypes.c_double, _D, _D]
+        L.or_roe2c_edge.argtypes = [_D, _D, ctypes.c_double, ctypes.c_double, _D, _D, _D]
         L.or_run_cart.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_int,
@@ -54,7 +55,7 @@ def lib():
         L.or_run_tri2.argtypes = [ctypes.c_int64, _D, ctypes.c_int64, _I32,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                   ctypes.c_int, _D, _D, _D, _D, _D, _D, _D, _D,
-                                  ctypes.c_int]
+                                  ctypes.c_int, ctypes.c_int]
         L.or_tri_geometry.argtypes = [ctypes.c_int64, _D, ctypes.c_int64, _I32,
                                       _I64, _D, _D, _D, _D]
         _lib = L
@@ -117,6 +118,17 @@ def roe2_edge(L, R, g=9.81, r=0.98):
     return phi, sp.value, lam
 
 
+def roe2c_edge(L, R, g=9.81, r=0.98):
+    """Classical Roe flux of two layers (full 6x6 Roe matrix), states and
+    results as roe2_edge."""
+    L = _f64(L); R = _f64(R)
+    phi = np.zeros(6); lam = np.zeros(4); sp = ctypes.c_double()
+    st = lib().or_roe2c_edge(_dp(L), _dp(R), g, r, _dp(phi), ctypes.byref(sp), _dp(lam))
+    if st:
+        raise OracleError(st)
+    return phi, sp.value, lam
+
+
 def roe2_wall(L, g=9.81, r=0.98):
     L = _f64(L)
     phi = np.zeros(6); sp = ctypes.c_double()
@@ -154,8 +166,8 @@ def run(w, nsteps=None, nthreads=None, check=True):
     dts = np.zeros(max(nsteps, 1))
     L = lib()
     classical = int(getattr(w, "scheme", "ir") == "classical")
-    if classical and w.nlayers != 1:
-        raise ValueError("the classical Roe variant is one-layer only")
+    if classical and w.kind == "cart" and w.nlayers != 1:
+        raise ValueError("two layers run on triangle meshes only")
     if w.kind == "cart":
         hc = st_arrays[3] if w.ntracers else None
         status = L.or_run_cart(w.nx, w.ny, w.dx, w.dy, int(w.bc_x == "periodic"),
@@ -175,7 +187,7 @@ def run(w, nsteps=None, nthreads=None, check=True):
         t = np.ascontiguousarray(w.tri, dtype=np.int32).ravel()
         status = L.or_run_tri2(xy.size // 2, _dp(xy), t.size // 3, t.ctypes.data_as(_I32),
                                w.g, w.r, w.cfl, nsteps, _dp(z),
-                               *[_dp(a) for a in st_arrays], _dp(dts), nthreads)
+                               *[_dp(a) for a in st_arrays], _dp(dts), nthreads, classical)
     if check and status:
         raise OracleError(status)
     return st_arrays, dts[:nsteps], status

@@ -50,6 +50,10 @@
  * step 3 (transverse momentum and pollutant upwinded by the sign of the mass
  * flux).  The pages contrast the two schemes; the classical one is the
  * reference the IR-Roe method improves on.  Same walls and same Eq. (5).
+ * Two layers: the full 6x6 Roe matrix of (h1, q1n, q1t, h2, q2n, q2t) --
+ * the 4x4 matrix A_ij of the normal system plus the transverse rows of each
+ * layer, linearised at that layer's Roe averages -- eigen-decomposed as a
+ * whole (K of 6 columns, K alpha = X solved by elimination).
  *
  * The flux is evaluated per cell from that cell's own side, literally as in
  * Eq. (4): every interior edge is therefore computed twice, once from each
@@ -427,6 +431,130 @@ int or_roe2_edge(const double *L, const double *R, double g, double r,
     return OR_OK;
 }
 
+/* Solve K a = x (n <= 6) by Gaussian elimination with partial pivoting. */
+static int solve_n(int n, const double Kin[6][6], const double x[6], double a[6])
+{
+    double K[6][7];
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < n; ++j) K[i][j] = Kin[i][j];
+        K[i][n] = x[i];
+    }
+    for (int c = 0; c < n; ++c) {
+        int piv = c;
+        for (int i = c + 1; i < n; ++i)
+            if (fabs(K[i][c]) > fabs(K[piv][c])) piv = i;
+        if (K[piv][c] == 0.0) return OR_NONHYPERBOLIC;
+        if (piv != c)
+            for (int j = 0; j <= n; ++j) {
+                double t = K[c][j]; K[c][j] = K[piv][j]; K[piv][j] = t;
+            }
+        for (int i = c + 1; i < n; ++i) {
+            double f = K[i][c] / K[c][c];
+            for (int j = c; j <= n; ++j) K[i][j] -= f * K[c][j];
+        }
+    }
+    for (int i = n - 1; i >= 0; --i) {
+        double s = K[i][n];
+        for (int j = i + 1; j < n; ++j) s -= K[i][j] * a[j];
+        a[i] = s / K[i][i];
+    }
+    return OR_OK;
+}
+
+/* Classical Roe flux, two layers: P^- X with the full 6x6 Roe matrix of the
+ * edge-normal system in W6 = (h1, q1n, q1t, h2, q2n, q2t).  Rows h_k and
+ * q_kn are those of A_ij (J_ij - B_ij); the row of q_kt is the Roe
+ * linearisation of its flux q_kn q_kt / h_k, (-u_k v_k, v_k, u_k) on
+ * (h_k, q_kn, q_kt), with v_k the sqrt(h)-weighted average of q_kt / h_k.
+ * The matrix is block triangular (the normal unknowns do not see q_kt), so
+ * its eigenvalues are the four of A_ij and u1, u2; the eigenvectors of
+ * u1, u2 are the unit vectors of q1t, q2t, and those of A_ij's eigenvalues
+ * are A_ij's eigenvectors completed by the q_kt rows of (A6 - lam I) v = 0.
+ * The transverse rows of X carry no bed or coupling term.
+ * L, R, phi, speed, lam: as or_roe2_edge (lam: A_ij's four eigenvalues). */
+int or_roe2c_edge(const double *L, const double *R, double g, double r,
+                  double *phi, double *speed, double *lam)
+{
+    double h1L = L[0], q1L = L[1], t1L = L[2], h2L = L[3], q2L = L[4], t2L = L[5], HL = L[6];
+    double h1R = R[0], q1R = R[1], t1R = R[2], h2R = R[3], q2R = R[4], t2R = R[5], HR = R[6];
+    if (!(h1L > 0.0) || !(h2L > 0.0) || !(h1R > 0.0) || !(h2R > 0.0)) return OR_DEPTH;
+
+    double s1L = sqrt(h1L), s1R = sqrt(h1R), s2L = sqrt(h2L), s2R = sqrt(h2R);
+    double u1 = (s1L * (q1L / h1L) + s1R * (q1R / h1R)) / (s1L + s1R);
+    double u2 = (s2L * (q2L / h2L) + s2R * (q2R / h2R)) / (s2L + s2R);
+    double v1 = (s1L * (t1L / h1L) + s1R * (t1R / h1R)) / (s1L + s1R);
+    double v2 = (s2L * (t2L / h2L) + s2R * (t2R / h2R)) / (s2L + s2R);
+    double h1 = 0.5 * (h1L + h1R), h2 = 0.5 * (h2L + h2R);
+
+    /* A6 = J6 - B6; B6 and the source S6 act on the normal rows only */
+    double A[6][6] = {{0.0, 1.0, 0.0, 0.0, 0.0, 0.0},
+                      {g * h1 - u1 * u1, 2.0 * u1, 0.0, g * h1, 0.0, 0.0},
+                      {-u1 * v1, v1, u1, 0.0, 0.0, 0.0},
+                      {0.0, 0.0, 0.0, 0.0, 1.0, 0.0},
+                      {r * g * h2, 0.0, 0.0, g * h2 - u2 * u2, 2.0 * u2, 0.0},
+                      {0.0, 0.0, 0.0, -u2 * v2, v2, u2}};
+    double B[6][6] = {{0.0}};
+    B[1][3] = -g * h1;
+    B[4][0] = -r * g * h2;
+    double S[6] = {0.0, g * h1, 0.0, 0.0, g * h2, 0.0};
+
+    /* eigenvalues: those of the normal block (rows/columns h1, q1n, h2, q2n) */
+    static const int nb[4] = {0, 1, 3, 4};
+    double A4[4][4], p[5], ev[4];
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) A4[i][j] = A[nb[i]][nb[j]];
+    charpoly4(A4, p);
+    int st = quartic_roots(p, ev);
+    if (st != OR_OK) return st;
+
+    double K[6][6] = {{0.0}}, mu[6];
+    for (int k = 0; k < 4; ++k) {
+        double M[4][4], v[4];
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j) M[i][j] = A4[i][j] - (i == j ? ev[k] : 0.0);
+        null_vector4(M, v);
+        for (int i = 0; i < 4; ++i) K[nb[i]][k] = v[i];
+        /* q_kt rows of (A6 - lam I) v = 0 */
+        for (int t = 2; t <= 5; t += 3) {
+            double sum = 0.0;
+            for (int j = 0; j < 6; ++j)
+                if (j != t) sum += A[t][j] * K[j][k];
+            K[t][k] = sum / (ev[k] - A[t][t]);
+        }
+        mu[k] = ev[k];
+    }
+    K[2][4] = 1.0;
+    mu[4] = u1;
+    K[5][5] = 1.0;
+    mu[5] = u2;
+
+    double FL[6] = {q1L, q1L * q1L / h1L + 0.5 * g * h1L * h1L, q1L * t1L / h1L,
+                    q2L, q2L * q2L / h2L + 0.5 * g * h2L * h2L, q2L * t2L / h2L};
+    double FR[6] = {q1R, q1R * q1R / h1R + 0.5 * g * h1R * h1R, q1R * t1R / h1R,
+                    q2R, q2R * q2R / h2R + 0.5 * g * h2R * h2R, q2R * t2R / h2R};
+    double dW[6] = {h1R - h1L, q1R - q1L, t1R - t1L, h2R - h2L, q2R - q2L, t2R - t2L};
+    double X[6];
+    for (int i = 0; i < 6; ++i) {
+        double BdW = 0.0;
+        for (int j = 0; j < 6; ++j) BdW += B[i][j] * dW[j];
+        X[i] = FR[i] - FL[i] - BdW - S[i] * (HR - HL);
+    }
+    double alpha[6];
+    st = solve_n(6, K, X, alpha);
+    if (st != OR_OK) return st;
+    for (int i = 0; i < 6; ++i) phi[i] = FL[i];
+    double m = 0.0;
+    for (int k = 0; k < 6; ++k) {
+        double w = 0.5 * (1.0 - sgn(mu[k]));
+        for (int i = 0; i < 6; ++i) phi[i] += w * alpha[k] * K[i][k];
+        m = fmax(m, fabs(mu[k]));
+    }
+    *speed = m;
+    if (lam)
+        for (int k = 0; k < 4; ++k) lam[k] = ev[k];
+    return OR_OK;
+}
+
 /* Reflective wall, two layers: mirror ghost through the same flux, then the
  * mass (and hence transverse) fluxes set to exactly zero. */
 int or_roe2_wall(const double *L, double g, double r, double *phi, double *speed)
@@ -684,7 +812,8 @@ int or_run_tri(int64_t nnodes, const double *xy, int64_t ncells,
 int or_run_tri2(int64_t nnodes, const double *xy, int64_t ncells,
                 const int32_t *tri, double g, double r, double cfl, int nsteps,
                 const double *z, double *h1, double *q1x, double *q1y,
-                double *h2, double *q2x, double *q2y, double *dts, int nthreads)
+                double *h2, double *q2x, double *q2y, double *dts, int nthreads,
+                int classical)
 {
     or_tri_cell *cells = malloc(sizeof(or_tri_cell) * ncells);
     double *acc = malloc(sizeof(double) * 6 * ncells);
@@ -714,7 +843,8 @@ int or_run_tri2(int64_t nnodes, const double *xy, int64_t ncells,
                     double Rst[7] = {h1[m], q1x[m] * ex + q1y[m] * ey, -q1x[m] * ey + q1y[m] * ex,
                                      h2[m], q2x[m] * ex + q2y[m] * ey, -q2x[m] * ey + q2y[m] * ex,
                                      -z[m]};
-                    st = or_roe2_edge(Lst, Rst, g, r, phi, &sp, NULL);
+                    st = classical ? or_roe2c_edge(Lst, Rst, g, r, phi, &sp, NULL)
+                                   : or_roe2_edge(Lst, Rst, g, r, phi, &sp, NULL);
                 }
                 if (st > err) err = st;
                 if (st != OR_OK) continue;

@@ -352,3 +352,129 @@ def test_roe1c_contact_wave_upwinds_by_roe_velocity():
     ref = L[1] * L[2] / L[0] + v * P0 + (X[2] - v * X[0])
     assert cl[2] == pytest.approx(ref, rel=1e-13)
     assert abs(cl[2] - ir[2]) > 1e-3
+
+
+def test_roe1c_test_matrix_has_the_roe_property():
+    # the matrix the classical pins compare against is itself pinned: a Roe
+    # matrix maps the jump of the state to the jump of the flux exactly
+    # (normal row: up to the hydrostatic term g hbar dh, which is exact too)
+    rng = np.random.default_rng(23)
+    for L, R in _random_states1(rng, 500):
+        A, h = _classical_matrix(L, R)
+        dW = (R - L)[:4]
+        dF = _F4(R) - _F4(L)
+        assert np.abs(A @ dW - dF).max() <= 1e-12 * (np.abs(dF).max() + 1.0)
+
+
+# ------------------------------------------------------- classical, 2 layers
+
+def _F6(s):
+    """flux of (h1, q1n, q1t, h2, q2n, q2t) along the normal (no coupling)"""
+    return np.array([s[1], s[1] ** 2 / s[0] + 0.5 * G * s[0] ** 2, s[1] * s[2] / s[0],
+                     s[4], s[4] ** 2 / s[3] + 0.5 * G * s[3] ** 2, s[4] * s[5] / s[3]])
+
+
+def _A6(L, R, r):
+    """Full two-layer Roe matrix J6 - B6 on (h1, q1n, q1t, h2, q2n, q2t) and
+    the parts of the path-conservative jump: returns (A6, B6, S6)."""
+    rows = {}
+    for k, o in enumerate((0, 3)):
+        sL, sR = math.sqrt(L[o]), math.sqrt(R[o])
+        avg = lambda a, b: (sL * a + sR * b) / (sL + sR)
+        rows[k] = (avg(L[o + 1] / L[o], R[o + 1] / R[o]), avg(L[o + 2] / L[o], R[o + 2] / R[o]),
+                   0.5 * (L[o] + R[o]))
+    (u1, v1, h1), (u2, v2, h2) = rows[0], rows[1]
+    J = np.zeros((6, 6))
+    J[0, 1] = 1.0
+    J[1, 0], J[1, 1] = G * h1 - u1 * u1, 2 * u1
+    J[2, 0], J[2, 1], J[2, 2] = -u1 * v1, v1, u1
+    J[3, 4] = 1.0
+    J[4, 3], J[4, 4] = G * h2 - u2 * u2, 2 * u2
+    J[5, 3], J[5, 4], J[5, 5] = -u2 * v2, v2, u2
+    B = np.zeros((6, 6))
+    B[1, 3] = -G * h1
+    B[4, 0] = -r * G * h2
+    S = np.array([0.0, G * h1, 0.0, 0.0, G * h2, 0.0])
+    return J - B, J, B, S
+
+
+def _distinct6(rng, n):
+    # states whose six eigenvalues are real and apart (a library
+    # eigen-decomposition is well conditioned there)
+    out = []
+    for L, R in _random_states2(rng, 3 * n):
+        A, _, _, _ = _A6(L, R, 0.98)
+        lam = np.linalg.eigvals(A)
+        d = np.abs(lam[:, None] - lam[None, :]) + np.eye(6)
+        if np.abs(lam.imag).max() == 0.0 and d.min() > 0.05:
+            out.append((L, R))
+        if len(out) == n:
+            break
+    return out
+
+
+def test_roe2c_test_matrix_has_the_roe_property():
+    rng = np.random.default_rng(31)
+    for L, R in _random_states2(rng, 300):
+        _, J, _, _ = _A6(L, R, 0.98)
+        dW = (R - L)[:6]
+        dF = _F6(R) - _F6(L)
+        assert np.abs(J @ dW - dF).max() <= 1e-12 * (np.abs(dF).max() + 1.0)
+
+
+def test_roe2c_matches_library_eigendecomposition():
+    rng = np.random.default_rng(32)
+    states = _distinct6(rng, 800)
+    assert len(states) >= 400
+    worst = 0.0
+    for L, R in states:
+        phi, sp, _ = oracle.roe2c_edge(L, R, G, 0.98)
+        A, _, B, S = _A6(L, R, 0.98)
+        P, lam = _pminus(A)
+        X = _F6(R) - _F6(L) - B @ (R - L)[:6] - S * (R[6] - L[6])
+        ref = _F6(L) + P @ X
+        scale = np.abs(_F6(L)).max() + np.abs(X).max()
+        worst = max(worst, np.abs(phi - ref).max() / scale)
+        assert sp == pytest.approx(np.abs(lam).max(), rel=1e-10)
+    assert worst < 1e-10
+
+
+def test_roe2c_normal_rows_and_speed_equal_ir_roe():
+    # the normal system (h_k, q_kn) does not see the transverse momenta
+    rng = np.random.default_rng(33)
+    for L, R in _random_states2(rng, 500):
+        a, sa, la = oracle.roe2_edge(L, R, G, 0.98)
+        b, sb, lb = oracle.roe2c_edge(L, R, G, 0.98)
+        n = [0, 1, 3, 4]
+        assert np.abs(a[n] - b[n]).max() <= 1e-12 * (np.abs(a[n]).max() + 1.0)
+        assert sa == sb and np.array_equal(la, lb)
+
+
+def test_roe2c_uniform_transverse_velocity_equals_ir_roe():
+    # with one transverse velocity per layer on both sides, the contact waves
+    # carry nothing and both schemes move q_t with the mass flux
+    rng = np.random.default_rng(34)
+    for L, R in _random_states2(rng, 300):
+        V1, V2 = rng.uniform(-1, 1, 2)
+        L, R = L.copy(), R.copy()
+        for s in (L, R):
+            s[2], s[5] = V1 * s[0], V2 * s[3]
+        a, _, _ = oracle.roe2_edge(L, R, G, 0.98)
+        b, _, _ = oracle.roe2c_edge(L, R, G, 0.98)
+        assert np.abs(a - b).max() <= 1e-11 * (np.abs(a).max() + 1.0)
+
+
+def test_roe2c_consistency_and_pure_shear():
+    s = np.array([1.4, 0.3, -0.2, 2.1, -0.1, 0.5, 0.2])
+    phi, _, _ = oracle.roe2c_edge(s, s, G, 0.9)
+    assert np.abs(phi - _F6(s)).max() <= 1e-14 * np.abs(_F6(s)).max()
+    # same depths and normal discharges, flat bed, only q_t jumps: the
+    # acoustic and internal waves carry nothing, each contact wave takes its
+    # transverse flux from the upwind side of its own layer's velocity
+    L = np.array([1.0, 0.4, 0.7, 2.0, -0.6, -0.3, 0.0])
+    R = np.array([1.0, 0.4, -0.5, 2.0, -0.6, 0.9, 0.0])
+    phi, _, _ = oracle.roe2c_edge(L, R, G, 0.98)
+    FL, FR = _F6(L), _F6(R)
+    assert np.abs(phi[[0, 1, 3, 4]] - FL[[0, 1, 3, 4]]).max() <= 1e-14 * np.abs(FL).max()
+    assert phi[2] == pytest.approx(FL[2], rel=1e-14)      # u1 > 0: from L
+    assert phi[5] == pytest.approx(FR[5], rel=1e-14)      # u2 < 0: from R

@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--precision", choices=["f32", "f64"], default=None)
     ap.add_argument("--path", choices=["auto", "edge"], default="auto")
     ap.add_argument("--scheme", choices=["ir", "classical"], default="ir",
-                    help="numerical flux: IR-Roe (default) or the classical Roe flux (one layer only)")
+                    help="numerical flux: IR-Roe (default) or the classical Roe flux")
     ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -195,9 +195,6 @@ def main():
                           "GBps_read_plus_write": 8 * n / (ms / 1e3) / 1e9}), flush=True)
         return
     w = inputs.make_config(args.config)
-    if args.scheme == "classical" and w.nlayers != 1:
-        print("the classical Roe flux is one-layer only", file=sys.stderr)
-        sys.exit(2)
     w.scheme = args.scheme
     prec = args.precision or w.precision
     K = args.steps or w.nsteps

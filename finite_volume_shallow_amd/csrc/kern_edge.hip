@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, 
                 R[3 * l + 1] = qx * nx + qy * ny;
                 R[3 * l + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T>(L, z[a], R, z[b], g, r);
+            f = roe2_interior<T, CL>(L, z[a], R, z[b], g, r);
         } else {
             f = roe2_wall<T>(L, z[a], g, r);
         }
@@ -204,7 +204,11 @@ static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
 hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
-    if (c->nlayers == 2) return f32 ? edge_step_t<float, 2, false>(c, step, cfl) : edge_step_t<double, 2, false>(c, step, cfl);
+    if (c->nlayers == 2) {
+        if (c->classical)
+            return f32 ? edge_step_t<float, 2, false, true>(c, step, cfl) : edge_step_t<double, 2, false, true>(c, step, cfl);
+        return f32 ? edge_step_t<float, 2, false>(c, step, cfl) : edge_step_t<double, 2, false>(c, step, cfl);
+    }
     if (c->classical) {
         if (c->ntracers)
             return f32 ? edge_step_t<float, 1, true, true>(c, step, cfl) : edge_step_t<double, 1, true, true>(c, step, cfl);

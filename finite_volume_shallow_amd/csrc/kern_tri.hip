@@ -160,7 +160,7 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
                 Rs[3 * l2 + 1] = qx * nx + qy * ny;
                 Rs[3 * l2 + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T>(L, CA.z(), Rs, CB.z(), g, rr);
+            f = roe2_interior<T, CL>(L, CA.z(), Rs, CB.z(), g, rr);
         } else {
             f = roe2_wall<T>(L, CA.z(), g, rr);
         }
@@ -805,7 +805,11 @@ static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
-    if (c->nlayers == 2) return f32 ? tri_batch_t<float, 2, false>(c, nsteps, cfl) : tri_batch_t<double, 2, false>(c, nsteps, cfl);
+    if (c->nlayers == 2) {
+        if (c->classical)
+            return f32 ? tri_batch_t<float, 2, false, true>(c, nsteps, cfl) : tri_batch_t<double, 2, false, true>(c, nsteps, cfl);
+        return f32 ? tri_batch_t<float, 2, false>(c, nsteps, cfl) : tri_batch_t<double, 2, false>(c, nsteps, cfl);
+    }
     if (c->classical) {
         if (c->ntracers)
             return f32 ? tri_batch_t<float, 1, true, true>(c, nsteps, cfl) : tri_batch_t<double, 1, true, true>(c, nsteps, cfl);

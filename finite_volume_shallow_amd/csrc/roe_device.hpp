@@ -269,7 +269,14 @@ __device__ __forceinline__ T newton_polish(T mu, T d1, T d2, T c1, T c2, T rc)
 
 // L/R: h1, q1n, q1t, h2, q2n, q2t (edge frame), z; pL/pR: sqrt(h1), 1/h1,
 // sqrt(h2), 1/h2 of each cell.
-template <typename T>
+//
+// CL selects the classical Roe flux of the whole 6x6 system: each layer's
+// transverse momentum row (-u_k v_k, v_k, u_k) adds a contact wave of speed
+// u_k with eigenvector e_{q_kt}, and completes every eigenvector of A_ij
+// with v_k times its h_k component.  So alpha of that contact wave is
+// X_kt - v_k X_hk and the side-a transverse fluctuation is
+// v_k (P^- X)_hk + w(u_k) (X_kt - v_k X_hk); the normal rows are unchanged.
+template <typename T, bool CL = false>
 __device__ __forceinline__ Flux2<T> roe2_pre(const T *L, const T *pL, T zL, const T *R, const T *pR, T zR, T g,
                                              T r)
 {
@@ -280,8 +287,9 @@ __device__ __forceinline__ Flux2<T> roe2_pre(const T *L, const T *pL, T zL, cons
     const T i1L = pL[1], i1R = pR[1], i2L = pL[3], i2R = pR[3];
     const T v1L = q1L * i1L, v1R = q1R * i1R, v2L = q2L * i2L, v2R = q2R * i2R;
     const T s1L = pL[0], s1R = pR[0], s2L = pL[2], s2R = pR[2];
-    const T u1 = (s1L * v1L + s1R * v1R) * rcp(s1L + s1R);
-    const T u2 = (s2L * v2L + s2R * v2R) * rcp(s2L + s2R);
+    const T is1 = rcp(s1L + s1R), is2 = rcp(s2L + s2R);
+    const T u1 = (s1L * v1L + s1R * v1R) * is1;
+    const T u2 = (s2L * v2L + s2R * v2R) * is2;
     const T c1 = g * T(0.5) * (h1L + h1R); // c1^2
     const T c2 = g * T(0.5) * (h2L + h2R); // c2^2
     const T rc = r * c1 * c2;
@@ -345,9 +353,18 @@ __device__ __forceinline__ Flux2<T> roe2_pre(const T *L, const T *pL, T zL, cons
     o.b[1] = X[1] - PX[1];
     o.b[3] = X[2] - PX[2];
     o.b[4] = X[3] - PX[3];
+    const T w1L = t1L * i1L, w1R = t1R * i1R, w2L = t2L * i2L, w2R = t2R * i2R;
+    if (CL) { // contact waves of the layers' Roe velocities
+        const T vb1 = (s1L * w1L + s1R * w1R) * is1, vb2 = (s2L * w2L + s2R * w2R) * is2;
+        const T Xt1 = q1R * w1R - q1L * w1L, Xt2 = q2R * w2R - q2L * w2L;
+        o.a[2] = vb1 * PX[0] + wminus(u1) * (Xt1 - vb1 * X[0]);
+        o.a[5] = vb2 * PX[2] + wminus(u2) * (Xt2 - vb2 * X[2]);
+        o.b[2] = Xt1 - o.a[2];
+        o.b[5] = Xt2 - o.a[5];
+        return o;
+    }
     // transverse momentum of each layer, upwinded by that layer's mass flux
     const T phi1 = q1L + PX[0], phi2 = q2L + PX[2];
-    const T w1L = t1L * i1L, w1R = t1R * i1R, w2L = t2L * i2L, w2R = t2R * i2R;
     if (phi1 > T(0)) {
         o.a[2] = PX[0] * w1L;
         o.b[2] = q1R * w1R - phi1 * w1L;
@@ -375,13 +392,13 @@ template <typename T> __device__ __forceinline__ void roe2_cellpre(const T *W, T
     p[3] = r2 * r2;
 }
 
-template <typename T>
+template <typename T, bool CL = false>
 __device__ __forceinline__ Flux2<T> roe2_interior(const T *L, T zL, const T *R, T zR, T g, T r)
 {
     T pL[4], pR[4];
     roe2_cellpre(L, pL);
     roe2_cellpre(R, pR);
-    return roe2_pre<T>(L, pL, zL, R, pR, zR, g, r);
+    return roe2_pre<T, CL>(L, pL, zL, R, pR, zR, g, r);
 }
 
 // Two-layer reflective wall seen from side a: the mirror ghost through the

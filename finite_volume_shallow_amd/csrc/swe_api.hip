@@ -70,7 +70,6 @@ int validate(const swe_mesh_desc *d, std::string &err)
     if (d->precision != SWE_F64 && d->precision != SWE_F32) { err = "bad precision"; return SWE_E_INVAL; }
     if (d->path < SWE_PATH_AUTO || d->path > SWE_PATH_FUSED) { err = "bad path"; return SWE_E_INVAL; }
     if (d->scheme != SWE_SCHEME_IR_ROE && d->scheme != SWE_SCHEME_ROE) { err = "bad scheme"; return SWE_E_INVAL; }
-    if (d->scheme == SWE_SCHEME_ROE && d->nlayers != 1) { err = "the classical Roe scheme is one-layer only"; return SWE_E_INVAL; }
     if (!(d->g > 0.0) || !std::isfinite(d->g)) { err = "g must be > 0"; return SWE_E_INVAL; }
     if (d->nlayers == 2 && !(d->r > 0.0 && d->r < 1.0)) { err = "r must lie in (0, 1)"; return SWE_E_INVAL; }
     if (d->mesh_kind == SWE_MESH_CART) {

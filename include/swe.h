@@ -61,11 +61,11 @@ enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2 };
  * the Roe matrix of the normal subsystem (2x2 for one layer, 4x4 for two),
  * with the transverse momentum and the pollutant carried by the mass flux
  * and upwinded by its sign.  SWE_SCHEME_ROE: the classical Roe scheme that
- * [IR] contrasts it with -- the Roe matrix of the whole one-layer edge
- * system (h, q_n, q_t, hc), whose transverse momentum and pollutant rows are
- * contact waves of the Roe velocity, upwinded like the other waves.  The
- * classical scheme is available for one layer only; both use the same walls
- * and the same Eq. (5) time step. */
+ * [IR] contrasts it with -- the Roe matrix of the whole edge system
+ * ((h, q_n, q_t, hc) for one layer, 6x6 for two), whose transverse momentum
+ * and pollutant rows are contact waves of each layer's Roe velocity,
+ * upwinded like the other waves.  Both use the same walls and the same
+ * Eq. (5) time step. */
 enum swe_scheme { SWE_SCHEME_IR_ROE = 0, SWE_SCHEME_ROE = 1 };
 
 typedef struct swe_mesh_desc {
@@ -75,7 +75,7 @@ typedef struct swe_mesh_desc {
     int32_t ntracers;    /* 0 or 1 pollutant (one layer only)                */
     int32_t precision;   /* SWE_F64 or SWE_F32: storage and arithmetic type  */
     int32_t path;        /* enum swe_path                                    */
-    int32_t scheme;      /* enum swe_scheme (classical Roe: one layer only)  */
+    int32_t scheme;      /* enum swe_scheme                                  */
     double g;            /* gravity, > 0                                     */
     double r;            /* density ratio rho1/rho2 in (0, 1) (two layers)   */
 

@@ -106,8 +106,7 @@ def test_create_rejects_bad_scheme():
         swe.mesh_desc(kind="cart", nx=4, ny=4, dx=1.0, dy=1.0, scheme="hllc")
 
 
-@pytest.mark.parametrize("case", ["clockwise", "node-range", "triple-edge", "two-layer-tracer", "bad-r",
-                                  "two-layer-classical"])
+@pytest.mark.parametrize("case", ["clockwise", "node-range", "triple-edge", "two-layer-tracer", "bad-r"])
 def test_create_rejects_bad_triangles(case):
     xy, tri = _square_mesh()
     kw = {}
@@ -124,8 +123,6 @@ def test_create_rejects_bad_triangles(case):
         kw = dict(nlayers=2, ntracers=1, r=0.9)
     elif case == "bad-r":
         kw = dict(nlayers=2, r=1.0)
-    elif case == "two-layer-classical":
-        kw = dict(nlayers=2, r=0.9, scheme="classical")
     d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, **kw)
     with pytest.raises(swe.SweError) as e:
         swe.swe_create_mesh(d)

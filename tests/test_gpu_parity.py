@@ -142,8 +142,8 @@ def _tri_pollutant(nq, seed=91):
 
 
 # The classical Roe flux (contact waves of the Roe velocity for the
-# transverse momentum and the pollutant) on every one-layer case, both paths.
-CLASSICAL = {n: CASES[n] for n in CASES if not n.startswith("c5")}
+# transverse momentum and the pollutant) on every case, both paths.
+CLASSICAL = dict(CASES)
 CLASSICAL["c4-tri-pollutant-23"] = (lambda: _tri_pollutant(23), 80, "f64")
 CLASSICAL["c4-tri-pollutant-33-f32"] = (lambda: _tri_pollutant(33), 80, "f32")
 
@@ -172,7 +172,7 @@ def test_parity_classical(name, path):
 
 
 @pytest.mark.parametrize("kernel", list(TRI_KERNELS))
-@pytest.mark.parametrize("name", ["c4-tri-pollutant-23", "c4-tri-40-f32"])
+@pytest.mark.parametrize("name", ["c4-tri-pollutant-23", "c4-tri-40-f32", "c5-two-layer-13"])
 def test_parity_classical_tri_kernels(name, kernel, monkeypatch):
     for k, v in TRI_KERNELS[kernel].items():
         monkeypatch.setenv(k, v)

@@ -145,7 +145,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
     ap.add_argument("--precision", choices=["f32", "f64"], default=None)
-    ap.add_argument("--path", choices=["auto", "edge"], default="auto")
+    ap.add_argument("--path", choices=["auto", "edge", "recompute"], default="auto",
+                    help="kernel path: the fused kernels (auto), the explicit-edge path, or the fused "
+                         "kernel with every cell evaluating all its edges (recompute, an ablation)")
     ap.add_argument("--scheme", choices=["ir", "classical"], default="ir",
                     help="numerical flux: IR-Roe (default) or the classical Roe flux")
     ap.add_argument("--repeats", type=int, default=3)
@@ -199,11 +201,12 @@ def main():
     prec = args.precision or w.precision
     K = args.steps or w.nsteps
     stream = torch.cuda.Stream()
-    path = {"auto": swe.SWE_PATH_AUTO, "edge": swe.SWE_PATH_EDGE}[args.path]
+    path = {"auto": swe.SWE_PATH_AUTO, "edge": swe.SWE_PATH_EDGE, "recompute": swe.SWE_PATH_RECOMPUTE}[args.path]
     desc, keep = swe.desc_from_workload(w, path=path, stream=stream, precision=prec)
     ctx = swe.swe_create_mesh(desc)
     del keep
-    used_path = "fused" if swe.swe_path(ctx) == swe.SWE_PATH_FUSED else "edge"
+    used_path = {swe.SWE_PATH_FUSED: "fused", swe.SWE_PATH_EDGE: "edge",
+                 swe.SWE_PATH_RECOMPUTE: "recompute"}[swe.swe_path(ctx)]
 
     swe.swe_set_state(ctx, w.z, w.state)
     if args.warmup:
@@ -235,9 +238,11 @@ def main():
         e = np.sort(np.stack([t, np.roll(t, -1, axis=1)], axis=2).reshape(-1, 2), axis=1)
         E = int(np.unique(e, axis=0).shape[0])
     bpc = alg_bytes_per_cell(w, prec, E)
-    if used_path == "fused":
+    if used_path != "edge":
         # one-layer triangle meshes of regular size run the pipelined kernel
         kernel = "k_cart_fused" if w.kind == "cart" else ("k_tri_pipe" if w.nlayers == 1 else "k_tri_fused")
+        if used_path == "recompute":
+            kernel += "-recompute"
     else:
         kernel = "k_edge_flux+k_cell_dt+k_cell_update"
     # one fused launch per step: the average launch duration is the time per

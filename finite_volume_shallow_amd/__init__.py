@@ -24,7 +24,7 @@ SWE_E_DEPTH, SWE_E_NONFINITE, SWE_E_NONHYPERBOLIC = -5, -6, -7
 SWE_MESH_CART, SWE_MESH_TRI = 0, 1
 SWE_F64, SWE_F32 = 0, 1
 SWE_BC_WALL, SWE_BC_PERIODIC = 0, 1
-SWE_PATH_AUTO, SWE_PATH_EDGE, SWE_PATH_FUSED = 0, 1, 2
+SWE_PATH_AUTO, SWE_PATH_EDGE, SWE_PATH_FUSED, SWE_PATH_RECOMPUTE = 0, 1, 2, 3
 SWE_SCHEME_IR_ROE, SWE_SCHEME_ROE = 0, 1
 
 _D = ctypes.POINTER(ctypes.c_double)

@@ -249,6 +249,11 @@ template <typename T> struct Carry {
     T np_h, np_s, np_b;          // W^{n+1} of row r-2: h, sqrt(h), qy / sqrt(h)
     bool nprow;                  // row r-2 inside the domain
     T sx_prev, sybot_prev;       // Eq. (5) speed sums of row r-2 (x-edges, bottom edge)
+    // recomputation variant only: W^n of row r-2 and W^{n+1} of row r-3
+    PC<T> prev2;
+    bool prev2row;
+    T np2_h, np2_s, np2_b;
+    bool np2row;
 };
 
 // A prefetched row of W^n for this lane.
@@ -266,6 +271,7 @@ template <typename T> struct Ld {
 template <typename T> struct TileC {
     int i, col, j0, rlast, rs0, rs1, rbase;
     bool colok, xwall_lane, wlane;
+    bool lwall_lane, prvok; // recomputation variant: a wall on the lane's left; column i-1 inside
     T fx, fy, g, lx, ly, g_half;
 };
 
@@ -275,7 +281,16 @@ constexpr int PREFETCH = 2;
 // One row step of a tile: row r of W^n arrives (cur), row r+PREFETCH is
 // requested into nxt_ld, row r-1 of W^{n+1} is completed and stored, and
 // the Eq. (5) speed sum of row r-2 is closed.  XW / YW: walls in x / y.
-template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL>
+//
+// RC: the recomputation variant.  Every cell evaluates all four of its
+// edges itself -- the left x-edge and the bottom y-edge again, although the
+// neighbouring lane and the previous row step already did -- instead of
+// taking the neighbour's part of the shared edge (a DPP move, a carried
+// register), for the fluxes and for the Eq. (5) speeds.  The inputs of a
+// recomputed edge are bit-identical to the shared one's; the results agree
+// to rounding (the compiler may contract the two evaluations' multiply-adds
+// differently).
+template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL, bool RC>
 __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
                                          bool &bad_depth, bool &bad_val)
@@ -307,10 +322,32 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
             ex.bc = c;
         }
     }
-    O.ax_m = ex.am + prv(ex.bm);
-    O.ax_x = ex.an + prv(ex.bn);
-    O.ax_y = ex.at + prv(ex.bt);
-    O.ax_c = TR ? ex.ac + prv(ex.bc) : T(0);
+    if constexpr (RC) {
+        // the left x-edge (lane-1, lane) of row r, evaluated again here
+        const T Lh = prv(cur.h), Ls = prv(cur.s), Lu = prv(cur.u), Lv = prv(cur.v), Lc = prv(cur.cc),
+                Lz = prv(cur.z), Lq = prv(cur.qx);
+        EF<T> el = flux<T, TR, CL>(Lh, Ls, Lq, Lu, Lv, Lc, Lz, cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, g);
+        if (XW && K.lwall_lane) {
+            el.bm = el.bn = el.bt = el.bc = T(0);
+            if (K.colok) { // wall on the left of this lane's cell (as seen by the lane on the left)
+                T m, n, t, c;
+                wall(cur.h, -cur.qx, -cur.v, cur.cc, g, m, n, t, c);
+                el.bm = m;
+                el.bn = -n;
+                el.bt = -t;
+                el.bc = c;
+            }
+        }
+        O.ax_m = ex.am + el.bm;
+        O.ax_x = ex.an + el.bn;
+        O.ax_y = ex.at + el.bt;
+        O.ax_c = TR ? ex.ac + el.bc : T(0);
+    } else {
+        O.ax_m = ex.am + prv(ex.bm);
+        O.ax_x = ex.an + prv(ex.bn);
+        O.ax_y = ex.at + prv(ex.bt);
+        O.ax_c = TR ? ex.ac + prv(ex.bc) : T(0);
+    }
 
     // ---- y-edge (row r-1, row r): normal (0, 1), qn = qy, ut = -u;
     // back-rotation (m, n, t, c) -> (m, -t, n, c)
@@ -339,14 +376,41 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     O.nprow = I.nprow;
     O.sx_prev = I.sx_prev;
     O.sybot_prev = I.sybot_prev;
+    if constexpr (RC) {
+        O.np2_h = I.np2_h;
+        O.np2_s = I.np2_s;
+        O.np2_b = I.np2_b;
+        O.np2row = I.np2row;
+    }
     if (r >= K.j0) {
         // ---- complete row r-1: W^{n+1} = W^n - dt/|V| sum |G| fluct, the
         // x- and y-edge sums scaled by dt |G_x| / |V| and dt |G_y| / |V|;
         // y-edge fluctuations map back as (m, n, t, c) -> (m, -t, n, c)
-        const T ym = I.yb_m + ey.am;
-        const T yt = I.yb_t + ey.at;
-        const T yn = I.yb_n + ey.an;
-        const T yc = I.yb_c + ey.ac;
+        T ybm = I.yb_m, ybt = I.yb_t, ybn = I.yb_n, ybc = I.yb_c;
+        if constexpr (RC) { // the bottom y-edge (r-2, r-1), evaluated again
+            const PC<T> &p2 = I.prev2;
+            EF<T> eb = flux<T, TR, CL>(p2.h, p2.s, p2.qy, p2.v, -p2.u, p2.cc, p2.z, prev.h, prev.s, prev.qy, prev.v,
+                                       -prev.u, prev.cc, prev.z, g);
+            if (YW && I.prev2row != I.prevrow) {
+                eb.bm = eb.bn = eb.bt = eb.bc = T(0);
+                if (I.prevrow) { // wall below row r-1
+                    T m, n, t, c;
+                    wall(prev.h, -prev.qy, prev.u, prev.cc, g, m, n, t, c);
+                    eb.bm = m;
+                    eb.bt = -t;
+                    eb.bn = -n;
+                    eb.bc = c;
+                }
+            }
+            ybm = eb.bm;
+            ybt = eb.bt;
+            ybn = eb.bn;
+            ybc = eb.bc;
+        }
+        const T ym = ybm + ey.am;
+        const T yt = ybt + ey.at;
+        const T yn = ybn + ey.an;
+        const T yc = ybc + ey.ac;
         const T fx = K.fx, fy = K.fy;
         const T h1 = prev.h - fx * I.ax_m - fy * ym;
         const T qx1 = prev.qx - fx * I.ax_x + fy * yt;
@@ -358,15 +422,29 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         const T Nh = nxt(h1), Ns = nxt(s1), Na = nxt(a1);
         T exs = espeed(h1, s1, a1, Nh, Ns, Na, g);
         if (XW && K.xwall_lane) exs = FM<T>::sqrt(g * (K.colok ? h1 : Nh));
-        const T sx_cur = lx * (exs + prv(exs));
+        T exl;
+        if constexpr (RC) { // the left x-edge's speed, evaluated again
+            const T Ph = prv(h1), Ps = prv(s1), Pa = prv(a1);
+            exl = espeed(Ph, Ps, Pa, h1, s1, a1, g);
+            if (XW && K.lwall_lane) exl = FM<T>::sqrt(g * (K.prvok ? Ph : h1));
+        } else {
+            exl = prv(exs);
+        }
+        const T sx_cur = lx * (exs + exl);
         if (r >= K.j0 + 1) {
             // y-edge (r-2, r-1) of W^{n+1} completes the speed sum of row r-2
             T eys;
             if (!YW || (I.nprow && I.prevrow)) eys = espeed(I.np_h, I.np_s, I.np_b, h1, s1, b1, g);
             else eys = FM<T>::sqrt(g * (I.nprow ? I.np_h : h1));
             eys *= ly;
+            T ysb = I.sybot_prev;
+            if constexpr (RC) { // row r-2's bottom edge (r-3, r-2), evaluated again
+                if (!YW || (I.np2row && I.nprow)) ysb = espeed(I.np2_h, I.np2_s, I.np2_b, I.np_h, I.np_s, I.np_b, g);
+                else ysb = FM<T>::sqrt(g * (I.np2row ? I.np2_h : I.np_h));
+                ysb *= ly;
+            }
             const int rr = r - 2;
-            if (rr >= K.rs0 && rr < K.rs1 && K.wlane) smax = fmax(smax, I.sx_prev + I.sybot_prev + eys);
+            if (rr >= K.rs0 && rr < K.rs1 && K.wlane) smax = fmax(smax, I.sx_prev + ysb + eys);
             O.sybot_prev = eys;
         }
         // ---- store row r-1 of the tile
@@ -380,6 +458,12 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
             bad_depth |= !(h1 > T(0));
             bad_val |= !isfinite(h1 + qx1 + qy1 + c1);
         }
+        if constexpr (RC) {
+            O.np2_h = I.np_h;
+            O.np2_s = I.np_s;
+            O.np2_b = I.np_b;
+            O.np2row = I.nprow;
+        }
         O.np_h = h1;
         O.np_s = s1;
         O.np_b = b1;
@@ -391,6 +475,10 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     O.yb_t = ey.bt;
     O.yb_n = ey.bn;
     O.yb_c = ey.bc;
+    if constexpr (RC) {
+        O.prev2 = I.prev;
+        O.prev2row = I.prevrow;
+    }
     O.prev = cur;
     O.prevrow = currow;
 }
@@ -399,7 +487,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 // tile's rows reach a wall in y.  Tiles with neither (almost all of them)
 // run without any wall code.  Returns the tile's largest Eq. (5) speed sum
 // sum |G| ||D|| (the smallest dt candidate is 2 gamma |V| over it).
-template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL>
+template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL, bool RC>
 __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, int lane, double dtd, T &smax_out,
                                           unsigned &bad_out)
 {
@@ -420,6 +508,8 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     (void)wrapc(K.i + 1, nxtok);
     // lanes whose x-edge to the right is a wall (either side outside)
     K.xwall_lane = K.colok != nxtok;
+    (void)wrapc(K.i - 1, K.prvok);
+    K.lwall_lane = K.colok != K.prvok;
     K.wlane = lane >= 2 && lane < 2 + CART_COLS && K.i >= 0 && K.i < A.nx;
     K.rlast = K.j0 + A.ty + 1; // last row loaded
     K.rbase = 2 * K.j0 + A.ty - 1; // DN: grid row = rbase - march row
@@ -448,6 +538,12 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
         c0.np_b = T(0);
         c0.nprow = false;
         c0.sx_prev = c0.sybot_prev = T(0);
+        c0.prev2 = c0.prev;
+        c0.prev2row = false;
+        c0.np2_h = T(1);
+        c0.np2_s = T(1);
+        c0.np2_b = T(0);
+        c0.np2row = false;
         load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 1) : K.j0 - 1, K.col, K.colok, DN ? T(-1) : T(1), l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
         load_row<XW || YW>(A, DN ? K.rbase - K.j0 : K.j0, K.col, K.colok, DN ? T(-1) : T(1), l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
     }
@@ -456,30 +552,30 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     // another), so no register is copied between rows.
     int r = K.j0 - 1;
     for (; r + 3 <= K.rlast; r += 4) {
-        row_step<T, TR, XW, YW, DN, CL>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, CL>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, CL>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, CL>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
     }
-    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, CL>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, CL>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, CL>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
     smax_out = smax;
     bad_out = (bad_depth ? FLAG_DEPTH : 0u) | (bad_val ? FLAG_NONFINITE : 0u);
 }
 
 // The tile variant for its walls (x, y) and march direction.
-template <typename T, bool TR, bool DN, bool CL>
+template <typename T, bool TR, bool DN, bool CL, bool RC>
 __device__ __forceinline__ void cart_tile_dispatch(const CartArgs<T, TR> &A, int tile, int lane, double dtd, bool xw,
                                                    bool yw, T &smax, unsigned &bad)
 {
-    if (!xw && !yw) cart_tile<T, TR, false, false, DN, CL>(A, tile, lane, dtd, smax, bad);
-    else if (!yw) cart_tile<T, TR, true, false, DN, CL>(A, tile, lane, dtd, smax, bad);
-    else if (!xw) cart_tile<T, TR, false, true, DN, CL>(A, tile, lane, dtd, smax, bad);
-    else cart_tile<T, TR, true, true, DN, CL>(A, tile, lane, dtd, smax, bad);
+    if (!xw && !yw) cart_tile<T, TR, false, false, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
+    else if (!yw) cart_tile<T, TR, true, false, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
+    else if (!xw) cart_tile<T, TR, false, true, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
+    else cart_tile<T, TR, true, true, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
 }
 
-template <typename T, bool TR, bool CL = false>
+template <typename T, bool TR, bool CL = false, bool RC = false>
 __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
 {
     const int lane = threadIdx.x;
@@ -509,8 +605,8 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     // on large grids odd row blocks march downward: neighbouring blocks then
     // reach the rows they share (each other's halo) at about the same time,
     // while those rows are still in L2
-    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, CL>(A, tile, lane, dtd, xw, yw, smax, bad);
-    else cart_tile_dispatch<T, TR, false, CL>(A, tile, lane, dtd, xw, yw, smax, bad);
+    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, CL, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
+    else cart_tile_dispatch<T, TR, false, CL, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
 
     // the tile's dt candidate 2 gamma |V| / max sum |G| ||D|| (Eq. (5))
     const double dmin = wave_min(smax > T(0) ? (double)(T(2) * A.cfl * A.dx * A.dy / smax) : __builtin_inf());
@@ -614,7 +710,7 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     return A;
 }
 
-template <typename T, bool TR, bool CL = false>
+template <typename T, bool TR, bool CL = false, bool RC = false>
 static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
     hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
@@ -628,7 +724,7 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
         const unsigned grid = (unsigned)(A.per_xcd * NUM_XCD);
-        hipLaunchKernelGGL((k_cart_fused<T, TR, CL>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
+        hipLaunchKernelGGL((k_cart_fused<T, TR, CL, RC>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
     }
     return hipGetLastError();
 }
@@ -636,6 +732,13 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
+    if (c->path == SWE_PATH_RECOMPUTE) { // IR-Roe only
+        if (c->ntracers)
+            return f32 ? cart_batch_t<float, true, false, true>(c, nsteps, cfl)
+                       : cart_batch_t<double, true, false, true>(c, nsteps, cfl);
+        return f32 ? cart_batch_t<float, false, false, true>(c, nsteps, cfl)
+                   : cart_batch_t<double, false, false, true>(c, nsteps, cfl);
+    }
     if (c->classical) {
         if (c->ntracers)
             return f32 ? cart_batch_t<float, true, true>(c, nsteps, cfl) : cart_batch_t<double, true, true>(c, nsteps, cfl);

@@ -68,7 +68,7 @@ int validate(const swe_mesh_desc *d, std::string &err)
     if (d->ntracers != 0 && d->ntracers != 1) { err = "ntracers must be 0 or 1"; return SWE_E_INVAL; }
     if (d->nlayers == 2 && d->ntracers) { err = "a pollutant is supported with one layer only"; return SWE_E_INVAL; }
     if (d->precision != SWE_F64 && d->precision != SWE_F32) { err = "bad precision"; return SWE_E_INVAL; }
-    if (d->path < SWE_PATH_AUTO || d->path > SWE_PATH_FUSED) { err = "bad path"; return SWE_E_INVAL; }
+    if (d->path < SWE_PATH_AUTO || d->path > SWE_PATH_RECOMPUTE) { err = "bad path"; return SWE_E_INVAL; }
     if (d->scheme != SWE_SCHEME_IR_ROE && d->scheme != SWE_SCHEME_ROE) { err = "bad scheme"; return SWE_E_INVAL; }
     if (!(d->g > 0.0) || !std::isfinite(d->g)) { err = "g must be > 0"; return SWE_E_INVAL; }
     if (d->nlayers == 2 && !(d->r > 0.0 && d->r < 1.0)) { err = "r must lie in (0, 1)"; return SWE_E_INVAL; }
@@ -261,6 +261,13 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             throw Fail{SWE_E_INVAL};
         }
         c->path = (d->path == SWE_PATH_EDGE || !fused_ok) ? SWE_PATH_EDGE : SWE_PATH_FUSED;
+        if (d->path == SWE_PATH_RECOMPUTE) {
+            if (d->mesh_kind != SWE_MESH_CART || d->scheme != SWE_SCHEME_IR_ROE) {
+                c->err = "the recomputation path exists for IR-Roe on Cartesian grids only";
+                throw Fail{SWE_E_INVAL};
+            }
+            c->path = SWE_PATH_RECOMPUTE;
+        }
         // the fused kernel addresses a field with 32-bit byte offsets
         if (d->mesh_kind == SWE_MESH_CART &&
             (d->nx > (int64_t)1 << 30 || d->ny > (int64_t)1 << 30 ||
@@ -496,7 +503,7 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
                 }
             c->hist_cap = cap;
         }
-        if (c->path == SWE_PATH_FUSED) {
+        if (c->path != SWE_PATH_EDGE) { // fused (or its recomputation variant)
             if (c->kind == SWE_MESH_CART) HIPTRY(launch_cart_batch(c, nsteps, cfl));
             else HIPTRY(launch_tri_batch(c, nsteps, cfl));
             c->cur ^= (nsteps & 1); // ping-pong: the last launch wrote the other buffer

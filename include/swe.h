@@ -54,8 +54,14 @@ enum swe_bc { SWE_BC_WALL = 0, SWE_BC_PERIODIC = 1 };
  * one-layer grids and triangle meshes); EDGE forces the generic
  * explicit-edge-list path (three launches per step) on any mesh; FUSED
  * requests the fused path and fails with SWE_E_INVAL where none exists
- * (two layers on a Cartesian grid are rejected anyway). */
-enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2 };
+ * (two layers on a Cartesian grid are rejected anyway).  RECOMPUTE is the
+ * fused path in the "recomputation" organisation that [MG] contrasts with
+ * its ghost-cell decoupling kernel: every cell evaluates all of its edges
+ * (fluxes and Eq. (5) speeds) itself, so each interior edge is evaluated
+ * twice, instead of once with the two cells sharing the result.  Same
+ * results as FUSED up to rounding; an ablation.  IR-Roe on Cartesian grids
+ * only (SWE_E_INVAL otherwise). */
+enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2, SWE_PATH_RECOMPUTE = 3 };
 
 /* Numerical flux.  SWE_SCHEME_IR_ROE: the IR-Roe scheme of [IR] Sec. 2.2 --
  * the Roe matrix of the normal subsystem (2x2 for one layer, 4x4 for two),
@@ -168,8 +174,8 @@ int swe_nvars(const swe_ctx *ctx);
 /* Number of cells; -1 for NULL. */
 int64_t swe_ncells(const swe_ctx *ctx);
 
-/* The kernel path the context runs (SWE_PATH_EDGE or SWE_PATH_FUSED);
- * -1 for NULL. */
+/* The kernel path the context runs (SWE_PATH_EDGE, SWE_PATH_FUSED or
+ * SWE_PATH_RECOMPUTE); -1 for NULL. */
 int swe_path(const swe_ctx *ctx);
 
 #ifdef __cplusplus

@@ -46,7 +46,8 @@ def test_binding_constants_match_header():
     assert int(re.search(r"#define SWE_ABI_VERSION (\d+)", hdr).group(1)) == swe.SWE_ABI_VERSION
     consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SWE_[A-Z0-9_]+) = (-?\d+)", hdr)}
     for name in ["SWE_MESH_CART", "SWE_MESH_TRI", "SWE_F64", "SWE_F32", "SWE_BC_WALL", "SWE_BC_PERIODIC",
-                 "SWE_PATH_AUTO", "SWE_PATH_EDGE", "SWE_PATH_FUSED", "SWE_SCHEME_IR_ROE", "SWE_SCHEME_ROE"]:
+                 "SWE_PATH_AUTO", "SWE_PATH_EDGE", "SWE_PATH_FUSED", "SWE_PATH_RECOMPUTE",
+                 "SWE_SCHEME_IR_ROE", "SWE_SCHEME_ROE"]:
         assert consts[name] == getattr(swe, name), name
 
 
@@ -94,6 +95,24 @@ def _square_mesh():
     xy = np.array([[0, 0], [1, 0], [1, 1], [0, 1]], dtype=float)
     tri = np.array([[0, 1, 2], [0, 2, 3]], dtype=np.int32)
     return xy, tri
+
+
+def test_recompute_path_is_cartesian_ir_roe_only():
+    xy, tri = _square_mesh()
+    d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, path=swe.SWE_PATH_RECOMPUTE)
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL and "recomputation" in str(e.value)
+    d, keep = _cart()
+    d.path = swe.SWE_PATH_RECOMPUTE
+    d.scheme = swe.SWE_SCHEME_ROE
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
+    d.path = 4
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
 
 
 def test_create_rejects_bad_scheme():

@@ -208,6 +208,50 @@ def test_classical_and_ir_differ_on_gpu():
     assert np.abs(ir[3] - cl[3]).max() > 1e-8 * np.abs(ir[3]).max()
 
 
+# The recomputation variant of the structured kernel (every cell evaluates
+# its four edges itself): against the oracle, and against the shared-edge
+# kernel in every tiling and march direction.  A recomputed edge has the
+# same inputs as the shared one, but the compiler may contract its
+# multiply-adds differently (only one side's fluctuation is live there), so
+# the two agree to rounding, not bit for bit.
+RC_TOL = {"f64": 1e-12, "f32": 2e-5}
+CART = [n for n in CASES if n.startswith(("c1", "c2", "c3"))]
+
+
+@pytest.mark.parametrize("name", CART)
+def test_parity_recompute(name):
+    make, nsteps, prec = CASES[name]
+    w = make()
+    say(f"[recompute] {name} steps={nsteps} prec={prec}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, path=3, precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    assert max(field_errors(got, ref, w.g)) <= tol
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+    shared, sdts, _ = gpu_run(w, nsteps=nsteps, path=2, precision=prec)
+    errs = field_errors(got, shared, w.g)
+    say(f"    recompute vs shared {['%.2e' % e for e in errs]}")
+    assert max(errs) <= RC_TOL[prec], errs
+    assert np.abs(dts - sdts).max() <= RC_TOL[prec] * sdts.max()
+
+
+@pytest.mark.parametrize("tiling", [f"{n}@ty{t}alt{a}" for n, v in TILINGS.items() for t, a in v])
+def test_recompute_in_every_tiling(tiling, monkeypatch):
+    name, rest = tiling.split("@")
+    ty, alt = rest[2:].split("alt")
+    monkeypatch.setenv("SWE_CART_TY", ty)
+    monkeypatch.setenv("SWE_CART_ALT", alt)
+    make, nsteps, prec = CASES[name]
+    w = make()
+    say(f"[recompute tiling] {name} rows/tile={ty} alternate={alt}")
+    a, da, _ = gpu_run(w, nsteps=min(nsteps, 40), path=3, precision=prec)
+    b, db, _ = gpu_run(w, nsteps=min(nsteps, 40), path=2, precision=prec)
+    errs = field_errors(a, b, w.g)
+    assert max(errs) <= RC_TOL[prec], errs
+    assert np.abs(da - db).max() <= RC_TOL[prec] * db.max()
+
+
 def test_config1_symmetry_on_gpu():
     w = inputs.config1()
     say("[sym] config1 rows identical, qy == 0")

@@ -254,11 +254,23 @@ template <typename T> __device__ __forceinline__ void tri_book(const TriArgs<T> 
     }
 }
 
+// An edge's packed cell pair (a | b << 16) in a real-valued LDS slot, exact.
+__device__ __forceinline__ float tri_pack(uint32_t v, float) { return __uint_as_float(v); }
+__device__ __forceinline__ double tri_pack(uint32_t v, double) { return (double)v; }
+__device__ __forceinline__ uint32_t tri_unpack(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t tri_unpack(double x) { return (uint32_t)x; }
+
 // RD: rounds of NT threads covering the largest local cell / edge / slot
 // counts of any block.  Every global load a thread will need in the launch
 // (halo ids, its edges' geometry, its cells' slot lists and 1/|V|) is issued
 // at the start, so the phases after the first barrier only touch LDS.
-template <typename T, int NL, bool TR, bool DT0, int RD, int NT, bool CL = false>
+//
+// RC: the recomputation variant.  Instead of evaluating each local edge
+// once into LDS records that its two cells gather, every cell evaluates all
+// three of its edges itself (interior edges twice over), for the fluxes and
+// for the Eq. (5) speeds; the LDS edge records then hold the edges' cell
+// pair and geometry.  Same inputs per edge, same accumulation order.
+template <typename T, int NL, bool TR, bool DT0, int RD, int NT, bool CL = false, bool RC = false>
 __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -363,10 +375,81 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
         enx[m] *= rq;
         eny[m] *= rq;
     }
+    if constexpr (RC && !DT0) { // edge records: cell pair, normal (side 0), length (side 1)
+#pragma unroll
+        for (int m = 0; m < RD; ++m) {
+            const int k = tid + m * NT;
+            if (k < ne) {
+                T *fa = fl + ER * k;
+                fa[0] = tri_pack(eab[m], T(0));
+                fa[1] = enx[m];
+                fa[2] = eny[m];
+                fl[ER * (EM + k)] = elen[m];
+            }
+        }
+    }
+    // the edge of a slot, from the records above (RC)
+    auto slot_edge = [&](unsigned sl, int &la, int &lb, bool &wall, T &nx, T &ny, T &len, bool &side_b) {
+        const unsigned q = sl / (unsigned)ER;
+        side_b = q >= (unsigned)EM;
+        const unsigned k = side_b ? q - (unsigned)EM : q;
+        const T *fa = fl + ER * k;
+        const uint32_t ab = tri_unpack(fa[0]);
+        nx = fa[1];
+        ny = fa[2];
+        len = fl[ER * (EM + k)];
+        la = (int)(ab & 0xFFFFu);
+        lb = (int)(ab >> 16);
+        wall = lb == 0xFFFF;
+        if (wall) lb = 0;
+    };
     __syncthreads();
 
     double dtd = 0.0;
-    if (!DT0) {
+    if constexpr (!DT0 && RC) {
+        // ---- 2-3 (RC). W^{n+1} of the block and ring 1, every cell
+        // evaluating its three edges itself; the new states wait in
+        // registers until every thread has read W^n
+        dtd = wave_min(dpart);
+        T nw[RD][NV];
+#pragma unroll
+        for (int m = 0; m < RD; ++m) {
+            const int l = tid + m * NT;
+            if (l < nc) {
+                T acc[NV];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) acc[v] = T(0);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    int la, lb;
+                    bool wall, sb;
+                    T nx, ny, len;
+                    slot_edge((unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu, la, lb, wall, nx, ny, len, sb);
+                    T Fa[NV], Fb[NV];
+                    tri_edge_flux<T, NL, TR, NV, CL>(Cell(sm, LCM, la), Cell(sm, LCM, lb), wall, nx, ny, len, g, rr,
+                                                     Fa, Fb, bad);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) acc[v] += sb ? Fb[v] : Fa[v];
+                }
+                const T fct = (T)dtd * cia[m];
+                const Cell c(sm, LCM, l);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) nw[m][v] = c.s[v] - fct * acc[v];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < RD; ++m) {
+            const int l = tid + m * NT;
+            if (l < nc) {
+                const Cell c(sm, LCM, l);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) c.s[v] = nw[m][v];
+                tri_cellpre<T, NL, NV>(c);
+            }
+        }
+        __syncthreads();
+    } else if (!DT0) {
         // ---- 2. every edge touching the block or ring 1, once
 #pragma unroll
         for (int m = 0; m < RD; ++m) {
@@ -419,7 +502,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int k = tid + m * NT;
-        if (k < es0) {
+        if (!(RC && !DT0) && k < es0) {
             const unsigned lb = eab[m] >> 16;
             const bool wall = lb == 0xFFFFu;
             const T sp = tri_edge_speed<T, NL, NV>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)),
@@ -429,7 +512,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
             fl[ER * (EM + k)] = sp;
         }
     }
-    __syncthreads();
+    if constexpr (!(RC && !DT0)) __syncthreads();
 
     // ---- 5. dt candidates of the block cells, W^{n+1} out.  dt_i =
     // 2 gamma / (S_i / |V_i|) and a correctly rounded quotient is monotone in
@@ -439,8 +522,23 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
         if (l < B0) {
-            const T S = fl[(unsigned)csl4[m] & 0xFFFFu] + fl[(unsigned)(csl4[m] >> 16) & 0xFFFFu] +
-                        fl[(unsigned)(csl4[m] >> 32) & 0xFFFFu];
+            T S;
+            if constexpr (RC && !DT0) { // the cell's three edge speeds, evaluated here
+                T sp[3];
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    int la, lb;
+                    bool wall, sb;
+                    T nx, ny, len;
+                    slot_edge((unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu, la, lb, wall, nx, ny, len, sb);
+                    sp[j] = tri_edge_speed<T, NL, NV>(Cell(sm, LCM, la), Cell(sm, LCM, lb), wall, nx, ny, len, g, rr,
+                                                      bad);
+                }
+                S = sp[0] + sp[1] + sp[2];
+            } else {
+                S = fl[(unsigned)csl4[m] & 0xFFFFu] + fl[(unsigned)(csl4[m] >> 16) & 0xFFFFu] +
+                    fl[(unsigned)(csl4[m] >> 32) & 0xFFFFu];
+            }
             rate = fmax(rate, cia[m] * S);
             if (!DT0) {
                 bool badv = false;
@@ -745,7 +843,7 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
 
 // CL: classical Roe flux.  The initial-state dt prologue computes speeds
 // only, which both fluxes share, so it is the IR-Roe instance.
-template <typename T, int NL, bool TR, int RD, int NT, bool CL>
+template <typename T, int NL, bool TR, int RD, int NT, bool CL, bool RC = false>
 static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -755,13 +853,13 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     if (lds > 65536) {
         hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, true, RD, NT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, CL>,
+        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, CL, RC>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     }
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
     hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
                        tri_args<T>(c, 0, cfl));
-    if constexpr (RD == 1) {
+    if constexpr (RD == 1 && !RC) {
         if (c->tb.pipe_wgs != 0) {
             if (lds > 65536)
                 hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT, CL>,
@@ -781,7 +879,7 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
         }
     }
     for (int64_t s = 0; s < nsteps; ++s)
-        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT, CL>), grid, block, lds, c->stream,
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT, CL, RC>), grid, block, lds, c->stream,
                            tri_args<T>(c, s, cfl));
     return hipGetLastError();
 }
@@ -802,9 +900,21 @@ static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     return tri_batch_rd<T, NL, TR, 3, 256, CL>(c, nsteps, cfl);
 }
 
+// The recomputation variant (IR-Roe, 512 threads per workgroup).
+template <typename T, int NL, bool TR> static hipError_t tri_batch_rc(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 512, false, true>(c, nsteps, cfl);
+    return tri_batch_rd<T, NL, TR, 2, 512, false, true>(c, nsteps, cfl);
+}
+
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
+    if (c->path == SWE_PATH_RECOMPUTE) {
+        if (c->nlayers == 2) return f32 ? tri_batch_rc<float, 2, false>(c, nsteps, cfl) : tri_batch_rc<double, 2, false>(c, nsteps, cfl);
+        if (c->ntracers) return f32 ? tri_batch_rc<float, 1, true>(c, nsteps, cfl) : tri_batch_rc<double, 1, true>(c, nsteps, cfl);
+        return f32 ? tri_batch_rc<float, 1, false>(c, nsteps, cfl) : tri_batch_rc<double, 1, false>(c, nsteps, cfl);
+    }
     if (c->nlayers == 2) {
         if (c->classical)
             return f32 ? tri_batch_t<float, 2, false, true>(c, nsteps, cfl) : tri_batch_t<double, 2, false, true>(c, nsteps, cfl);

@@ -262,8 +262,8 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         }
         c->path = (d->path == SWE_PATH_EDGE || !fused_ok) ? SWE_PATH_EDGE : SWE_PATH_FUSED;
         if (d->path == SWE_PATH_RECOMPUTE) {
-            if (d->mesh_kind != SWE_MESH_CART || d->scheme != SWE_SCHEME_IR_ROE) {
-                c->err = "the recomputation path exists for IR-Roe on Cartesian grids only";
+            if (d->scheme != SWE_SCHEME_IR_ROE) {
+                c->err = "the recomputation path exists for the IR-Roe flux only";
                 throw Fail{SWE_E_INVAL};
             }
             c->path = SWE_PATH_RECOMPUTE;
@@ -320,6 +320,11 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             if (const char *e = std::getenv("SWE_TRI_NT"))
                 if (std::atoi(e) == 256) c->tb.nt = 256;
             if (const char *e = std::getenv("SWE_TRI_PIPE")) pipe = std::atoi(e) != 0;
+            if (c->path == SWE_PATH_RECOMPUTE) { // one workgroup of 512 threads per block
+                c->tb.nt = 512;
+                if (pipe && !std::getenv("SWE_TRI_B")) B = 288; // the per-block kernel's first choice
+                pipe = false;
+            }
             for (;;) {
                 st = build_tri_blocks(he, c->N, B, hb, c->err);
                 if (st != SWE_OK) throw Fail{st};

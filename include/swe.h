@@ -59,8 +59,9 @@ enum swe_bc { SWE_BC_WALL = 0, SWE_BC_PERIODIC = 1 };
  * its ghost-cell decoupling kernel: every cell evaluates all of its edges
  * (fluxes and Eq. (5) speeds) itself, so each interior edge is evaluated
  * twice, instead of once with the two cells sharing the result.  Same
- * results as FUSED up to rounding; an ablation.  IR-Roe on Cartesian grids
- * only (SWE_E_INVAL otherwise). */
+ * results as FUSED up to rounding; an ablation.  IR-Roe flux only
+ * (SWE_E_INVAL otherwise); on triangle meshes it runs the one-workgroup-
+ * per-block kernel. */
 enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2, SWE_PATH_RECOMPUTE = 3 };
 
 /* Numerical flux.  SWE_SCHEME_IR_ROE: the IR-Roe scheme of [IR] Sec. 2.2 --

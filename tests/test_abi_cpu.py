@@ -97,9 +97,9 @@ def _square_mesh():
     return xy, tri
 
 
-def test_recompute_path_is_cartesian_ir_roe_only():
+def test_recompute_path_is_ir_roe_only():
     xy, tri = _square_mesh()
-    d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, path=swe.SWE_PATH_RECOMPUTE)
+    d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, path=swe.SWE_PATH_RECOMPUTE, scheme="classical")
     with pytest.raises(swe.SweError) as e:
         swe.swe_create_mesh(d)
     assert e.value.status == swe.SWE_E_INVAL and "recomputation" in str(e.value)

@@ -208,17 +208,15 @@ def test_classical_and_ir_differ_on_gpu():
     assert np.abs(ir[3] - cl[3]).max() > 1e-8 * np.abs(ir[3]).max()
 
 
-# The recomputation variant of the structured kernel (every cell evaluates
-# its four edges itself): against the oracle, and against the shared-edge
-# kernel in every tiling and march direction.  A recomputed edge has the
-# same inputs as the shared one, but the compiler may contract its
-# multiply-adds differently (only one side's fluctuation is live there), so
-# the two agree to rounding, not bit for bit.
+# The recomputation variants of the fused kernels (every cell evaluates all
+# of its edges itself): against the oracle, and against the shared-edge
+# kernels (on Cartesian grids in every tiling and march direction).  A
+# recomputed edge has the same inputs as the shared one, but the compiler
+# may contract its multiply-adds differently, so the two agree to rounding.
 RC_TOL = {"f64": 1e-12, "f32": 2e-5}
-CART = [n for n in CASES if n.startswith(("c1", "c2", "c3"))]
 
 
-@pytest.mark.parametrize("name", CART)
+@pytest.mark.parametrize("name", list(CASES))
 def test_parity_recompute(name):
     make, nsteps, prec = CASES[name]
     w = make()

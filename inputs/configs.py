@@ -51,8 +51,10 @@ class Workload:
     # triangle meshes
     node_xy: np.ndarray | None = None
     tri: np.ndarray | None = None
-    # "ir" (the IR-Roe scheme) or "classical" (full Roe matrix, one layer)
+    # "ir" (the IR-Roe scheme) or "classical" (full Roe matrix)
     scheme: str = "ir"
+    # 1: Harten-Hyman entropy fix (one layer, IR-Roe)
+    entropy_fix: int = 0
 
     @property
     def ncells(self) -> int:

@@ -41,6 +41,7 @@ def lib():
         L = ctypes.CDLL(_build.LIB)
         L.or_roe1_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
         L.or_roe1c_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
+        L.or_roe1_edge_fix.argtypes = [_D, _D, ctypes.c_double, ctypes.c_int, _D, _D]
         L.or_roe1_wall.argtypes = [_D, ctypes.c_double, _D, _D]
         L.or_roe2_edge.argtypes = [_D, _D, ctypes.c_double, ctypes.c_double, _D, _D, _D]
         L.or_roe2_wall.argtypes = [_D, ctypes.c_double, ctypes.c_double, _D, _D]
@@ -48,10 +49,10 @@ def lib():
         L.or_run_cart.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_int,
-                                  _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int]
+                                  _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.or_run_tri.argtypes = [ctypes.c_int64, _D, ctypes.c_int64, _I32,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_int,
-                                 _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int]
+                                 _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.or_run_tri2.argtypes = [ctypes.c_int64, _D, ctypes.c_int64, _I32,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                   ctypes.c_int, _D, _D, _D, _D, _D, _D, _D, _D,
@@ -81,6 +82,16 @@ def roe1_edge(L, R, g=9.81):
     L = _f64(L); R = _f64(R)
     phi = np.zeros(4); sp = ctypes.c_double()
     st = lib().or_roe1_edge(_dp(L), _dp(R), g, _dp(phi), ctypes.byref(sp))
+    if st:
+        raise OracleError(st)
+    return phi, sp.value
+
+
+def roe1_edge_fix(L, R, g=9.81, fix=1):
+    """As roe1_edge, with the Harten-Hyman entropy fix (fix=1)."""
+    L = _f64(L); R = _f64(R)
+    phi = np.zeros(4); sp = ctypes.c_double()
+    st = lib().or_roe1_edge_fix(_dp(L), _dp(R), g, int(fix), _dp(phi), ctypes.byref(sp))
     if st:
         raise OracleError(st)
     return phi, sp.value
@@ -166,6 +177,9 @@ def run(w, nsteps=None, nthreads=None, check=True):
     dts = np.zeros(max(nsteps, 1))
     L = lib()
     classical = int(getattr(w, "scheme", "ir") == "classical")
+    fix = int(getattr(w, "entropy_fix", 0))
+    if fix and (classical or w.nlayers != 1):
+        raise ValueError("the entropy fix is implemented for the one-layer IR-Roe flux")
     if classical and w.kind == "cart" and w.nlayers != 1:
         raise ValueError("two layers run on triangle meshes only")
     if w.kind == "cart":
@@ -173,7 +187,7 @@ def run(w, nsteps=None, nthreads=None, check=True):
         status = L.or_run_cart(w.nx, w.ny, w.dx, w.dy, int(w.bc_x == "periodic"),
                                int(w.bc_y == "periodic"), w.g, w.cfl, nsteps,
                                _dp(z), _dp(st_arrays[0]), _dp(st_arrays[1]),
-                               _dp(st_arrays[2]), _dp(hc), _dp(dts), nthreads, classical)
+                               _dp(st_arrays[2]), _dp(hc), _dp(dts), nthreads, classical, fix)
     elif w.nlayers == 1:
         xy = _f64(w.node_xy).ravel()
         t = np.ascontiguousarray(w.tri, dtype=np.int32).ravel()
@@ -181,7 +195,7 @@ def run(w, nsteps=None, nthreads=None, check=True):
         status = L.or_run_tri(xy.size // 2, _dp(xy), t.size // 3, t.ctypes.data_as(_I32),
                               w.g, w.cfl, nsteps, _dp(z), _dp(st_arrays[0]),
                               _dp(st_arrays[1]), _dp(st_arrays[2]), _dp(hc), _dp(dts),
-                              nthreads, classical)
+                              nthreads, classical, fix)
     else:
         xy = _f64(w.node_xy).ravel()
         t = np.ascontiguousarray(w.tri, dtype=np.int32).ravel()

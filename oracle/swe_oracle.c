@@ -31,7 +31,19 @@
  *  - sgn(0) = 0, so a wave of zero speed is split half and half.
  *  - The upwind choice for the transverse momentum and the pollutant takes
  *    the left state when the mass flux is > 0, else the right state.
- *  - No entropy fix.
+ *  - No entropy fix by default.  [IR] Sec. 2.2 only says the Harten-Hyman
+ *    fix of its ref. [25] can be adapted; the optional one here (one layer,
+ *    IR-Roe) is that fix in its wave-splitting form, applied to the
+ *    conservative part of each acoustic wave: with b = K^-1 (W_R - W_L) the
+ *    state jumps of the Roe waves and W* = W_L + b_1 r_1 the state between
+ *    them, a wave k whose characteristic speed is < 0 on its left state and
+ *    > 0 on its right state (a transonic rarefaction) is split into a part
+ *    of speed lam_left going left and one of speed lam_right going right,
+ *    with the fraction (lam_right - lam_k)/(lam_right - lam_left) going left,
+ *    so that its left-going flux jump min(lam_k, 0) b_k r_k becomes
+ *    lam_left (lam_right - lam_k)/(lam_right - lam_left) b_k r_k.  The
+ *    source part of the wave is untouched (a lake at rest has no transonic
+ *    wave, so the fix keeps the scheme well-balanced).
  *  - The pollutant is a passive scalar carried by the mass flux, upwinded
  *    like the transverse momentum of step 3 ([MG] gives no other flux).
  *  - Reflective wall = mirror ghost (normal momentum negated) pushed through
@@ -93,8 +105,54 @@ static double sgn(double x) { return (x > 0.0) - (x < 0.0); }
 /* L, R: (h, q_normal, q_transverse, hc, H).  phi: (mass, normal momentum,
  * transverse momentum, pollutant) flux leaving L through the edge.  speed:
  * max |eigenvalue| of the Roe matrix. */
+/* Harten-Hyman correction of the left-going flux jump (P0, P1) of the
+ * one-layer 2x2 Roe solution (see the header): lam1, lam2 the Roe speeds. */
+static void hh_fix(const double *L, const double *R, double g, double lam1,
+                   double lam2, double *P0, double *P1)
+{
+    double hL = L[0], qL = L[1], hR = R[0], qR = R[1];
+    double dh = hR - hL, dq = qR - qL;
+    double b1 = (lam2 * dh - dq) / (lam2 - lam1);  /* K^-1 (W_R - W_L) */
+    double b2 = (dq - lam1 * dh) / (lam2 - lam1);
+    double hs = hL + b1, qs = qL + b1 * lam1;       /* W* */
+    if (!(hs > 0.0)) return;
+    double us = qs / hs, cs = sqrt(g * hs);
+    double uL = qL / hL, uR = qR / hR;
+    /* wave 1 between W_L and W*, wave 2 between W* and W_R */
+    double l1L = uL - sqrt(g * hL), l1R = us - cs;
+    double l2L = us + cs, l2R = uR + sqrt(g * hR);
+    if (l1L < 0.0 && l1R > 0.0) {
+        double lb = l1L * (l1R - lam1) / (l1R - l1L);
+        double corr = lb - fmin(lam1, 0.0);
+        *P0 += corr * b1;
+        *P1 += corr * b1 * lam1;
+    }
+    if (l2L < 0.0 && l2R > 0.0) {
+        double lb = l2L * (l2R - lam2) / (l2R - l2L);
+        double corr = lb - fmin(lam2, 0.0);
+        *P0 += corr * b2;
+        *P1 += corr * b2 * lam2;
+    }
+}
+
+static int roe1_ir(const double *L, const double *R, double g, int fix,
+                   double *phi, double *speed);
+
 int or_roe1_edge(const double *L, const double *R, double g, double *phi,
                  double *speed)
+{
+    return roe1_ir(L, R, g, 0, phi, speed);
+}
+
+/* As or_roe1_edge, with the Harten-Hyman entropy fix when fix != 0. */
+int or_roe1_edge_fix(const double *L, const double *R, double g, int fix,
+                     double *phi, double *speed)
+{
+    return roe1_ir(L, R, g, fix, phi, speed);
+}
+
+static int roe1_ir(const double *L, const double *R, double g, int fix,
+                   double *phi, double *speed)
 {
     double hL = L[0], qL = L[1], tL = L[2], cL = L[3], HL = L[4];
     double hR = R[0], qR = R[1], tR = R[2], cR = R[3], HR = R[4];
@@ -121,6 +179,7 @@ int or_roe1_edge(const double *L, const double *R, double g, double *phi,
     double w2 = 0.5 * (1.0 - sgn(lam2));
     double P0 = w1 * a1 + w2 * a2;
     double P1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    if (fix) hh_fix(L, R, g, lam1, lam2, &P0, &P1);
 
     double f0 = FL0 + P0;
     double f1 = FL1 + P1;
@@ -588,7 +647,7 @@ static int check_state(int64_t n, int nv, double *const *W)
 int or_run_cart(int nx, int ny, double dx, double dy, int periodic_x,
                 int periodic_y, double g, double cfl, int nsteps,
                 const double *z, double *h, double *qx, double *qy, double *hc,
-                double *dts, int nthreads, int classical)
+                double *dts, int nthreads, int classical, int fix)
 {
     int64_t N = (int64_t)nx * ny;
     double area = dx * dy;
@@ -630,7 +689,7 @@ int or_run_cart(int nx, int ny, double dx, double dy, int periodic_x,
                                      -qx[m] * ey[sd] + qy[m] * ex[sd],
                                      hc ? hc[m] : 0.0, -z[m]};
                     st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)
-                                   : or_roe1_edge(Lst, Rst, g, phi, &sp);
+                                   : roe1_ir(Lst, Rst, g, fix, phi, &sp);
                 }
                 if (st > err) err = st;
                 /* back-rotation T^-1 and accumulation of |G| F^- */
@@ -747,7 +806,7 @@ static int build_tri_cells(int64_t nnodes, const double *xy, int64_t ncells,
 int or_run_tri(int64_t nnodes, const double *xy, int64_t ncells,
                const int32_t *tri, double g, double cfl, int nsteps,
                const double *z, double *h, double *qx, double *qy, double *hc,
-               double *dts, int nthreads, int classical)
+               double *dts, int nthreads, int classical, int fix)
 {
     or_tri_cell *cells = malloc(sizeof(or_tri_cell) * ncells);
     double *acc = malloc(sizeof(double) * 4 * ncells);
@@ -775,7 +834,7 @@ int or_run_tri(int64_t nnodes, const double *xy, int64_t ncells,
                     double Rst[5] = {h[m], qx[m] * ex + qy[m] * ey, -qx[m] * ey + qy[m] * ex,
                                      hc ? hc[m] : 0.0, -z[m]};
                     st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)
-                                   : or_roe1_edge(Lst, Rst, g, phi, &sp);
+                                   : roe1_ir(Lst, Rst, g, fix, phi, &sp);
                 }
                 if (st > err) err = st;
                 a[0] += C->len[k] * phi[0];

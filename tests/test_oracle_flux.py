@@ -478,3 +478,74 @@ def test_roe2c_consistency_and_pure_shear():
     assert np.abs(phi[[0, 1, 3, 4]] - FL[[0, 1, 3, 4]]).max() <= 1e-14 * np.abs(FL).max()
     assert phi[2] == pytest.approx(FL[2], rel=1e-14)      # u1 > 0: from L
     assert phi[5] == pytest.approx(FR[5], rel=1e-14)      # u2 < 0: from R
+
+
+# ------------------------------------------------ Harten-Hyman entropy fix
+
+def _subcritical_small_jumps(rng, n):
+    # every state near the others and well below critical speed: no wave
+    # can change the sign of its characteristic speed
+    out = []
+    for _ in range(n):
+        h = rng.uniform(0.5, 5.0)
+        hL, hR = h * rng.uniform(0.85, 1.15, 2)
+        c = math.sqrt(G * h)
+        uL, uR = rng.uniform(-0.3, 0.3, 2) * c
+        out.append((np.array([hL, uL * hL, rng.uniform(-1, 1), 0.3 * hL, rng.uniform(-0.2, 0.2)]),
+                    np.array([hR, uR * hR, rng.uniform(-1, 1), 0.6 * hR, rng.uniform(-0.2, 0.2)])))
+    return out
+
+
+def _transonic_dam_breaks(rng, n):
+    # deep side at rest or slowly moving, shallow side much shallower: the
+    # left rarefaction of the Riemann problem straddles the edge
+    out = []
+    for _ in range(n):
+        hL = rng.uniform(1.0, 4.0)
+        hR = hL * rng.uniform(0.01, 0.08)
+        cL = math.sqrt(G * hL)
+        L = np.array([hL, rng.uniform(0.0, 0.3) * cL * hL, rng.uniform(-1, 1), 0.5 * hL, rng.uniform(-0.05, 0.05)])
+        R = np.array([hR, rng.uniform(0.0, 0.3) * cL * hR, rng.uniform(-1, 1), 0.2 * hR, rng.uniform(-0.05, 0.05)])
+        out.append((L, R))
+    return out
+
+
+def test_entropy_fix_is_inactive_without_transonic_waves():
+    rng = np.random.default_rng(41)
+    for L, R in _subcritical_small_jumps(rng, 1000):
+        a, sa = oracle.roe1_edge(L, R, G)
+        b, sb = oracle.roe1_edge_fix(L, R, G)
+        assert np.array_equal(a, b) and sa == sb
+    # supercritical flow with moderate jumps: every speed has the sign of u
+    for L, R in _subcritical_small_jumps(rng, 500):
+        sg = rng.choice([-1.0, 1.0])
+        for st in (L, R):
+            st[1] = sg * rng.uniform(2.5, 3.5) * math.sqrt(G * st[0]) * st[0]
+        a, _ = oracle.roe1_edge(L, R, G)
+        b, _ = oracle.roe1_edge_fix(L, R, G)
+        assert np.array_equal(a, b)
+    # a lake at rest over a step
+    L = np.array([2.0, 0.0, 0.0, 0.0, -0.3])
+    R = np.array([1.7, 0.0, 0.0, 0.0, 0.0])
+    assert np.array_equal(oracle.roe1_edge(L, R, G)[0], oracle.roe1_edge_fix(L, R, G)[0])
+
+
+def test_entropy_fix_acts_on_transonic_rarefactions_and_stays_conservative():
+    # the fix changes the flux, and seen from both sides of the edge mass,
+    # transverse momentum and pollutant are still conserved and the normal
+    # momentum jump is still S dH (a wave is split, its total flux jump kept)
+    rng = np.random.default_rng(42)
+    changed = 0
+    for L, R in _transonic_dam_breaks(rng, 1000):
+        phi_ij, _ = oracle.roe1_edge_fix(L, R, G)
+        plain, _ = oracle.roe1_edge(L, R, G)
+        changed += not np.array_equal(phi_ij, plain)
+        phi_ji, _ = oracle.roe1_edge_fix(_flip(R, [1, 2]), _flip(L, [1, 2]), G)
+        into_j = np.array([-phi_ji[0], phi_ji[1], phi_ji[2], -phi_ji[3]])
+        h = 0.5 * (L[0] + R[0])
+        scale = abs(phi_ij).max() + 1.0
+        assert abs(into_j[0] - phi_ij[0]) < 1e-13 * scale
+        assert abs(into_j[2] - phi_ij[2]) < 1e-13 * scale
+        assert abs(into_j[3] - phi_ij[3]) < 1e-13 * scale
+        assert abs((into_j[1] - phi_ij[1]) - G * h * (R[4] - L[4])) < 1e-12 * scale
+    assert changed > 800   # most of these straddle the edge

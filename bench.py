@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--path", choices=["auto", "edge", "recompute"], default="auto",
                     help="kernel path: the fused kernels (auto), the explicit-edge path, or the fused "
                          "kernel with every cell evaluating all its edges (recompute, an ablation)")
+    ap.add_argument("--entropy-fix", action="store_true",
+                    help="with the Harten-Hyman entropy fix (one layer, IR-Roe)")
     ap.add_argument("--scheme", choices=["ir", "classical"], default="ir",
                     help="numerical flux: IR-Roe (default) or the classical Roe flux")
     ap.add_argument("--repeats", type=int, default=3)
@@ -198,6 +200,7 @@ def main():
         return
     w = inputs.make_config(args.config)
     w.scheme = args.scheme
+    w.entropy_fix = int(args.entropy_fix)
     prec = args.precision or w.precision
     K = args.steps or w.nsteps
     stream = torch.cuda.Stream()
@@ -251,7 +254,8 @@ def main():
     src_hash = kernel_source_hash(ROOT)
     # counters are recorded per kernel instance: the classical-flux kernel is
     # another instance (its own name in the traffic table)
-    traffic = measured_traffic(kernel + ("-classical" if args.scheme == "classical" else ""), args.config, src_hash)
+    variant = ("-classical" if args.scheme == "classical" else "") + ("-hh" if args.entropy_fix else "")
+    traffic = measured_traffic(kernel + variant, args.config, src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": kernel, "alg_bytes_per_cell": bpc, "src_hash": src_hash}
@@ -269,8 +273,9 @@ def main():
         "dtype": prec,
         "data": "synthetic",
         "config": {"workload": f"config {args.config}: {WORKLOADS[args.config]}"
-                               + (" (classical Roe flux)" if args.scheme == "classical" else ""), "cells": N,
-                   "scheme": args.scheme,
+                               + (" (classical Roe flux)" if args.scheme == "classical" else "")
+                               + (" (Harten-Hyman entropy fix)" if args.entropy_fix else ""), "cells": N,
+                   "scheme": args.scheme, "entropy_fix": bool(args.entropy_fix),
                    "precision": prec, "path": used_path, "simulated_seconds": t_adv},
         "roofline": roofline,
     }

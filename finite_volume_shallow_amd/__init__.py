@@ -26,6 +26,7 @@ SWE_F64, SWE_F32 = 0, 1
 SWE_BC_WALL, SWE_BC_PERIODIC = 0, 1
 SWE_PATH_AUTO, SWE_PATH_EDGE, SWE_PATH_FUSED, SWE_PATH_RECOMPUTE = 0, 1, 2, 3
 SWE_SCHEME_IR_ROE, SWE_SCHEME_ROE = 0, 1
+SWE_ENTROPY_FIX_NONE, SWE_ENTROPY_FIX_HH = 0, 1
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I32 = ctypes.POINTER(ctypes.c_int32)
@@ -36,7 +37,7 @@ class swe_mesh_desc(ctypes.Structure):
         ("abi_version", ctypes.c_int32), ("mesh_kind", ctypes.c_int32),
         ("nlayers", ctypes.c_int32), ("ntracers", ctypes.c_int32),
         ("precision", ctypes.c_int32), ("path", ctypes.c_int32),
-        ("scheme", ctypes.c_int32),
+        ("scheme", ctypes.c_int32), ("entropy_fix", ctypes.c_int32),
         ("g", ctypes.c_double), ("r", ctypes.c_double),
         ("nx", ctypes.c_int64), ("ny", ctypes.c_int64),
         ("dx", ctypes.c_double), ("dy", ctypes.c_double),
@@ -183,7 +184,7 @@ def swe_path(ctx):
 # ------------------------------------------------------------------ helpers
 
 def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUTO,
-              scheme="ir", g=9.81, r=0.0, nx=0, ny=0, dx=0.0, dy=0.0, bc_x="wall", bc_y="wall",
+              scheme="ir", entropy_fix=0, g=9.81, r=0.0, nx=0, ny=0, dx=0.0, dy=0.0, bc_x="wall", bc_y="wall",
               node_xy=None, tri=None, stream=None):
     """Fill a swe_mesh_desc.  Returns (desc, keepalive) - keep the second
     value referenced until swe_create_mesh returned."""
@@ -197,6 +198,7 @@ def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUT
     if scheme not in ("ir", "classical"):
         raise ValueError(f"unknown scheme {scheme!r}")
     d.scheme = SWE_SCHEME_ROE if scheme == "classical" else SWE_SCHEME_IR_ROE
+    d.entropy_fix = int(entropy_fix)
     d.g = g
     d.r = r
     keep = []
@@ -220,10 +222,11 @@ def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUT
 def desc_from_workload(w, path=SWE_PATH_AUTO, stream=None, precision=None):
     """Mesh description of an object with the fields of a workload record
     (kind, nlayers, ntracers, precision, g, r, nx, ny, dx, dy, bc_x, bc_y,
-    node_xy, tri, and optionally scheme)."""
+    node_xy, tri, and optionally scheme and entropy_fix)."""
     return mesh_desc(kind=w.kind, nlayers=w.nlayers, ntracers=w.ntracers,
                      precision=precision or w.precision, path=path,
-                     scheme=getattr(w, "scheme", "ir"), g=w.g, r=w.r,
+                     scheme=getattr(w, "scheme", "ir"), entropy_fix=getattr(w, "entropy_fix", 0),
+                     g=w.g, r=w.r,
                      nx=w.nx, ny=w.ny, dx=w.dx, dy=w.dy, bc_x=w.bc_x, bc_y=w.bc_y,
                      node_xy=w.node_xy, tri=w.tri, stream=stream)
 

@@ -128,11 +128,12 @@ template <typename T> struct EF {
 // transverse).  [IR] Sec. 2.2 steps 1-3 with one layer: Roe averages,
 // X = F(W_b) - F(W_a) - S dH, P^- X by the 2x2 eigen-decomposition,
 // the transverse momentum and the pollutant upwinded by the mass flux.
-// CL: the classical Roe flux of the whole system instead, whose transverse
-// momentum and pollutant rows are contact waves of speed ubar (Roe averages
-// vbar, Cbar of the transverse velocity and the concentration, weighted by
-// sqrt(h) like ubar).
-template <typename T, bool TR, bool CL>
+// FX = FLUX_ROE: the classical Roe flux of the whole system instead, whose
+// transverse momentum and pollutant rows are contact waves of speed ubar
+// (Roe averages vbar, Cbar of the transverse velocity and the
+// concentration, weighted by sqrt(h) like ubar).  FX = FLUX_IR_HH: IR-Roe
+// with the Harten-Hyman entropy fix (hh_fix).
+template <typename T, bool TR, int FX>
 __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, T hR, T sR, T qR, T uR, T tR,
                                       T cR, T zR, T g)
 {
@@ -149,13 +150,14 @@ __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, 
     const T a1 = (lam2 * X0 - X1) * i2c;
     const T a2 = (X1 - lam1 * X0) * i2c;
     const T w1 = wminus(lam1), w2 = wminus(lam2);
-    const T pm0 = w1 * a1 + w2 * a2;
-    const T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    T pm0 = w1 * a1 + w2 * a2;
+    T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    if (FX == FLUX_IR_HH) hh_fix(hL, qL, uL, hR, qR, uR, lam1, lam2, i2c, g, pm0, pm1);
     o.am = pm0;
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
-    if (CL) {
+    if (FX == FLUX_ROE) {
         const T wu = wminus(ubar);
         const T vbar = (sL * tL + sR * tR) * isum;
         const T Xt = qR * tR - qL * tL;
@@ -290,7 +292,7 @@ constexpr int PREFETCH = 2;
 // recomputed edge are bit-identical to the shared one's; the results agree
 // to rounding (the compiler may contract the two evaluations' multiply-adds
 // differently).
-template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL, bool RC>
+template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC>
 __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
                                          bool &bad_depth, bool &bad_val)
@@ -306,7 +308,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     // ---- x-edge (lane, lane+1) of row r
     const T Rh = nxt(cur.h), Rs = nxt(cur.s), Ru = nxt(cur.u), Rv = nxt(cur.v), Rc = nxt(cur.cc),
             Rz = nxt(cur.z), Rq = nxt(cur.qx);
-    EF<T> ex = flux<T, TR, CL>(cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, Rh, Rs, Rq, Ru, Rv, Rc, Rz, g);
+    EF<T> ex = flux<T, TR, FX>(cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, Rh, Rs, Rq, Ru, Rv, Rc, Rz, g);
     if (XW && K.xwall_lane) {
         if (K.colok) { // wall on the right of this lane's cell
             wall(cur.h, cur.qx, cur.v, cur.cc, g, ex.am, ex.an, ex.at, ex.ac);
@@ -326,7 +328,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         // the left x-edge (lane-1, lane) of row r, evaluated again here
         const T Lh = prv(cur.h), Ls = prv(cur.s), Lu = prv(cur.u), Lv = prv(cur.v), Lc = prv(cur.cc),
                 Lz = prv(cur.z), Lq = prv(cur.qx);
-        EF<T> el = flux<T, TR, CL>(Lh, Ls, Lq, Lu, Lv, Lc, Lz, cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, g);
+        EF<T> el = flux<T, TR, FX>(Lh, Ls, Lq, Lu, Lv, Lc, Lz, cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, g);
         if (XW && K.lwall_lane) {
             el.bm = el.bn = el.bt = el.bc = T(0);
             if (K.colok) { // wall on the left of this lane's cell (as seen by the lane on the left)
@@ -351,7 +353,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 
     // ---- y-edge (row r-1, row r): normal (0, 1), qn = qy, ut = -u;
     // back-rotation (m, n, t, c) -> (m, -t, n, c)
-    EF<T> ey = flux<T, TR, CL>(prev.h, prev.s, prev.qy, prev.v, -prev.u, prev.cc, prev.z, cur.h, cur.s, cur.qy, cur.v,
+    EF<T> ey = flux<T, TR, FX>(prev.h, prev.s, prev.qy, prev.v, -prev.u, prev.cc, prev.z, cur.h, cur.s, cur.qy, cur.v,
                            -cur.u, cur.cc, cur.z, g);
     if (YW && I.prevrow != currow) {
         if (I.prevrow) { // wall above row r-1
@@ -389,7 +391,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         T ybm = I.yb_m, ybt = I.yb_t, ybn = I.yb_n, ybc = I.yb_c;
         if constexpr (RC) { // the bottom y-edge (r-2, r-1), evaluated again
             const PC<T> &p2 = I.prev2;
-            EF<T> eb = flux<T, TR, CL>(p2.h, p2.s, p2.qy, p2.v, -p2.u, p2.cc, p2.z, prev.h, prev.s, prev.qy, prev.v,
+            EF<T> eb = flux<T, TR, FX>(p2.h, p2.s, p2.qy, p2.v, -p2.u, p2.cc, p2.z, prev.h, prev.s, prev.qy, prev.v,
                                        -prev.u, prev.cc, prev.z, g);
             if (YW && I.prev2row != I.prevrow) {
                 eb.bm = eb.bn = eb.bt = eb.bc = T(0);
@@ -487,7 +489,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 // tile's rows reach a wall in y.  Tiles with neither (almost all of them)
 // run without any wall code.  Returns the tile's largest Eq. (5) speed sum
 // sum |G| ||D|| (the smallest dt candidate is 2 gamma |V| over it).
-template <typename T, bool TR, bool XW, bool YW, bool DN, bool CL, bool RC>
+template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC>
 __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, int lane, double dtd, T &smax_out,
                                           unsigned &bad_out)
 {
@@ -552,30 +554,30 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     // another), so no register is copied between rows.
     int r = K.j0 - 1;
     for (; r + 3 <= K.rlast; r += 4) {
-        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
     }
-    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, CL, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
     smax_out = smax;
     bad_out = (bad_depth ? FLAG_DEPTH : 0u) | (bad_val ? FLAG_NONFINITE : 0u);
 }
 
 // The tile variant for its walls (x, y) and march direction.
-template <typename T, bool TR, bool DN, bool CL, bool RC>
+template <typename T, bool TR, bool DN, int FX, bool RC>
 __device__ __forceinline__ void cart_tile_dispatch(const CartArgs<T, TR> &A, int tile, int lane, double dtd, bool xw,
                                                    bool yw, T &smax, unsigned &bad)
 {
-    if (!xw && !yw) cart_tile<T, TR, false, false, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
-    else if (!yw) cart_tile<T, TR, true, false, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
-    else if (!xw) cart_tile<T, TR, false, true, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
-    else cart_tile<T, TR, true, true, DN, CL, RC>(A, tile, lane, dtd, smax, bad);
+    if (!xw && !yw) cart_tile<T, TR, false, false, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
+    else if (!yw) cart_tile<T, TR, true, false, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
+    else if (!xw) cart_tile<T, TR, false, true, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
+    else cart_tile<T, TR, true, true, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
 }
 
-template <typename T, bool TR, bool CL = false, bool RC = false>
+template <typename T, bool TR, int FX = FLUX_IR, bool RC = false>
 __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
 {
     const int lane = threadIdx.x;
@@ -605,8 +607,8 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     // on large grids odd row blocks march downward: neighbouring blocks then
     // reach the rows they share (each other's halo) at about the same time,
     // while those rows are still in L2
-    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, CL, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
-    else cart_tile_dispatch<T, TR, false, CL, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
+    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, FX, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
+    else cart_tile_dispatch<T, TR, false, FX, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
 
     // the tile's dt candidate 2 gamma |V| / max sum |G| ||D|| (Eq. (5))
     const double dmin = wave_min(smax > T(0) ? (double)(T(2) * A.cfl * A.dx * A.dy / smax) : __builtin_inf());
@@ -710,7 +712,7 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     return A;
 }
 
-template <typename T, bool TR, bool CL = false, bool RC = false>
+template <typename T, bool TR, int FX = FLUX_IR, bool RC = false>
 static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
     hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
@@ -724,28 +726,25 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
         const unsigned grid = (unsigned)(A.per_xcd * NUM_XCD);
-        hipLaunchKernelGGL((k_cart_fused<T, TR, CL, RC>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
+        hipLaunchKernelGGL((k_cart_fused<T, TR, FX, RC>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
+template <int FX, bool RC> static hipError_t cart_batch_fx(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
-    if (c->path == SWE_PATH_RECOMPUTE) { // IR-Roe only
-        if (c->ntracers)
-            return f32 ? cart_batch_t<float, true, false, true>(c, nsteps, cfl)
-                       : cart_batch_t<double, true, false, true>(c, nsteps, cfl);
-        return f32 ? cart_batch_t<float, false, false, true>(c, nsteps, cfl)
-                   : cart_batch_t<double, false, false, true>(c, nsteps, cfl);
-    }
-    if (c->classical) {
-        if (c->ntracers)
-            return f32 ? cart_batch_t<float, true, true>(c, nsteps, cfl) : cart_batch_t<double, true, true>(c, nsteps, cfl);
-        return f32 ? cart_batch_t<float, false, true>(c, nsteps, cfl) : cart_batch_t<double, false, true>(c, nsteps, cfl);
-    }
-    if (c->ntracers) return f32 ? cart_batch_t<float, true>(c, nsteps, cfl) : cart_batch_t<double, true>(c, nsteps, cfl);
-    return f32 ? cart_batch_t<float, false>(c, nsteps, cfl) : cart_batch_t<double, false>(c, nsteps, cfl);
+    if (c->ntracers)
+        return f32 ? cart_batch_t<float, true, FX, RC>(c, nsteps, cfl) : cart_batch_t<double, true, FX, RC>(c, nsteps, cfl);
+    return f32 ? cart_batch_t<float, false, FX, RC>(c, nsteps, cfl) : cart_batch_t<double, false, FX, RC>(c, nsteps, cfl);
+}
+
+hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
+{
+    if (c->path == SWE_PATH_RECOMPUTE) return cart_batch_fx<FLUX_IR, true>(c, nsteps, cfl); // IR-Roe only
+    if (c->classical) return cart_batch_fx<FLUX_ROE, false>(c, nsteps, cfl);
+    if (c->hh) return cart_batch_fx<FLUX_IR_HH, false>(c, nsteps, cfl);
+    return cart_batch_fx<FLUX_IR, false>(c, nsteps, cfl);
 }
 
 } // namespace swe

@@ -24,8 +24,8 @@ template <typename T> struct EdgeArrays {
     const T *nx, *ny, *len;
 };
 
-// CL: classical Roe flux (one layer) instead of IR-Roe.
-template <typename T, int NL, bool TR, bool CL>
+// FX: the flux variant (FLUX_IR, FLUX_ROE, FLUX_IR_HH).
+template <typename T, int NL, bool TR, int FX>
 __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, StatePtrs<T> W,
                                                    const T *__restrict__ z, T g, T r,
                                                    T *__restrict__ out, unsigned *flags)
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, 
             const T hb = W.v[0][b], qxb = W.v[1][b], qyb = W.v[2][b];
             const T cb = TR ? W.v[3][b] : T(0);
             const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-            f = roe1_interior<T, TR, CL>(ha, qna, qta, ca, z[a], hb, qnb, qtb, cb, z[b], g);
+            f = roe1_interior<T, TR, FX>(ha, qna, qta, ca, z[a], hb, qnb, qtb, cb, z[b], g);
         } else {
             f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
         }
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, 
                 R[3 * l + 1] = qx * nx + qy * ny;
                 R[3 * l + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T, CL>(L, z[a], R, z[b], g, r);
+            f = roe2_interior<T, FX == FLUX_ROE>(L, z[a], R, z[b], g, r);
         } else {
             f = roe2_wall<T>(L, z[a], g, r);
         }
@@ -183,7 +183,7 @@ template <typename T> static StatePtrs<T> state_ptrs(swe_ctx *c)
     return p;
 }
 
-template <typename T, int NL, bool TR, bool CL = false>
+template <typename T, int NL, bool TR, int FX = FLUX_IR>
 static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -192,7 +192,7 @@ static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
     StatePtrs<T> W = state_ptrs<T>(c);
     T *out = (T *)c->e_out;
     const dim3 ge((unsigned)((c->E + bs - 1) / bs)), gc((unsigned)((c->N + bs - 1) / bs));
-    hipLaunchKernelGGL((k_edge_flux<T, NL, TR, CL>), ge, dim3(bs), 0, c->stream, c->E, ed, W,
+    hipLaunchKernelGGL((k_edge_flux<T, NL, TR, FX>), ge, dim3(bs), 0, c->stream, c->E, ed, W,
                        (const T *)c->zbed, (T)c->g, (T)c->r, out, c->book.flags);
     hipLaunchKernelGGL((k_cell_dt<T, NV>), gc, dim3(bs), 0, c->stream, c->N, c->E, c->c_off, c->c_edge,
                        (const T *)c->c_area, (const T *)out, (T)cfl, c->book.slots + (step % 3));
@@ -201,21 +201,19 @@ static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
     return hipGetLastError();
 }
 
-hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl)
+template <int FX> static hipError_t edge_step_fx(swe_ctx *c, int64_t step, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
-    if (c->nlayers == 2) {
-        if (c->classical)
-            return f32 ? edge_step_t<float, 2, false, true>(c, step, cfl) : edge_step_t<double, 2, false, true>(c, step, cfl);
-        return f32 ? edge_step_t<float, 2, false>(c, step, cfl) : edge_step_t<double, 2, false>(c, step, cfl);
-    }
-    if (c->classical) {
-        if (c->ntracers)
-            return f32 ? edge_step_t<float, 1, true, true>(c, step, cfl) : edge_step_t<double, 1, true, true>(c, step, cfl);
-        return f32 ? edge_step_t<float, 1, false, true>(c, step, cfl) : edge_step_t<double, 1, false, true>(c, step, cfl);
-    }
-    if (c->ntracers) return f32 ? edge_step_t<float, 1, true>(c, step, cfl) : edge_step_t<double, 1, true>(c, step, cfl);
-    return f32 ? edge_step_t<float, 1, false>(c, step, cfl) : edge_step_t<double, 1, false>(c, step, cfl);
+    if (c->nlayers == 2) return f32 ? edge_step_t<float, 2, false, FX>(c, step, cfl) : edge_step_t<double, 2, false, FX>(c, step, cfl);
+    if (c->ntracers) return f32 ? edge_step_t<float, 1, true, FX>(c, step, cfl) : edge_step_t<double, 1, true, FX>(c, step, cfl);
+    return f32 ? edge_step_t<float, 1, false, FX>(c, step, cfl) : edge_step_t<double, 1, false, FX>(c, step, cfl);
+}
+
+hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl)
+{
+    if (c->classical) return edge_step_fx<FLUX_ROE>(c, step, cfl);
+    if (c->hh) return edge_step_fx<FLUX_IR_HH>(c, step, cfl); // one layer only (checked at create)
+    return edge_step_fx<FLUX_IR>(c, step, cfl);
 }
 
 } // namespace swe

@@ -110,9 +110,9 @@ template <typename T, int NL, int NV> __device__ __forceinline__ void tri_cellpr
 }
 
 // Fluctuations |G| T^-1 (...) of both sides of a local edge between the
-// cell records A and B (B == nullptr: a wall), in the x-y frame.  CL: the
-// classical Roe flux (one layer) instead of IR-Roe.
-template <typename T, int NL, bool TR, int NV, bool CL = false>
+// cell records A and B (B == nullptr: a wall), in the x-y frame.  FX: the
+// flux variant (FLUX_IR, FLUX_ROE, FLUX_IR_HH; two layers: FLUX_ROE or not).
+template <typename T, int NL, bool TR, int NV, int FX = FLUX_IR>
 __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, const TriCell<T, NL, NV> &CB, bool wall,
                                               T nx, T ny, T len, T g, T rr, T (&Fa)[NV], T (&Fb)[NV],
                                               unsigned &bad)
@@ -127,7 +127,7 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
             const T hb = B[0], qxb = B[1], qyb = B[2];
             const T cb = TR ? B[3] : T(0);
             const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-            f = roe1_pre<T, TR, CL>(ha, CA.sq(), CA.ih(), qna, qta, ca, CA.z(), hb, CB.sq(), CB.ih(), qnb, qtb, cb,
+            f = roe1_pre<T, TR, FX>(ha, CA.sq(), CA.ih(), qna, qta, ca, CA.z(), hb, CB.sq(), CB.ih(), qnb, qtb, cb,
                                 CB.z(), g);
         } else {
             f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
@@ -160,7 +160,7 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
                 Rs[3 * l2 + 1] = qx * nx + qy * ny;
                 Rs[3 * l2 + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T, CL>(L, CA.z(), Rs, CB.z(), g, rr);
+            f = roe2_interior<T, FX == FLUX_ROE>(L, CA.z(), Rs, CB.z(), g, rr);
         } else {
             f = roe2_wall<T>(L, CA.z(), g, rr);
         }
@@ -270,7 +270,7 @@ __device__ __forceinline__ uint32_t tri_unpack(double x) { return (uint32_t)x; }
 // three of its edges itself (interior edges twice over), for the fluxes and
 // for the Eq. (5) speeds; the LDS edge records then hold the edges' cell
 // pair and geometry.  Same inputs per edge, same accumulation order.
-template <typename T, int NL, bool TR, bool DT0, int RD, int NT, bool CL = false, bool RC = false>
+template <typename T, int NL, bool TR, bool DT0, int RD, int NT, int FX = FLUX_IR, bool RC = false>
 __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
                     T nx, ny, len;
                     slot_edge((unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu, la, lb, wall, nx, ny, len, sb);
                     T Fa[NV], Fb[NV];
-                    tri_edge_flux<T, NL, TR, NV, CL>(Cell(sm, LCM, la), Cell(sm, LCM, lb), wall, nx, ny, len, g, rr,
+                    tri_edge_flux<T, NL, TR, NV, FX>(Cell(sm, LCM, la), Cell(sm, LCM, lb), wall, nx, ny, len, g, rr,
                                                      Fa, Fb, bad);
 #pragma unroll
                     for (int v = 0; v < NV; ++v) acc[v] += sb ? Fb[v] : Fa[v];
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
                 const unsigned lb = eab[m] >> 16;
                 const bool wall = lb == 0xFFFFu;
                 T Fa[NV], Fb[NV];
-                tri_edge_flux<T, NL, TR, NV, CL>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)), Cell(sm, LCM, wall ? 0 : (int)lb),
+                tri_edge_flux<T, NL, TR, NV, FX>(Cell(sm, LCM, (int)(eab[m] & 0xFFFFu)), Cell(sm, LCM, wall ? 0 : (int)lb),
                                              wall, enx[m], eny[m], elen[m], g, rr, Fa, Fb, bad);
                 T *fa = fl + ER * k, *fb = fl + ER * (EM + k);
 #pragma unroll
@@ -626,7 +626,7 @@ __device__ __forceinline__ void tri_state(const TriArgs<T> &A, const TriBlk &b, 
     st[NV] = ld32(A.z, gi);
 }
 
-template <typename T, int NL, bool TR, int NT, bool CL = false>
+template <typename T, int NL, bool TR, int NT, int FX = FLUX_IR>
 __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         // ---- 2. every edge touching the block or ring 1, once
         if (tid < cb.ne) {
             T Fa[NV], Fb[NV];
-            tri_edge_flux<T, NL, TR, NV, CL>(Cell(sm, LCM, (int)la), Cell(sm, LCM, wall ? 0 : (int)lb), wall, enx, eny,
+            tri_edge_flux<T, NL, TR, NV, FX>(Cell(sm, LCM, (int)la), Cell(sm, LCM, wall ? 0 : (int)lb), wall, enx, eny,
                                          elen, g, rr, Fa, Fb, bad);
             T *fa = fl + ER * tid, *fb = fl + ER * (EM + tid);
 #pragma unroll
@@ -841,9 +841,9 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     return A;
 }
 
-// CL: classical Roe flux.  The initial-state dt prologue computes speeds
+// FX: the flux variant.  The initial-state dt prologue computes speeds
 // only, which both fluxes share, so it is the IR-Roe instance.
-template <typename T, int NL, bool TR, int RD, int NT, bool CL, bool RC = false>
+template <typename T, int NL, bool TR, int RD, int NT, int FX, bool RC = false>
 static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
@@ -853,7 +853,7 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     if (lds > 65536) {
         hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, true, RD, NT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, CL, RC>,
+        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, FX, RC>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     }
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
@@ -862,11 +862,11 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     if constexpr (RD == 1 && !RC) {
         if (c->tb.pipe_wgs != 0) {
             if (lds > 65536)
-                hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT, CL>,
+                hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT, FX>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (c->tb.pipe_wgs < 0) { // as many workgroups as can be resident at once
                 int per_cu = 0, cus = 0;
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT, CL>, NT, lds) !=
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT, FX>, NT, lds) !=
                         hipSuccess ||
                     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess)
                     return hipErrorUnknown;
@@ -874,17 +874,17 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
             }
             const dim3 pgrid((unsigned)(TRI_XCD * std::max(1, std::min(c->tb.pipe_wgs / TRI_XCD, per_xcd))));
             for (int64_t s = 0; s < nsteps; ++s)
-                hipLaunchKernelGGL((k_tri_pipe<T, NL, TR, NT, CL>), pgrid, block, lds, c->stream, tri_args<T>(c, s, cfl));
+                hipLaunchKernelGGL((k_tri_pipe<T, NL, TR, NT, FX>), pgrid, block, lds, c->stream, tri_args<T>(c, s, cfl));
             return hipGetLastError();
         }
     }
     for (int64_t s = 0; s < nsteps; ++s)
-        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT, CL, RC>), grid, block, lds, c->stream,
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, false, RD, NT, FX, RC>), grid, block, lds, c->stream,
                            tri_args<T>(c, s, cfl));
     return hipGetLastError();
 }
 
-template <typename T, int NL, bool TR, bool CL = false>
+template <typename T, int NL, bool TR, int FX = FLUX_IR>
 static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
     // 512 threads per workgroup (eight wavefronts: the block's latency is
@@ -892,12 +892,12 @@ static hipError_t tri_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     // rounds of threads cover the largest local cell / edge / update counts
     // (checked at create)
     if (c->tb.nt == 512) {
-        if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 512, CL>(c, nsteps, cfl);
-        return tri_batch_rd<T, NL, TR, 2, 512, CL>(c, nsteps, cfl);
+        if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 512, FX>(c, nsteps, cfl);
+        return tri_batch_rd<T, NL, TR, 2, 512, FX>(c, nsteps, cfl);
     }
-    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 256, CL>(c, nsteps, cfl);
-    if (c->tb.rounds <= 2) return tri_batch_rd<T, NL, TR, 2, 256, CL>(c, nsteps, cfl);
-    return tri_batch_rd<T, NL, TR, 3, 256, CL>(c, nsteps, cfl);
+    if (c->tb.rounds <= 1) return tri_batch_rd<T, NL, TR, 1, 256, FX>(c, nsteps, cfl);
+    if (c->tb.rounds <= 2) return tri_batch_rd<T, NL, TR, 2, 256, FX>(c, nsteps, cfl);
+    return tri_batch_rd<T, NL, TR, 3, 256, FX>(c, nsteps, cfl);
 }
 
 // The recomputation variant (IR-Roe, 512 threads per workgroup).
@@ -910,20 +910,25 @@ template <typename T, int NL, bool TR> static hipError_t tri_batch_rc(swe_ctx *c
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     const bool f32 = c->prec == SWE_F32;
-    if (c->path == SWE_PATH_RECOMPUTE) {
+    if (c->path == SWE_PATH_RECOMPUTE) { // IR-Roe only
         if (c->nlayers == 2) return f32 ? tri_batch_rc<float, 2, false>(c, nsteps, cfl) : tri_batch_rc<double, 2, false>(c, nsteps, cfl);
         if (c->ntracers) return f32 ? tri_batch_rc<float, 1, true>(c, nsteps, cfl) : tri_batch_rc<double, 1, true>(c, nsteps, cfl);
         return f32 ? tri_batch_rc<float, 1, false>(c, nsteps, cfl) : tri_batch_rc<double, 1, false>(c, nsteps, cfl);
     }
     if (c->nlayers == 2) {
         if (c->classical)
-            return f32 ? tri_batch_t<float, 2, false, true>(c, nsteps, cfl) : tri_batch_t<double, 2, false, true>(c, nsteps, cfl);
+            return f32 ? tri_batch_t<float, 2, false, FLUX_ROE>(c, nsteps, cfl) : tri_batch_t<double, 2, false, FLUX_ROE>(c, nsteps, cfl);
         return f32 ? tri_batch_t<float, 2, false>(c, nsteps, cfl) : tri_batch_t<double, 2, false>(c, nsteps, cfl);
     }
     if (c->classical) {
         if (c->ntracers)
-            return f32 ? tri_batch_t<float, 1, true, true>(c, nsteps, cfl) : tri_batch_t<double, 1, true, true>(c, nsteps, cfl);
-        return f32 ? tri_batch_t<float, 1, false, true>(c, nsteps, cfl) : tri_batch_t<double, 1, false, true>(c, nsteps, cfl);
+            return f32 ? tri_batch_t<float, 1, true, FLUX_ROE>(c, nsteps, cfl) : tri_batch_t<double, 1, true, FLUX_ROE>(c, nsteps, cfl);
+        return f32 ? tri_batch_t<float, 1, false, FLUX_ROE>(c, nsteps, cfl) : tri_batch_t<double, 1, false, FLUX_ROE>(c, nsteps, cfl);
+    }
+    if (c->hh) {
+        if (c->ntracers)
+            return f32 ? tri_batch_t<float, 1, true, FLUX_IR_HH>(c, nsteps, cfl) : tri_batch_t<double, 1, true, FLUX_IR_HH>(c, nsteps, cfl);
+        return f32 ? tri_batch_t<float, 1, false, FLUX_IR_HH>(c, nsteps, cfl) : tri_batch_t<double, 1, false, FLUX_IR_HH>(c, nsteps, cfl);
     }
     if (c->ntracers) return f32 ? tri_batch_t<float, 1, true>(c, nsteps, cfl) : tri_batch_t<double, 1, true>(c, nsteps, cfl);
     return f32 ? tri_batch_t<float, 1, false>(c, nsteps, cfl) : tri_batch_t<double, 1, false>(c, nsteps, cfl);

@@ -54,6 +54,42 @@ template <> __device__ __forceinline__ double wminus(double lam)
     return fmin(fmax(__builtin_fma(lam, -0x1p600, 0.5), 0.0), 1.0);
 }
 
+// Flux variants of the one-layer edge: IR-Roe, the classical Roe flux of
+// the whole edge system, IR-Roe with the Harten-Hyman entropy fix.
+enum : int { FLUX_IR = 0, FLUX_ROE = 1, FLUX_IR_HH = 2 };
+
+// Harten-Hyman entropy fix of the 2x2 Roe solution ([IR] Sec. 2.2 names the
+// fix of its ref. 25).  b = K^-1 (W_b - W_a) are the waves' state jumps and
+// W* = W_a + b1 r1 the state between them; a wave whose characteristic
+// speed is < 0 on its left state and > 0 on its right one (a transonic
+// rarefaction) is split into a part moving left at the left speed and one
+// moving right at the right speed, carrying the fraction
+// (lam_right - lam~)/(lam_right - lam_left) to the left, so its left-going
+// flux jump min(lam~, 0) b r becomes lam_left (lam_right - lam~) /
+// (lam_right - lam_left) b r.  (pm0, pm1) is the left-going flux jump P^- X;
+// the source part of each wave is untouched.  i2c = 1 / (lam2 - lam1).
+template <typename T>
+__device__ __forceinline__ void hh_fix(T hL, T qL, T uL, T hR, T qR, T uR, T lam1, T lam2, T i2c, T g, T &pm0,
+                                       T &pm1)
+{
+    const T dh = hR - hL, dq = qR - qL;
+    const T b1 = (lam2 * dh - dq) * i2c;
+    const T b2 = (dq - lam1 * dh) * i2c;
+    const T hs = hL + b1, qs = qL + b1 * lam1;
+    // a wave can only be transonic if W* is supercritical (u* - c* > 0 for
+    // the first, u* + c* < 0 for the second): q*^2 > g h*^3, no root needed
+    if (hs > T(0) && qs * qs > g * hs * hs * hs) {
+        const T us = qs * FM<T>::rcp(hs), cs = FM<T>::sqrt(g * hs);
+        const T l1L = uL - FM<T>::sqrt(g * hL), l1R = us - cs;
+        const T l2L = us + cs, l2R = uR + FM<T>::sqrt(g * hR);
+        T k1 = T(0), k2 = T(0);
+        if (l1L < T(0) && l1R > T(0)) k1 = (l1L * (l1R - lam1) * FM<T>::rcp(l1R - l1L) - fmin(lam1, T(0))) * b1;
+        if (l2L < T(0) && l2R > T(0)) k2 = (l2L * (l2R - lam2) * FM<T>::rcp(l2R - l2L) - fmin(lam2, T(0))) * b2;
+        pm0 += k1 + k2;
+        pm1 += k1 * lam1 + k2 * lam2;
+    }
+}
+
 // One-layer interior edge.  Inputs are edge-frame states: depth h, normal
 // discharge qn, transverse discharge qt, pollutant hc, bed z.
 // Output: fluctuations for side a (da*) and side b (db*), in the edge frame,
@@ -66,7 +102,7 @@ template <typename T, bool TRACER> struct Flux1 {
 
 // As roe1_interior, with sqrt(h) and 1/h of both cells supplied.
 //
-// CL selects the classical Roe flux of the whole edge system
+// FX = FLUX_ROE selects the classical Roe flux of the whole edge system
 // (h, qn, qt, hc): its Roe matrix adds to the 2x2 block two contact waves of
 // speed ubar, with eigenvectors e_qt and e_hc, while the acoustic
 // eigenvectors carry the Roe averages vbar, Cbar (sqrt(h)-weighted, like
@@ -74,7 +110,7 @@ template <typename T, bool TRACER> struct Flux1 {
 // alpha_c = X_c - Cbar X_0, the side-a fluctuation of those rows is
 // vbar (P^- X)_0 + w(ubar) alpha_t, and the same with Cbar; mass and normal
 // momentum are those of the IR-Roe flux.
-template <typename T, bool TRACER, bool CL = false>
+template <typename T, bool TRACER, int FX = FLUX_IR>
 __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T qtL, T cL, T zL, T hR, T sR,
                                                       T ihR, T qnR, T qtR, T cR, T zR, T g)
 {
@@ -94,14 +130,15 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     const T a1 = (lam2 * X0 - X1) * i2c;
     const T a2 = (X1 - lam1 * X0) * i2c;
     const T w1 = wminus(lam1), w2 = wminus(lam2);
-    const T pm0 = w1 * a1 + w2 * a2;
-    const T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    T pm0 = w1 * a1 + w2 * a2;
+    T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
+    if (FX == FLUX_IR_HH) hh_fix(hL, qnL, uL, hR, qnR, uR, lam1, lam2, i2c, g, pm0, pm1);
     o.am = pm0;
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
     const T utL = qtL * ihL, utR = qtR * ihR;
-    if (CL) {
+    if (FX == FLUX_ROE) {
         const T wu = wminus(ubar);
         const T vbar = (sL * utL + sR * utR) * isum;
         const T Xt = qnR * utR - qnL * utL;
@@ -145,12 +182,12 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     return o;
 }
 
-template <typename T, bool TRACER, bool CL = false>
+template <typename T, bool TRACER, int FX = FLUX_IR>
 __device__ __forceinline__ Flux1<T, TRACER> roe1_interior(T hL, T qnL, T qtL, T cL, T zL,
                                                            T hR, T qnR, T qtR, T cR, T zR, T g)
 {
     const T rL = FM<T>::rsq(hL), rR = FM<T>::rsq(hR);
-    return roe1_pre<T, TRACER, CL>(hL, hL * rL, rL * rL, qnL, qtL, cL, zL, hR, hR * rR, rR * rR, qnR, qtR, cR, zR, g);
+    return roe1_pre<T, TRACER, FX>(hL, hL * rL, rL * rL, qnL, qtL, cL, zL, hR, hR * rR, rR * rR, qnR, qtR, cR, zR, g);
 }
 
 // One-layer reflective wall seen from side a.

@@ -70,6 +70,12 @@ int validate(const swe_mesh_desc *d, std::string &err)
     if (d->precision != SWE_F64 && d->precision != SWE_F32) { err = "bad precision"; return SWE_E_INVAL; }
     if (d->path < SWE_PATH_AUTO || d->path > SWE_PATH_RECOMPUTE) { err = "bad path"; return SWE_E_INVAL; }
     if (d->scheme != SWE_SCHEME_IR_ROE && d->scheme != SWE_SCHEME_ROE) { err = "bad scheme"; return SWE_E_INVAL; }
+    if (d->entropy_fix != SWE_ENTROPY_FIX_NONE && d->entropy_fix != SWE_ENTROPY_FIX_HH) { err = "bad entropy_fix"; return SWE_E_INVAL; }
+    if (d->entropy_fix == SWE_ENTROPY_FIX_HH &&
+        (d->nlayers != 1 || d->scheme != SWE_SCHEME_IR_ROE || d->path == SWE_PATH_RECOMPUTE)) {
+        err = "the entropy fix is available for one layer with the IR-Roe flux on the fused and edge paths";
+        return SWE_E_INVAL;
+    }
     if (!(d->g > 0.0) || !std::isfinite(d->g)) { err = "g must be > 0"; return SWE_E_INVAL; }
     if (d->nlayers == 2 && !(d->r > 0.0 && d->r < 1.0)) { err = "r must lie in (0, 1)"; return SWE_E_INVAL; }
     if (d->mesh_kind == SWE_MESH_CART) {
@@ -243,6 +249,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         c->ntracers = d->ntracers;
         c->prec = d->precision;
         c->classical = d->scheme == SWE_SCHEME_ROE;
+        c->hh = d->entropy_fix == SWE_ENTROPY_FIX_HH;
         c->g = d->g;
         c->r = d->nlayers == 2 ? d->r : 0.0;
         c->nx = d->nx;

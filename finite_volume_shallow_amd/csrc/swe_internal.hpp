@@ -80,7 +80,8 @@ struct swe_ctx {
     int bc_x = 0, bc_y = 0;
     int64_t N = 0;
     int nv = 3;
-    bool classical = false; // classical Roe flux (one layer) instead of IR-Roe
+    bool classical = false; // classical Roe flux instead of IR-Roe
+    bool hh = false;        // Harten-Hyman entropy fix (one layer, IR-Roe)
     size_t rs = 8; // bytes per real
     int device = 0;
     hipStream_t stream = nullptr;

@@ -75,6 +75,18 @@ enum swe_path { SWE_PATH_AUTO = 0, SWE_PATH_EDGE = 1, SWE_PATH_FUSED = 2, SWE_PA
  * Eq. (5) time step. */
 enum swe_scheme { SWE_SCHEME_IR_ROE = 0, SWE_SCHEME_ROE = 1 };
 
+/* Entropy fix.  [IR] Sec. 2.2 notes that the Roe solution needs one where
+ * sonic rarefactions occur and names the Harten-Hyman fix.
+ * SWE_ENTROPY_FIX_HH: that fix in its wave-splitting form, on the 2x2 part
+ * of the one-layer IR-Roe flux: with b = K^-1 (W_b - W_a) the state jumps of
+ * the two Roe waves and W* = W_a + b_1 r_1 the state between them, a wave
+ * whose characteristic speed changes sign from < 0 on its left state to > 0
+ * on its right state is split into a left-moving part at the left speed and
+ * a right-moving part at the right speed (fractions chosen so that the
+ * wave's total flux jump is kept); the source term is untouched.  Available
+ * for one layer with the IR-Roe flux on the FUSED and EDGE paths. */
+enum swe_entropy_fix { SWE_ENTROPY_FIX_NONE = 0, SWE_ENTROPY_FIX_HH = 1 };
+
 typedef struct swe_mesh_desc {
     int32_t abi_version; /* must be SWE_ABI_VERSION                          */
     int32_t mesh_kind;   /* SWE_MESH_CART or SWE_MESH_TRI                    */
@@ -83,6 +95,7 @@ typedef struct swe_mesh_desc {
     int32_t precision;   /* SWE_F64 or SWE_F32: storage and arithmetic type  */
     int32_t path;        /* enum swe_path                                    */
     int32_t scheme;      /* enum swe_scheme                                  */
+    int32_t entropy_fix; /* 0: none; 1: Harten-Hyman (one layer, IR-Roe)     */
     double g;            /* gravity, > 0                                     */
     double r;            /* density ratio rho1/rho2 in (0, 1) (two layers)   */
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 def test_struct_layout_matches_header():
     # offsets follow the C layout of swe_mesh_desc on x86-64
     d = swe.swe_mesh_desc
-    assert d.scheme.offset == 24 and d.g.offset == 32 and d.nx.offset == 48
+    assert d.scheme.offset == 24 and d.entropy_fix.offset == 28 and d.g.offset == 32 and d.nx.offset == 48
     assert d.bc_x.offset == 80 and d.nnodes.offset == 88 and d.node_xy.offset == 104
     assert d.hip_stream.offset == 120 and ctypes.sizeof(d) == 128
 
@@ -47,7 +47,7 @@ def test_binding_constants_match_header():
     consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SWE_[A-Z0-9_]+) = (-?\d+)", hdr)}
     for name in ["SWE_MESH_CART", "SWE_MESH_TRI", "SWE_F64", "SWE_F32", "SWE_BC_WALL", "SWE_BC_PERIODIC",
                  "SWE_PATH_AUTO", "SWE_PATH_EDGE", "SWE_PATH_FUSED", "SWE_PATH_RECOMPUTE",
-                 "SWE_SCHEME_IR_ROE", "SWE_SCHEME_ROE"]:
+                 "SWE_SCHEME_IR_ROE", "SWE_SCHEME_ROE", "SWE_ENTROPY_FIX_NONE", "SWE_ENTROPY_FIX_HH"]:
         assert consts[name] == getattr(swe, name), name
 
 
@@ -110,6 +110,24 @@ def test_recompute_path_is_ir_roe_only():
         swe.swe_create_mesh(d)
     assert e.value.status == swe.SWE_E_INVAL
     d.path = 4
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
+
+
+def test_entropy_fix_is_one_layer_ir_roe_only():
+    for kw in (dict(scheme="classical"), dict(path=swe.SWE_PATH_RECOMPUTE)):
+        d, keep = swe.mesh_desc(kind="cart", nx=8, ny=8, dx=1.0, dy=1.0, entropy_fix=1, **kw)
+        with pytest.raises(swe.SweError) as e:
+            swe.swe_create_mesh(d)
+        assert e.value.status == swe.SWE_E_INVAL and "entropy" in str(e.value)
+    xy, tri = _square_mesh()
+    d, keep = swe.mesh_desc(kind="tri", node_xy=xy, tri=tri, nlayers=2, r=0.9, entropy_fix=1)
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL
+    d, keep = _cart()
+    d.entropy_fix = 3
     with pytest.raises(swe.SweError) as e:
         swe.swe_create_mesh(d)
     assert e.value.status == swe.SWE_E_INVAL

@@ -250,6 +250,89 @@ def test_recompute_in_every_tiling(tiling, monkeypatch):
     assert np.abs(da - db).max() <= RC_TOL[prec] * db.max()
 
 
+# The Harten-Hyman entropy fix: transonic dam breaks (the rarefaction
+# straddles the dam, so the fix acts every step) on a Cartesian strip and a
+# triangle mesh, and ordinary workloads with the fix switched on.
+def _transonic_cart(nx, ny):
+    w = inputs.config1(nx=nx, ny=ny)
+    x = (np.arange(nx) + 0.5) * w.dx
+    left = np.tile(x < nx * w.dx / 2, ny)
+    h = np.where(left, 1.0, 0.05)
+    w.state = [h, np.zeros_like(h), np.zeros_like(h), h * np.where(left, 1.0, 0.2)]
+    w.entropy_fix = 1
+    return w
+
+
+def _transonic_tri(nq):
+    w = inputs.config4(nq=nq)
+    w.z = np.zeros_like(w.z)
+    w.state[0] = np.where(w.state[0] > 2.0, 3.0, 0.12)
+    w.entropy_fix = 1
+    return w
+
+
+def _with_fix(make):
+    def f():
+        w = make()
+        w.entropy_fix = 1
+        return w
+    return f
+
+
+HH = {
+    "hh-dam-break-200x6-f64": (lambda: _transonic_cart(200, 6), 150, "f64"),
+    "hh-dam-break-131x5-f32": (lambda: _transonic_cart(131, 5), 100, "f32"),
+    "hh-tri-circular-24-f64": (lambda: _transonic_tri(24), 80, "f64"),
+    "hh-tri-circular-30-f32": (lambda: _transonic_tri(30), 60, "f32"),
+    "hh-c3-flow-160x96-f32": (_with_fix(CASES["c3-flow-160x96-f32"][0]), 100, "f32"),
+    "hh-c4-tri-ragged-19": (_with_fix(CASES["c4-tri-ragged-19"][0]), 25, "f64"),
+}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("name", list(HH))
+def test_parity_entropy_fix(name, path):
+    make, nsteps, prec = HH[name]
+    w = make()
+    say(f"[entropy fix] {name} path={path} steps={nsteps} prec={prec}")
+    got, dts, t = gpu_run(w, nsteps=nsteps, path=PATHS[path], precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    errs = field_errors(got, ref, w.g)
+    say(f"    field errors {['%.2e' % e for e in errs]}")
+    assert max(errs) <= tol, errs
+    dtol = 1e-12 if prec == "f64" else 1e-5
+    assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+
+
+@pytest.mark.parametrize("variant", ["ty4alt1", "ty12alt1", "per-block-128", "per-block-288"])
+def test_parity_entropy_fix_kernel_variants(variant, monkeypatch):
+    if variant.startswith("ty"):
+        ty, alt = variant[2:].split("alt")
+        monkeypatch.setenv("SWE_CART_TY", ty)
+        monkeypatch.setenv("SWE_CART_ALT", alt)
+        make, nsteps, prec = HH["hh-dam-break-200x6-f64"]
+    else:
+        for k, v in TRI_KERNELS[variant].items():
+            monkeypatch.setenv(k, v)
+        make, nsteps, prec = HH["hh-tri-circular-24-f64"]
+    w = make()
+    say(f"[entropy fix variant] {variant}")
+    got, dts, _ = gpu_run(w, nsteps=nsteps, precision=prec)
+    ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+    assert max(field_errors(got, ref, w.g)) <= FP64_TOL
+    assert np.abs(dts - rdts).max() <= 1e-12 * rdts.max()
+
+
+def test_entropy_fix_acts_on_gpu():
+    for make in (lambda: _transonic_cart(200, 6), lambda: _transonic_tri(24)):
+        w = make()
+        fixed, _, _ = gpu_run(w, nsteps=60)
+        w.entropy_fix = 0
+        plain, _, _ = gpu_run(w, nsteps=60)
+        assert np.abs(fixed[0] - plain[0]).max() > 1e-3
+
+
 def test_config1_symmetry_on_gpu():
     w = inputs.config1()
     say("[sym] config1 rows identical, qy == 0")

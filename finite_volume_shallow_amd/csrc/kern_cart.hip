@@ -219,9 +219,11 @@ template <typename T> __device__ __forceinline__ T &at(T *base, uint32_t k)
 
 // Load a row of W^n for this lane.  CHECK: the row or the column may lie
 // outside the domain (walls); such cells get benign placeholder values.
-// `row` is the grid row; sy = -1 loads the y-mirrored state (qy negated).
+// `row` is the grid row.  The values are raw: a downward-marching tile
+// negates qy where it uses them, not here, so that nothing waits on a load
+// before its row is needed.
 template <bool CHECK, typename T, bool TR>
-__device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int col, bool colok, T sy, T &h,
+__device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int col, bool colok, T &h,
                                          T &qx, T &qy, T &c, T &z, bool &rowok)
 {
     rowok = true;
@@ -233,7 +235,7 @@ __device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int 
         const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
         h = at(A.h, k);
         qx = at(A.qx, k);
-        qy = sy * at(A.qy, k);
+        qy = at(A.qy, k);
         c = TR ? at(A.hc, k) : T(0);
         z = at(A.z, k);
     } else {
@@ -297,11 +299,12 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
                                          bool &bad_depth, bool &bad_val)
 {
-    const PC<T> cur = prep(cur_ld.h, cur_ld.qx, cur_ld.qy, cur_ld.c, cur_ld.z);
-    const bool currow = cur_ld.rowok; // uniform across the wavefront
+    // the row PREFETCH ahead is requested before anything waits on row r
     if (r + PREFETCH <= K.rlast)
-        load_row<XW || YW>(A, DN ? K.rbase - (r + PREFETCH) : r + PREFETCH, K.col, K.colok, DN ? T(-1) : T(1), nxt_ld.h,
-                           nxt_ld.qx, nxt_ld.qy, nxt_ld.c, nxt_ld.z, nxt_ld.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - (r + PREFETCH) : r + PREFETCH, K.col, K.colok, nxt_ld.h, nxt_ld.qx,
+                           nxt_ld.qy, nxt_ld.c, nxt_ld.z, nxt_ld.rowok);
+    const PC<T> cur = prep(cur_ld.h, cur_ld.qx, DN ? -cur_ld.qy : cur_ld.qy, cur_ld.c, cur_ld.z);
+    const bool currow = cur_ld.rowok; // uniform across the wavefront
     const PC<T> &prev = I.prev;
     const T g = K.g, lx = K.lx, ly = K.ly;
 
@@ -530,8 +533,7 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     Ld<T> l0, l1, l2, l3;
     {
         Ld<T> p;
-        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 2) : K.j0 - 2, K.col, K.colok, DN ? T(-1) : T(1), p.h, p.qx, p.qy, p.c, p.z, p.rowok);
-        c0.prev = prep(p.h, p.qx, p.qy, p.c, p.z);
+        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 2) : K.j0 - 2, K.col, K.colok, p.h, p.qx, p.qy, p.c, p.z, p.rowok);
         c0.prevrow = p.rowok;
         c0.ax_m = c0.ax_x = c0.ax_y = c0.ax_c = T(0);
         c0.yb_m = c0.yb_n = c0.yb_t = c0.yb_c = T(0);
@@ -540,14 +542,15 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
         c0.np_b = T(0);
         c0.nprow = false;
         c0.sx_prev = c0.sybot_prev = T(0);
-        c0.prev2 = c0.prev;
         c0.prev2row = false;
         c0.np2_h = T(1);
         c0.np2_s = T(1);
         c0.np2_b = T(0);
         c0.np2row = false;
-        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 1) : K.j0 - 1, K.col, K.colok, DN ? T(-1) : T(1), l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
-        load_row<XW || YW>(A, DN ? K.rbase - K.j0 : K.j0, K.col, K.colok, DN ? T(-1) : T(1), l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 1) : K.j0 - 1, K.col, K.colok, l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
+        load_row<XW || YW>(A, DN ? K.rbase - K.j0 : K.j0, K.col, K.colok, l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
+        c0.prev = prep(p.h, p.qx, DN ? -p.qy : p.qy, p.c, p.z);
+        c0.prev2 = c0.prev;
     }
     // Four rows per trip: the carried registers alternate between c0 and c1
     // and the four row buffers rotate (row r in one, row r+2 requested into

@@ -133,9 +133,18 @@ def cpu_baseline(w, prec, budget_s):
     steps = max(2, min(w.nsteps, int(budget_s / per_step)))
     tn = timed(steps)
     rate = w.ncells * (steps - 1) / max(tn - t1, 1e-9)
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": rate, "unit": "cell-updates/s", "cores": nthreads, "kind": "oracle",
             "sample": f"steps 2..{steps} of the same workload ({w.ncells} cells), fp64 oracle, "
-                      f"{tn:.1f} s for {steps} steps minus {t1:.1f} s for the first"}
+                      f"{tn:.1f} s for {steps} steps minus {t1:.1f} s for the first; "
+                      f"{nthreads} OpenMP threads of {os.cpu_count()} logical CPUs ({model})"}
 
 
 def main():
@@ -152,7 +161,8 @@ def main():
                     help="with the Harten-Hyman entropy fix (one layer, IR-Roe)")
     ap.add_argument("--scheme", choices=["ir", "classical"], default="ir",
                     help="numerical flux: IR-Roe (default) or the classical Roe flux")
-    ap.add_argument("--repeats", type=int, default=3)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed batches of --steps steps each, every one from W^0; the median is reported")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", type=float, default=0.0, metavar="GIB",
@@ -214,7 +224,7 @@ def main():
     swe.swe_set_state(ctx, w.z, w.state)
     if args.warmup:
         swe.swe_step(ctx, args.warmup, w.cfl)
-    best = None
+    times = []
     for _ in range(max(1, args.repeats)):
         swe.swe_set_state(ctx, w.z, w.state)   # every timed call starts from W^0
         torch.cuda.synchronize()
@@ -226,13 +236,14 @@ def main():
         ev1.synchronize()
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1)
-        if best is None or ms < best:
-            best = ms
+        times.append(ms)
     swe.swe_destroy(ctx)
 
     N = w.ncells
-    value = N * K / (best / 1e3)
-    ms_step = best / K
+    times.sort()
+    med = times[len(times) // 2]  # median batch
+    value = N * K / (med / 1e3)
+    ms_step = med / K
     E = None
     if w.kind == "tri":
         # edges of a triangle mesh: (3 N + boundary) / 2, counted from the mesh

@@ -126,7 +126,12 @@ typedef struct swe_mesh_desc {
  * Errors: SWE_E_INVAL for a NULL pointer, a wrong abi_version, nlayers not 1
  * or 2, a pollutant with two layers, two layers on a Cartesian grid,
  * nx or ny < 2, dx, dy or g <= 0, r outside (0, 1), a node id out of range,
- * a triangle with area <= 0, an edge shared by more than two triangles;
+ * a triangle with area <= 0, an edge shared by more than two triangles,
+ * path, scheme or entropy_fix outside their enums, SWE_PATH_FUSED where no
+ * fused path exists, SWE_PATH_RECOMPUTE with the classical scheme, the
+ * entropy fix with two layers, the classical scheme or SWE_PATH_RECOMPUTE,
+ * a grid too large for 32-bit byte offsets of a field (fused Cartesian
+ * path), a triangle mesh whose blocks cannot be formed (fused path);
  * SWE_E_NOMEM / SWE_E_HIP on allocation or runtime failure.  On error *out
  * is set to NULL and nothing leaks. */
 int swe_create_mesh(const swe_mesh_desc *desc, swe_ctx **out);

@@ -34,11 +34,14 @@ class OracleError(RuntimeError):
 
 
 def lib():
+    """The compiled oracle.  SWE_ORACLE_LIB names another build of it (the
+    planted-mistake check of the tests loads deliberately broken copies)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("SWE_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         L.or_roe1_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
         L.or_roe1c_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
         L.or_roe1_edge_fix.argtypes = [_D, _D, ctypes.c_double, ctypes.c_int, _D, _D]

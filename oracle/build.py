@@ -15,16 +15,17 @@ SRC = os.path.join(HERE, "swe_oracle.c")
 LIB = os.path.join(HERE, "libswe_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    """Compile src (default: the oracle) into the shared library lib."""
+    tmp = lib + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off",
            "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-Wall",
-           "-o", tmp, SRC, "-lm"]
+           "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

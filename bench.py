@@ -29,13 +29,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 WORKLOADS = {
-    1: "one-layer SWE + pollutant, 64x64 structured, 1 m cells, flat bed, dam break, walls, fp64",
-    2: "one-layer SWE + pollutant, 1024x1024 structured, 1 m cells, 16-Gaussian bed, Gaussian hump, walls",
-    3: "one-layer SWE + pollutant, 4096x4096 structured, 10 m cells, 64-Gaussian bed, smooth flow, "
-       "periodic x / walls y, fp32",
-    4: "one-layer SWE, 2M-triangle jittered Morton-ordered mesh, circular dam break, walls, fp64",
-    5: "two-layer SWE (IR-Roe 4x4), 1M-triangle jittered mesh, internal dam break, walls, fp64",
+    "dam-break-64": "one-layer SWE + pollutant, 64x64 structured, 1 m cells, flat bed, dam break, walls, fp64",
+    "hump-1024": "one-layer SWE + pollutant, 1024x1024 structured, 1 m cells, 16-Gaussian bed, Gaussian hump, walls",
+    "flow-4096": "one-layer SWE + pollutant, 4096x4096 structured, 10 m cells, 64-Gaussian bed, smooth flow, "
+                 "periodic x / walls y, fp32",
+    "tri-2M": "one-layer SWE, 2M-triangle jittered Morton-ordered mesh, circular dam break, walls, fp64",
+    "two-layer-1M": "two-layer SWE (IR-Roe 4x4), 1M-triangle jittered mesh, internal dam break, walls, fp64",
 }
+# the precision each workload runs in unless --precision says otherwise
+PRECISION = {"dam-break-64": "f64", "hump-1024": "f64", "flow-4096": "f32", "tri-2M": "f64", "two-layer-1M": "f64"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -58,7 +60,7 @@ def kernel_source_hash(path):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload_id, src_hash):
+def measured_traffic(kernel, workload, prec, src_hash):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; else None."""
     path = os.path.join(PROFILE_DIR, "traffic.json")
@@ -68,7 +70,7 @@ def measured_traffic(kernel, workload_id, src_hash):
         data = json.load(open(path))
     except Exception:
         return None
-    rec = data.get(f"{kernel}@config{workload_id}")
+    rec = data.get(f"{kernel}@{workload}-{prec}")
     if not rec or rec.get("src_hash") != src_hash:
         return None
     return rec.get("bytes_per_launch")
@@ -103,7 +105,8 @@ def ingest_pmc(args):
     wr = w_k * 1024.0 * w_scale
     path = os.path.join(PROFILE_DIR, "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
-    key = f"{args.ingest_name}@config{args.config}"
+    prec = args.precision or PRECISION[args.workload]
+    key = f"{args.ingest_name}@{args.workload}-{prec}"
     data[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                  "fetch_scale": f_scale, "write_scale": w_scale,
                  "dispatches": [n_f, n_w], "src_hash": kernel_source_hash(ROOT)}
@@ -152,7 +155,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="flow-4096", choices=list(WORKLOADS))
     ap.add_argument("--precision", choices=["f32", "f64"], default=None)
     ap.add_argument("--path", choices=["auto", "edge", "recompute"], default="auto",
                     help="kernel path: the fused kernels (auto), the explicit-edge path, or the fused "
@@ -208,7 +211,7 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "ms": ms,
                           "GBps_read_plus_write": 8 * n / (ms / 1e3) / 1e9}), flush=True)
         return
-    w = inputs.make_config(args.config)
+    w = inputs.make_workload(args.workload)
     w.scheme = args.scheme
     w.entropy_fix = int(args.entropy_fix)
     prec = args.precision or w.precision
@@ -266,7 +269,7 @@ def main():
     # counters are recorded per kernel instance: the classical-flux kernel is
     # another instance (its own name in the traffic table)
     variant = ("-classical" if args.scheme == "classical" else "") + ("-hh" if args.entropy_fix else "")
-    traffic = measured_traffic(kernel + variant, args.config, src_hash)
+    traffic = measured_traffic(kernel + variant, args.workload, prec, src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": kernel, "alg_bytes_per_cell": bpc, "src_hash": src_hash}
@@ -283,7 +286,7 @@ def main():
         "vs_baseline": None,
         "dtype": prec,
         "data": "synthetic",
-        "config": {"workload": f"config {args.config}: {WORKLOADS[args.config]}"
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}"
                                + (" (classical Roe flux)" if args.scheme == "classical" else "")
                                + (" (Harten-Hyman entropy fix)" if args.entropy_fix else ""), "cells": N,
                    "scheme": args.scheme, "entropy_fix": bool(args.entropy_fix),

@@ -5,15 +5,16 @@ from seeded random draws.  It holds none of the numerical method (no fluxes,
 no geometry of edges, no time step), so both the CPU oracle and the GPU
 library can consume what it produces without sharing any arithmetic.
 """
-from .configs import (  # noqa: F401
+from .workloads import (  # noqa: F401
     G,
     Workload,
-    config1,
-    config2,
-    config3,
-    config4,
-    config5,
-    make_config,
+    dam_break,
+    gaussian_hump,
+    smooth_flow,
+    circular_dam_break,
+    two_layer_dam_break,
+    WORKLOADS,
+    make_workload,
     lattice_triangles,
     round_to_f32,
 )

@@ -15,8 +15,9 @@ Conventions (shared by every consumer, stated once here):
   ``[h1, q1x, q1y, h2, q2x, q2y]`` with layer 1 on top.
 * ``z`` is the bed elevation; the depth function of the two-layer model
   is ``H = -z`` (only differences of ``H`` enter the scheme).
-* Random draws come from ``numpy.random.default_rng(1000 + config_id)`` in
-  the fixed order written in each generator.
+* Random draws come from ``numpy.random.default_rng(seed)`` with a fixed
+  seed per workload (1001 ... 1005, the default of each generator's ``seed``)
+  in the fixed order written in each generator.
 """
 from __future__ import annotations
 
@@ -178,7 +179,7 @@ def triangle_centroids(node_xy, tri):
 # the five workloads
 # ----------------------------------------------------------------------------
 
-def config1(nx=64, ny=64, nsteps=100):
+def dam_break(nx=64, ny=64, nsteps=100):
     """Dam break with pollutant on a flat bed, 1 m square cells, walls.
 
     Depth 2 and concentration 1 for cell centres x < nx/2, else depth 1 and
@@ -199,7 +200,7 @@ def config1(nx=64, ny=64, nsteps=100):
         dx=1.0, dy=1.0, bc_x="wall", bc_y="wall")
 
 
-def config2(n=1024, nsteps=1000, precision="f64", seed=1002, hump=True,
+def gaussian_hump(n=1024, nsteps=1000, precision="f64", seed=1002, hump=True,
             blob=True):
     """Gaussian hump over a 16-Gaussian bed (lake at rest at 5 m).
 
@@ -242,7 +243,7 @@ def _stream_modes(rng):
     return a, ph
 
 
-def config3(nx=4096, ny=4096, nsteps=500, precision="f32", seed=1003,
+def smooth_flow(nx=4096, ny=4096, nsteps=500, precision="f32", seed=1003,
             flat=False, still=False):
     """Smooth random flow over a 64-Gaussian bed on 20 m depth.
 
@@ -303,7 +304,7 @@ def config3(nx=4096, ny=4096, nsteps=500, precision="f32", seed=1003,
         nx=nx, ny=ny, dx=dx, dy=dx, bc_x="periodic", bc_y="wall")
 
 
-def config4(nq=1000, nsteps=200, seed=1004, still=False):
+def circular_dam_break(nq=1000, nsteps=200, seed=1004, still=False):
     """Circular dam break on a jittered, Morton-ordered triangle mesh.
 
     The domain is 1000 m square, nq x nq quads (1 m at nq = 1000), each split
@@ -335,11 +336,11 @@ def config4(nq=1000, nsteps=200, seed=1004, still=False):
         node_xy=node_xy, tri=tri)
 
 
-def config5(nq=707, nsteps=200, seed=1005, step=True):
+def two_layer_dam_break(nq=707, nsteps=200, seed=1005, step=True):
     """Two-layer internal dam break on a jittered triangle mesh.
 
     The domain is 707 m square, nq x nq quads (1 m at nq = 707).  Draw
-    order: node jitter, the 16-Gaussian bed (as in config 4), then the
+    order: node jitter, the 16-Gaussian bed (as for the circular dam break), then the
     half-plane angle U[0, 2pi) and a point uniform in the central half of
     the domain.  At rest h1 = 2.5 and h2 = 2.5 - z; inside the half-plane
     the interface is raised by 0.5 m (h2 + 0.5, h1 - 0.5).  Density ratio
@@ -371,5 +372,15 @@ def config5(nq=707, nsteps=200, seed=1005, step=True):
         node_xy=node_xy, tri=tri)
 
 
-def make_config(k: int, **kw) -> Workload:
-    return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[k](**kw)
+# the workloads by name (each at its full size by default)
+WORKLOADS = {
+    "dam-break-64": dam_break,
+    "hump-1024": gaussian_hump,
+    "flow-4096": smooth_flow,
+    "tri-2M": circular_dam_break,
+    "two-layer-1M": two_layer_dam_break,
+}
+
+
+def make_workload(name: str, **kw) -> Workload:
+    return WORKLOADS[name](**kw)

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -184,3 +185,14 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "swe_oracle" not in text, f
+
+
+def test_bench_names_every_workload_with_its_precision():
+    import inputs
+    sys.path.insert(0, os.path.join(os.path.dirname(__file__), ".."))
+    import bench
+    assert list(bench.WORKLOADS) == list(inputs.WORKLOADS) == list(bench.PRECISION)
+    small = {"dam-break-64": dict(nx=8, ny=8), "hump-1024": dict(n=16), "flow-4096": dict(nx=16, ny=16),
+             "tri-2M": dict(nq=4), "two-layer-1M": dict(nq=4)}
+    for name, kw in small.items():
+        assert inputs.make_workload(name, **kw).precision == bench.PRECISION[name], name

@@ -18,12 +18,12 @@ from helpers import (FP32_TOL, FP64_TOL, field_errors, fsum, gpu_run,
 pytestmark = pytest.mark.gpu
 
 FULL = {
-    "c1-64x64-f64": (lambda: inputs.config1(), "f64", 100),
-    "c2-1024-f64": (lambda: inputs.config2(), "f64", 1000),
-    "c2-1024-f32": (lambda: inputs.config2(), "f32", 100),
-    "c3-4096-f32": (lambda: inputs.config3(), "f32", 100),
-    "c4-2M-tri-f64": (lambda: inputs.config4(), "f64", 200),
-    "c5-1M-two-layer-f64": (lambda: inputs.config5(), "f64", 4),
+    "dam-break-64x64-f64": (lambda: inputs.dam_break(), "f64", 100),
+    "hump-1024-f64": (lambda: inputs.gaussian_hump(), "f64", 1000),
+    "hump-1024-f32": (lambda: inputs.gaussian_hump(), "f32", 100),
+    "flow-4096-f32": (lambda: inputs.smooth_flow(), "f32", 100),
+    "tri-2M-f64": (lambda: inputs.circular_dam_break(), "f64", 200),
+    "two-layer-1M-f64": (lambda: inputs.two_layer_dam_break(), "f64", 4),
 }
 
 
@@ -43,10 +43,10 @@ def test_fullsize_parity(name):
 
 
 LONG = {
-    "c2-1024-f32-1000": (lambda: inputs.config2(), "f32", 1000),
-    "c3-4096-f32-500": (lambda: inputs.config3(), "f32", 500),
-    "c3-4096-f64-500": (lambda: inputs.config3(), "f64", 500),
-    "c5-1M-two-layer-200": (lambda: inputs.config5(), "f64", 200),
+    "hump-1024-f32-1000": (lambda: inputs.gaussian_hump(), "f32", 1000),
+    "flow-4096-f32-500": (lambda: inputs.smooth_flow(), "f32", 500),
+    "flow-4096-f64-500": (lambda: inputs.smooth_flow(), "f64", 500),
+    "two-layer-1M-200": (lambda: inputs.two_layer_dam_break(), "f64", 200),
 }
 
 

@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 PATHS = {"auto": 0, "edge": 1}
 
 def _shuffled_tri(nq, seed=77):
-    """config 4 with its cells listed in a random order (not Morton)."""
-    w = inputs.config4(nq=nq)
+    """the circular dam break with its cells listed in a random order (not Morton)."""
+    w = inputs.circular_dam_break(nq=nq)
     order = np.random.default_rng(seed).permutation(w.ncells)
     w.tri = np.ascontiguousarray(w.tri[order])
     w.z = w.z[order]
@@ -30,7 +30,7 @@ def _shuffled_tri(nq, seed=77):
 
 def _periodic_xy(nx, ny):
     """the 4096^2-style flow on a small grid, periodic in both directions"""
-    w = inputs.config3(nx=nx, ny=ny)
+    w = inputs.smooth_flow(nx=nx, ny=ny)
     w.bc_y = "periodic"
     w.precision = "f64"
     return w
@@ -38,32 +38,32 @@ def _periodic_xy(nx, ny):
 
 CASES = {
     # name: (workload factory, steps, precision)
-    "c1-dam-break-64x64": (lambda: inputs.config1(), 100, "f64"),
-    "c2-hump-96-f64": (lambda: inputs.config2(n=96), 300, "f64"),
-    "c2-hump-96-f32": (lambda: inputs.config2(n=96), 100, "f32"),
-    "c3-flow-160x96-f32": (lambda: inputs.config3(nx=160, ny=96), 100, "f32"),
-    "c3-flow-160x96-f64": (lambda: inputs.config3(nx=160, ny=96), 150, "f64"),
-    "c3-ragged-67x33-f64": (lambda: inputs.config3(nx=67, ny=33), 80, "f64"),
-    "c1-ragged-131x5": (lambda: inputs.config1(nx=131, ny=5), 60, "f64"),
-    "c4-tri-36": (lambda: inputs.config4(nq=36), 120, "f64"),
-    "c4-tri-ragged-19": (lambda: inputs.config4(nq=19), 25, "f64"),
-    "c5-two-layer-30": (lambda: inputs.config5(nq=30), 200, "f64"),
-    "c5-two-layer-13": (lambda: inputs.config5(nq=13), 100, "f64"),
-    "c4-tri-shuffled-30": (lambda: _shuffled_tri(30), 60, "f64"),
-    "c4-tri-40-f32": (lambda: inputs.config4(nq=40), 100, "f32"),
-    "c3-periodic-xy-67x40-f64": (lambda: _periodic_xy(67, 40), 60, "f64"),
+    "dam-break-64x64": (lambda: inputs.dam_break(), 100, "f64"),
+    "hump-96-f64": (lambda: inputs.gaussian_hump(n=96), 300, "f64"),
+    "hump-96-f32": (lambda: inputs.gaussian_hump(n=96), 100, "f32"),
+    "flow-160x96-f32": (lambda: inputs.smooth_flow(nx=160, ny=96), 100, "f32"),
+    "flow-160x96-f64": (lambda: inputs.smooth_flow(nx=160, ny=96), 150, "f64"),
+    "flow-ragged-67x33-f64": (lambda: inputs.smooth_flow(nx=67, ny=33), 80, "f64"),
+    "dam-break-ragged-131x5": (lambda: inputs.dam_break(nx=131, ny=5), 60, "f64"),
+    "tri-36": (lambda: inputs.circular_dam_break(nq=36), 120, "f64"),
+    "tri-ragged-19": (lambda: inputs.circular_dam_break(nq=19), 25, "f64"),
+    "two-layer-30": (lambda: inputs.two_layer_dam_break(nq=30), 200, "f64"),
+    "two-layer-13": (lambda: inputs.two_layer_dam_break(nq=13), 100, "f64"),
+    "tri-shuffled-30": (lambda: _shuffled_tri(30), 60, "f64"),
+    "tri-40-f32": (lambda: inputs.circular_dam_break(nq=40), 100, "f32"),
+    "flow-periodic-xy-67x40-f64": (lambda: _periodic_xy(67, 40), 60, "f64"),
 }
 
 
 # Cartesian tilings the size heuristic picks only on large grids, forced on
 # small ones: (rows per tile, alternate march direction)
 TILINGS = {
-    "c1-dam-break-64x64": [(8, 1), (12, 1)],
-    "c2-hump-96-f64": [(8, 1), (5, 1)],
-    "c3-flow-160x96-f32": [(12, 1), (8, 0)],
-    "c3-ragged-67x33-f64": [(4, 1), (12, 1)],
-    "c1-ragged-131x5": [(4, 1)],
-    "c3-periodic-xy-67x40-f64": [(4, 1), (8, 1), (12, 1)],
+    "dam-break-64x64": [(8, 1), (12, 1)],
+    "hump-96-f64": [(8, 1), (5, 1)],
+    "flow-160x96-f32": [(12, 1), (8, 0)],
+    "flow-ragged-67x33-f64": [(4, 1), (12, 1)],
+    "dam-break-ragged-131x5": [(4, 1)],
+    "flow-periodic-xy-67x40-f64": [(4, 1), (8, 1), (12, 1)],
 }
 
 
@@ -94,7 +94,7 @@ TRI_KERNELS = {"per-block-288": {"SWE_TRI_PIPE": "0", "SWE_TRI_B": "288"},
 
 
 @pytest.mark.parametrize("kernel", list(TRI_KERNELS))
-@pytest.mark.parametrize("name", ["c4-tri-36", "c4-tri-ragged-19", "c4-tri-shuffled-30", "c4-tri-40-f32"])
+@pytest.mark.parametrize("name", ["tri-36", "tri-ragged-19", "tri-shuffled-30", "tri-40-f32"])
 def test_parity_tri_kernels(name, kernel, monkeypatch):
     for k, v in TRI_KERNELS[kernel].items():
         monkeypatch.setenv(k, v)
@@ -131,7 +131,7 @@ def test_parity(name, path):
 def _tri_pollutant(nq, seed=91):
     """the triangle dam break with a pollutant: concentration a seeded
     smooth field in [0.2, 1] (no triangle workload carries one)"""
-    w = inputs.config4(nq=nq)
+    w = inputs.circular_dam_break(nq=nq)
     rng = np.random.default_rng(seed)
     xy = w.node_xy[w.tri].mean(axis=1)
     kx, ky, ph = rng.uniform(1.0, 4.0), rng.uniform(1.0, 4.0), rng.uniform(0, 2 * np.pi)
@@ -144,8 +144,8 @@ def _tri_pollutant(nq, seed=91):
 # The classical Roe flux (contact waves of the Roe velocity for the
 # transverse momentum and the pollutant) on every case, both paths.
 CLASSICAL = dict(CASES)
-CLASSICAL["c4-tri-pollutant-23"] = (lambda: _tri_pollutant(23), 80, "f64")
-CLASSICAL["c4-tri-pollutant-33-f32"] = (lambda: _tri_pollutant(33), 80, "f32")
+CLASSICAL["tri-pollutant-23"] = (lambda: _tri_pollutant(23), 80, "f64")
+CLASSICAL["tri-pollutant-33-f32"] = (lambda: _tri_pollutant(33), 80, "f32")
 
 
 def _classical(make):
@@ -172,7 +172,7 @@ def test_parity_classical(name, path):
 
 
 @pytest.mark.parametrize("kernel", list(TRI_KERNELS))
-@pytest.mark.parametrize("name", ["c4-tri-pollutant-23", "c4-tri-40-f32", "c5-two-layer-13"])
+@pytest.mark.parametrize("name", ["tri-pollutant-23", "tri-40-f32", "two-layer-13"])
 def test_parity_classical_tri_kernels(name, kernel, monkeypatch):
     for k, v in TRI_KERNELS[kernel].items():
         monkeypatch.setenv(k, v)
@@ -201,7 +201,7 @@ def test_parity_ir_pollutant_triangles():
 def test_classical_and_ir_differ_on_gpu():
     # the two schemes share mass and normal momentum fluxes but not the
     # pollutant's: after a few steps of a sheared flow they must differ
-    w = inputs.config3(nx=64, ny=40)
+    w = inputs.smooth_flow(nx=64, ny=40)
     w.precision = "f64"
     ir, _, _ = gpu_run(w, nsteps=20)
     cl, _, _ = gpu_run(_classical(lambda: w.copy()), nsteps=20)
@@ -254,7 +254,7 @@ def test_recompute_in_every_tiling(tiling, monkeypatch):
 # straddles the dam, so the fix acts every step) on a Cartesian strip and a
 # triangle mesh, and ordinary workloads with the fix switched on.
 def _transonic_cart(nx, ny):
-    w = inputs.config1(nx=nx, ny=ny)
+    w = inputs.dam_break(nx=nx, ny=ny)
     x = (np.arange(nx) + 0.5) * w.dx
     left = np.tile(x < nx * w.dx / 2, ny)
     h = np.where(left, 1.0, 0.05)
@@ -264,7 +264,7 @@ def _transonic_cart(nx, ny):
 
 
 def _transonic_tri(nq):
-    w = inputs.config4(nq=nq)
+    w = inputs.circular_dam_break(nq=nq)
     w.z = np.zeros_like(w.z)
     w.state[0] = np.where(w.state[0] > 2.0, 3.0, 0.12)
     w.entropy_fix = 1
@@ -284,8 +284,8 @@ HH = {
     "hh-dam-break-131x5-f32": (lambda: _transonic_cart(131, 5), 100, "f32"),
     "hh-tri-circular-24-f64": (lambda: _transonic_tri(24), 80, "f64"),
     "hh-tri-circular-30-f32": (lambda: _transonic_tri(30), 60, "f32"),
-    "hh-c3-flow-160x96-f32": (_with_fix(CASES["c3-flow-160x96-f32"][0]), 100, "f32"),
-    "hh-c4-tri-ragged-19": (_with_fix(CASES["c4-tri-ragged-19"][0]), 25, "f64"),
+    "hh-flow-160x96-f32": (_with_fix(CASES["flow-160x96-f32"][0]), 100, "f32"),
+    "hh-tri-ragged-19": (_with_fix(CASES["tri-ragged-19"][0]), 25, "f64"),
 }
 
 
@@ -333,9 +333,9 @@ def test_entropy_fix_acts_on_gpu():
         assert np.abs(fixed[0] - plain[0]).max() > 1e-3
 
 
-def test_config1_symmetry_on_gpu():
-    w = inputs.config1()
-    say("[sym] config1 rows identical, qy == 0")
+def test_dam_break_symmetry_on_gpu():
+    w = inputs.dam_break()
+    say("[sym] dam_break rows identical, qy == 0")
     got, _, _ = gpu_run(w)
     assert np.abs(got[2]).max() <= 1e-14
     for a in got:
@@ -344,13 +344,13 @@ def test_config1_symmetry_on_gpu():
 
 
 def test_conservation_on_gpu():
-    say("[cons] config2 96^2 and config5 30 conservation")
-    w = inputs.config2(n=96)
+    say("[cons] gaussian_hump 96^2 and two_layer_dam_break 30 conservation")
+    w = inputs.gaussian_hump(n=96)
     got, _, _ = gpu_run(w, nsteps=500)
     area = w.dx * w.dy
     for v in (0, 3):
         assert abs(fsum(got[v]) - fsum(w.state[v])) * area <= 1e-12 * fsum(w.state[v]) * area
-    w = inputs.config5(nq=30)
+    w = inputs.two_layer_dam_break(nq=30)
     got, _, _ = gpu_run(w, nsteps=200)
     ar = tri_areas(w)
     for v in (0, 3):
@@ -360,7 +360,7 @@ def test_conservation_on_gpu():
 
 def test_lake_at_rest_on_gpu():
     say("[rest] lake at rest, Cartesian fp64 and fp32, triangles")
-    w = inputs.config2(n=96, hump=False, blob=False)
+    w = inputs.gaussian_hump(n=96, hump=False, blob=False)
     got, _, _ = gpu_run(w, nsteps=500)
     assert np.abs(got[1] / got[0]).max() <= 1e-12
     assert np.abs(got[0] + w.z - 5.0).max() <= 1e-12
@@ -368,7 +368,7 @@ def test_lake_at_rest_on_gpu():
     z32 = w.z.astype(np.float32).astype(np.float64)
     assert np.abs(got[1] / got[0]).max() <= 1e-5
     assert np.abs(got[0] + z32 - 5.0).max() <= 1e-5
-    w = inputs.config4(nq=24, still=True)
+    w = inputs.circular_dam_break(nq=24, still=True)
     got, _, _ = gpu_run(w, nsteps=200)
     assert np.abs(got[1] / got[0]).max() <= 1e-12
     assert np.abs(got[0] + w.z - 5.0).max() <= 1e-12
@@ -376,7 +376,7 @@ def test_lake_at_rest_on_gpu():
 
 def test_determinism_and_resume():
     import finite_volume_shallow_amd as swe
-    w = inputs.config4(nq=30)
+    w = inputs.circular_dam_break(nq=30)
     say("[det] two runs bitwise equal; 2n steps == n + get/set + n")
     a, da, _ = gpu_run(w, nsteps=40)
     b, db, _ = gpu_run(w, nsteps=40)
@@ -402,7 +402,7 @@ def test_device_state_roundtrip_and_stream():
     import torch
     import finite_volume_shallow_amd as swe
     say("[dev] device set/get on a torch stream")
-    w = inputs.config3(nx=64, ny=40)
+    w = inputs.smooth_flow(nx=64, ny=40)
     s = torch.cuda.Stream()
     desc, keep = swe.desc_from_workload(w, stream=s, precision="f32")
     ctx = swe.swe_create_mesh(desc)
@@ -453,20 +453,20 @@ def test_device_state_roundtrip_triangles():
 def test_error_paths():
     import finite_volume_shallow_amd as swe
     say("[err] depth, non-hyperbolic, bad arguments, zero steps")
-    w = inputs.config1(nx=16, ny=8)
+    w = inputs.dam_break(nx=16, ny=8)
     w.state[0][17] = -0.5
     with pytest.raises(swe.SweError) as e:
         gpu_run(w, nsteps=2)
     assert e.value.status == swe.SWE_E_DEPTH
 
-    w = inputs.config5(nq=6)
+    w = inputs.two_layer_dam_break(nq=6)
     for v in (1, 4):
         w.state[v] = (1.5 if v == 1 else -1.5) * w.state[v - 1]
     with pytest.raises(swe.SweError) as e:
         gpu_run(w, nsteps=1)
     assert e.value.status == swe.SWE_E_NONHYPERBOLIC
 
-    w = inputs.config1(nx=8, ny=8)
+    w = inputs.dam_break(nx=8, ny=8)
     desc, keep = swe.desc_from_workload(w)
     ctx = swe.swe_create_mesh(desc)
     try:
@@ -490,10 +490,10 @@ def test_error_paths():
 def test_degenerate_meshes(case):
     say(f"[degenerate] {case}")
     if case == "2x2-walls":
-        w = inputs.config1(nx=2, ny=2)
+        w = inputs.dam_break(nx=2, ny=2)
         w.state[0] = np.array([2.0, 1.0, 1.5, 1.2])
     elif case == "2x3-periodic":
-        w = inputs.config3(nx=2, ny=3)
+        w = inputs.smooth_flow(nx=2, ny=3)
         w.bc_y = "periodic"
         w.precision = "f64"
     else:

@@ -34,7 +34,7 @@ def _tri_areas(w):
 # ---------------------------------------------------------------- well-balance
 
 def test_lake_at_rest_cartesian():
-    w = inputs.config2(n=96, nsteps=1000, hump=False, blob=False)
+    w = inputs.gaussian_hump(n=96, nsteps=1000, hump=False, blob=False)
     st, dts, _ = oracle.run(w)
     h, qx, qy = st[0], st[1], st[2]
     assert np.abs(qx / h).max() <= 1e-12
@@ -43,7 +43,7 @@ def test_lake_at_rest_cartesian():
 
 
 def test_lake_at_rest_triangles():
-    w = inputs.config4(nq=24, nsteps=200, still=True)
+    w = inputs.circular_dam_break(nq=24, nsteps=200, still=True)
     st, _, _ = oracle.run(w)
     h, qx, qy = st
     assert np.abs(qx / h).max() <= 1e-12
@@ -52,7 +52,7 @@ def test_lake_at_rest_triangles():
 
 
 def test_lake_at_rest_two_layers():
-    w = inputs.config5(nq=20, nsteps=200, step=False)
+    w = inputs.two_layer_dam_break(nq=20, nsteps=200, step=False)
     st, _, _ = oracle.run(w)
     h1, q1x, q1y, h2, q2x, q2y = st
     for q, h in ((q1x, h1), (q1y, h1), (q2x, h2), (q2y, h2)):
@@ -63,18 +63,18 @@ def test_lake_at_rest_two_layers():
 
 # ---------------------------------------------------------------- conservation
 
-@pytest.mark.parametrize("case", ["c1", "c3", "c4", "c4tracer"])
+@pytest.mark.parametrize("case", ["dam-break", "flow", "tri", "tri-pollutant"])
 def test_mass_conservation_one_layer(case):
-    if case == "c1":
-        w = inputs.config1()
+    if case == "dam-break":
+        w = inputs.dam_break()
         area = np.full(w.ncells, w.dx * w.dy)
-    elif case == "c3":
-        w = inputs.config3(nx=64, ny=48, nsteps=100)
+    elif case == "flow":
+        w = inputs.smooth_flow(nx=64, ny=48, nsteps=100)
         area = np.full(w.ncells, w.dx * w.dy)
     else:
-        w = inputs.config4(nq=30, nsteps=60)
+        w = inputs.circular_dam_break(nq=30, nsteps=60)
         area = _tri_areas(w)
-        if case == "c4tracer":
+        if case == "tri-pollutant":
             rng = np.random.default_rng(2)
             w.ntracers = 1
             w.state.append(w.state[0] * rng.uniform(0, 1, w.ncells))
@@ -86,7 +86,7 @@ def test_mass_conservation_one_layer(case):
 
 
 def test_mass_conservation_two_layers():
-    w = inputs.config5(nq=20, nsteps=150)
+    w = inputs.two_layer_dam_break(nq=20, nsteps=150)
     area = _tri_areas(w)
     m0 = [_fsum(w.state[v] * area) for v in (0, 3)]
     st, _, _ = oracle.run(w)
@@ -97,7 +97,7 @@ def test_mass_conservation_two_layers():
 
 def test_x_momentum_conserved_in_flat_periodic_channel():
     # walls at y = 0, Ly exert no x-force, the bed is flat, x is periodic
-    w = inputs.config3(nx=64, ny=32, nsteps=100, flat=True)
+    w = inputs.smooth_flow(nx=64, ny=32, nsteps=100, flat=True)
     scale = _fsum(np.abs(w.state[1]))
     p0 = _fsum(w.state[1])
     st, _, _ = oracle.run(w)
@@ -141,7 +141,7 @@ def test_stoker_constants():
 
 def _dam_break_error(nx):
     L = 64.0
-    w = inputs.config1(nx=nx, ny=4)
+    w = inputs.dam_break(nx=nx, ny=4)
     w.dx = w.dy = L / nx
     st, dts, _ = oracle.run(w, nsteps=10 * nx)
     t = np.cumsum(dts)
@@ -169,8 +169,8 @@ def test_dam_break_matches_stoker():
 
 # ---------------------------------------------------------------- symmetries
 
-def test_config1_rows_identical_and_no_transverse_flow():
-    w = inputs.config1()
+def test_dam_break_rows_identical_and_no_transverse_flow():
+    w = inputs.dam_break()
     st, _, _ = oracle.run(w)
     for a in st:
         g2 = a.reshape(64, 64)
@@ -179,7 +179,7 @@ def test_config1_rows_identical_and_no_transverse_flow():
 
 
 def test_mirror_in_x():
-    w = inputs.config1(nx=50, ny=6)
+    w = inputs.dam_break(nx=50, ny=6)
     rng = np.random.default_rng(4)
     w.state[1] = rng.uniform(-0.3, 0.3, w.ncells) * w.state[0]
     w.state[2] = rng.uniform(-0.3, 0.3, w.ncells) * w.state[0]
@@ -202,7 +202,7 @@ def test_mirror_in_x():
 
 
 def test_transpose_xy():
-    w = inputs.config2(n=40, nsteps=50)
+    w = inputs.gaussian_hump(n=40, nsteps=50)
     rng = np.random.default_rng(8)
     w.state[1] = rng.uniform(-0.2, 0.2, w.ncells) * w.state[0]
     t = w.copy()
@@ -225,10 +225,10 @@ def test_rotation_invariance_triangles(layers):
     th = 0.3
     c, s = math.cos(th), math.sin(th)
     if layers == 1:
-        w = inputs.config4(nq=16, nsteps=60)
+        w = inputs.circular_dam_break(nq=16, nsteps=60)
         nv_pairs = [(1, 2)]
     else:
-        w = inputs.config5(nq=14, nsteps=60)
+        w = inputs.two_layer_dam_break(nq=14, nsteps=60)
         nv_pairs = [(1, 2), (4, 5)]
     rng = np.random.default_rng(9)
     for (a, b) in nv_pairs:
@@ -256,7 +256,7 @@ def test_rotation_invariance_triangles(layers):
 # ---------------------------------------------------------------- pollutant
 
 def test_constant_concentration_is_preserved_exactly():
-    w = inputs.config2(n=48, nsteps=120)
+    w = inputs.gaussian_hump(n=48, nsteps=120)
     w.state[3] = w.state[0].copy()          # c = 1 everywhere
     st, _, _ = oracle.run(w)
     assert (st[3] == st[0]).all()
@@ -264,7 +264,7 @@ def test_constant_concentration_is_preserved_exactly():
 
 def test_pollutant_bounded():
     # a first-order upwind transport keeps c inside the initial range
-    w = inputs.config1()
+    w = inputs.dam_break()
     st, _, _ = oracle.run(w)
     c = st[3] / st[0]
     assert c.min() >= -1e-14 and c.max() <= 1.0 + 1e-14
@@ -274,13 +274,13 @@ def test_pollutant_bounded():
 
 def test_first_time_step_is_eq5():
     # at rest the fastest wave is sqrt(g h) on every side of a depth-2 cell
-    w = inputs.config1()
+    w = inputs.dam_break()
     _, dts, _ = oracle.run(w, nsteps=1)
     assert dts[0] == pytest.approx(2 * 0.9 * 1.0 / (4 * math.sqrt(G * 2.0)), rel=1e-15)
 
 
 def test_thread_count_does_not_change_results():
-    w = inputs.config4(nq=20, nsteps=30)
+    w = inputs.circular_dam_break(nq=20, nsteps=30)
     a, da, _ = oracle.run(w, nthreads=1)
     b, db, _ = oracle.run(w, nthreads=4)
     assert (da == db).all()
@@ -289,7 +289,7 @@ def test_thread_count_does_not_change_results():
 
 
 def test_depth_failure_is_reported():
-    w = inputs.config1(nx=8, ny=4)
+    w = inputs.dam_break(nx=8, ny=4)
     w.state[0][5] = -1.0
     with pytest.raises(oracle.OracleError) as e:
         oracle.run(w, nsteps=1)
@@ -307,23 +307,23 @@ def _classical(w):
 
 
 def test_classical_lake_at_rest():
-    w = _classical(inputs.config2(n=64, nsteps=400, hump=False, blob=False))
+    w = _classical(inputs.gaussian_hump(n=64, nsteps=400, hump=False, blob=False))
     st, _, _ = oracle.run(w)
     assert np.abs(st[1] / st[0]).max() <= 1e-12 and np.abs(st[2] / st[0]).max() <= 1e-12
     assert np.abs(st[0] + w.z - 5.0).max() <= 1e-12
-    w = _classical(inputs.config4(nq=20, nsteps=150, still=True))
+    w = _classical(inputs.circular_dam_break(nq=20, nsteps=150, still=True))
     st, _, _ = oracle.run(w)
     assert np.abs(st[1] / st[0]).max() <= 1e-12 and np.abs(st[2] / st[0]).max() <= 1e-12
     assert np.abs(st[0] + w.z - 5.0).max() <= 1e-12
 
 
-@pytest.mark.parametrize("case", ["c3", "c4tracer"])
+@pytest.mark.parametrize("case", ["flow", "tri-pollutant"])
 def test_classical_mass_and_pollutant_conservation(case):
-    if case == "c3":
-        w = _classical(inputs.config3(nx=64, ny=48, nsteps=100))
+    if case == "flow":
+        w = _classical(inputs.smooth_flow(nx=64, ny=48, nsteps=100))
         area = np.full(w.ncells, w.dx * w.dy)
     else:
-        w = _classical(inputs.config4(nq=30, nsteps=60))
+        w = _classical(inputs.circular_dam_break(nq=30, nsteps=60))
         area = _tri_areas(w)
         rng = np.random.default_rng(2)
         w.ntracers = 1
@@ -335,7 +335,7 @@ def test_classical_mass_and_pollutant_conservation(case):
 
 
 def test_classical_x_momentum_in_flat_periodic_channel():
-    w = _classical(inputs.config3(nx=64, ny=32, nsteps=100, flat=True))
+    w = _classical(inputs.smooth_flow(nx=64, ny=32, nsteps=100, flat=True))
     scale = _fsum(np.abs(w.state[1]))
     p0 = _fsum(w.state[1])
     st, _, _ = oracle.run(w)
@@ -346,7 +346,7 @@ def test_classical_dam_break_rows_identical_and_equal_to_ir_roe():
     # no transverse flow: depth and momenta of the two schemes coincide up to
     # rounding (the 2x2 part is the same); the pollutant differs, carried by
     # the contact wave (Roe velocity) instead of by the mass flux
-    w = inputs.config1(nsteps=60)
+    w = inputs.dam_break(nsteps=60)
     a, da, _ = oracle.run(w)
     b, db, _ = oracle.run(_classical(w.copy()))
     for x in b:
@@ -362,7 +362,7 @@ def test_classical_dam_break_rows_identical_and_equal_to_ir_roe():
 def test_classical_rotation_invariance_triangles():
     th = 0.3
     c, s = math.cos(th), math.sin(th)
-    w = _classical(inputs.config4(nq=16, nsteps=60))
+    w = _classical(inputs.circular_dam_break(nq=16, nsteps=60))
     rng = np.random.default_rng(9)
     w.state[1] = rng.uniform(-0.05, 0.05, w.ncells) * w.state[0]
     w.state[2] = rng.uniform(-0.05, 0.05, w.ncells) * w.state[0]
@@ -381,7 +381,7 @@ def test_classical_rotation_invariance_triangles():
 
 
 def test_classical_constant_concentration_is_preserved_exactly():
-    w = _classical(inputs.config2(n=48, nsteps=120))
+    w = _classical(inputs.gaussian_hump(n=48, nsteps=120))
     w.state[3] = w.state[0].copy()
     st, _, _ = oracle.run(w)
     assert (st[3] == st[0]).all()
@@ -389,7 +389,7 @@ def test_classical_constant_concentration_is_preserved_exactly():
 
 def test_classical_differs_from_ir_roe_with_transverse_flow():
     # a sheared flow: the contact waves change the transverse momentum
-    w = inputs.config3(nx=48, ny=40, nsteps=40)
+    w = inputs.smooth_flow(nx=48, ny=40, nsteps=40)
     a, _, _ = oracle.run(w)
     b, _, _ = oracle.run(_classical(w.copy()))
     rel = np.abs(a[2] - b[2]).max() / np.abs(a[2]).max()
@@ -400,7 +400,7 @@ def test_classical_differs_from_ir_roe_with_transverse_flow():
 # velocity carry that layer's transverse momentum).
 
 def test_classical_two_layer_lake_at_rest():
-    w = _classical(inputs.config5(nq=20, nsteps=200, step=False))
+    w = _classical(inputs.two_layer_dam_break(nq=20, nsteps=200, step=False))
     st, _, _ = oracle.run(w)
     h1, q1x, q1y, h2, q2x, q2y = st
     for q, h in ((q1x, h1), (q1y, h1), (q2x, h2), (q2y, h2)):
@@ -410,7 +410,7 @@ def test_classical_two_layer_lake_at_rest():
 
 
 def test_classical_two_layer_mass_conservation():
-    w = _classical(inputs.config5(nq=20, nsteps=150))
+    w = _classical(inputs.two_layer_dam_break(nq=20, nsteps=150))
     area = _tri_areas(w)
     m0 = [_fsum(w.state[v] * area) for v in (0, 3)]
     st, _, _ = oracle.run(w)
@@ -421,7 +421,7 @@ def test_classical_two_layer_mass_conservation():
 def test_classical_two_layer_rotation_invariance():
     th = -0.45
     c, s = math.cos(th), math.sin(th)
-    w = _classical(inputs.config5(nq=14, nsteps=60))
+    w = _classical(inputs.two_layer_dam_break(nq=14, nsteps=60))
     rng = np.random.default_rng(19)
     for a, b in ((1, 2), (4, 5)):
         w.state[a] = rng.uniform(-0.05, 0.05, w.ncells) * w.state[a - 1]
@@ -446,7 +446,7 @@ def test_classical_two_layer_differs_from_ir_roe():
     # the interface release sets up transverse shear along the mesh's
     # oblique edges; the two schemes agree on the first dt, then their
     # transverse momenta part
-    w = inputs.config5(nq=16, nsteps=80)
+    w = inputs.two_layer_dam_break(nq=16, nsteps=80)
     a, da, _ = oracle.run(w)
     b, db, _ = oracle.run(_classical(w.copy()))
     assert da[0] == db[0]
@@ -462,7 +462,7 @@ def test_classical_two_layer_differs_from_ir_roe():
 # dam is smooth (jumps O(dx)) and converges to the exact solution.
 
 def _transonic_dam_break(nx, fix, T=4.0, hL=1.0, hR=0.05, L=100.0):
-    w = inputs.config1(nx=nx, ny=4)
+    w = inputs.dam_break(nx=nx, ny=4)
     w.dx = w.dy = L / nx
     x = (np.arange(nx) + 0.5) * w.dx
     h0 = np.where(x < L / 2, hL, hR)
@@ -504,8 +504,8 @@ def test_entropy_fix_conserves_and_keeps_lakes_at_rest():
     _, _, st, w = _transonic_dam_break(200, 1)
     for v, v0 in ((0, 0), (3, 3)):
         assert abs(_fsum(st[v]) - _fsum(w.state[v0])) <= 1e-12 * _fsum(w.state[v0])
-    for make in (lambda: inputs.config2(n=48, nsteps=200, hump=False, blob=False),
-                 lambda: inputs.config4(nq=16, nsteps=100, still=True)):
+    for make in (lambda: inputs.gaussian_hump(n=48, nsteps=200, hump=False, blob=False),
+                 lambda: inputs.circular_dam_break(nq=16, nsteps=100, still=True)):
         a = make()
         b = make()
         b.entropy_fix = 1
@@ -518,7 +518,7 @@ def test_entropy_fix_conserves_and_keeps_lakes_at_rest():
 def test_entropy_fix_on_triangles_is_rotation_invariant_and_conservative():
     th = 0.7
     c, s = math.cos(th), math.sin(th)
-    w = inputs.config4(nq=16, nsteps=40)
+    w = inputs.circular_dam_break(nq=16, nsteps=40)
     w.state[0] = np.where(w.state[0] > 2.0, 3.0, 0.12)    # a transonic circular dam break
     w.z = np.zeros_like(w.z)
     w.entropy_fix = 1

@@ -459,6 +459,16 @@ def test_error_paths():
         gpu_run(w, nsteps=2)
     assert e.value.status == swe.SWE_E_DEPTH
 
+    # a non-finite pollutant leaves depth and momentum alone (the pollutant
+    # does not feed back) but is reported, on both fused paths and the edge path
+    for make in (lambda: inputs.dam_break(nx=16, ny=8), lambda: _tri_pollutant(8)):
+        for path in (0, 1):
+            w = make()
+            w.state[3][20] = np.inf
+            with pytest.raises(swe.SweError) as e:
+                gpu_run(w, nsteps=2, path=path)
+            assert e.value.status == swe.SWE_E_NONFINITE
+
     w = inputs.two_layer_dam_break(nq=6)
     for v in (1, 4):
         w.state[v] = (1.5 if v == 1 else -1.5) * w.state[v - 1]

@@ -52,11 +52,40 @@ def alg_bytes_per_cell(w, prec, E=None):
     return (2 * nv + 2) * s + (E / w.ncells) * (8 + 3 * s)
 
 
+def _code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed
+    (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(path):
+    """Hash of the library's code (comments and layout ignored): counter
+    records taken on other code are not reused."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "finite_volume_shallow_amd", "csrc"))):
+    csrc = os.path.join(path, "finite_volume_shallow_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(ROOT, "finite_volume_shallow_amd", "csrc", f), "rb").read())
+            h.update(f.encode())
+            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -117,16 +117,13 @@ template <typename T> void upload_geometry(swe_ctx *c, const HostEdges &h)
     upload_raw(c, c->c_iarea, iar.data(), N * sizeof(T));
 }
 
-// Rows per tile of the fused Cartesian kernel: at most 32 (measured best on
-// the 4096^2 grid: taller tiles lose latency hiding, shorter ones add halo
-// rows), reduced until the grid gives at least 2048 wavefronts (two per SIMD
-// of the 1024 SIMDs), never below 8 rows.  SWE_CART_TY overrides it (tuning).
 // Rows per tile of the fused Cartesian kernel (one 64-lane wavefront per
 // tile of 60 columns) and whether odd row blocks march downward.  Large
 // grids: 12 rows, alternating (measured on 4096^2: the halo rows two
 // neighbouring tiles share are then read close together and served from
 // L2).  Smaller grids: 10 rows, halved while there are fewer than 1024
-// tiles, down to 4.
+// tiles, down to 4.  SWE_CART_TY / SWE_CART_ALT override both (tuning and
+// tests).
 void cart_tiling(int64_t nx, int64_t ny, int &ty, int &alt)
 {
     const int64_t strips = (nx + 59) / 60;

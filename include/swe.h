@@ -119,6 +119,17 @@ typedef struct swe_mesh_desc {
     void *hip_stream;
 } swe_mesh_desc;
 
+/* Environment (read at swe_create_mesh; for tuning and tests, not needed in
+ * normal use -- results do not depend on them beyond rounding):
+ *   SWE_CART_TY=n, SWE_CART_ALT=0|1  rows per tile (4..4096) and alternating
+ *                                    march of the fused Cartesian kernel;
+ *   SWE_TRI_B=n                      cells per triangle block (64..512, a
+ *                                    multiple of 32), before the size checks;
+ *   SWE_TRI_LDS=bytes                LDS cap per triangle block;
+ *   SWE_TRI_NT=256                   256-thread triangle workgroups;
+ *   SWE_TRI_PIPE=0|1                 the pipelined persistent triangle kernel
+ *                                    (one layer) on or off. */
+
 /* Create a context for a mesh and upload its geometry ([IR] Sec. 2.2: cells
  * V_i with area |V_i|, edges G_ij with length |G_ij| and unit normal eta_ij
  * pointing from V_i to V_j; [IR] Sec. 3: the mesh is built once from the

@@ -190,7 +190,7 @@ def main():
                     help="kernel path: the fused kernels (auto), the explicit-edge path, or the fused "
                          "kernel with every cell evaluating all its edges (recompute, an ablation)")
     ap.add_argument("--entropy-fix", action="store_true",
-                    help="with the Harten-Hyman entropy fix (one layer, IR-Roe)")
+                    help="with the Harten-Hyman entropy fix (one layer)")
     ap.add_argument("--scheme", choices=["ir", "classical"], default="ir",
                     help="numerical flux: IR-Roe (default) or the classical Roe flux")
     ap.add_argument("--repeats", type=int, default=5,

@@ -131,8 +131,8 @@ template <typename T> struct EF {
 // FX = FLUX_ROE: the classical Roe flux of the whole system instead, whose
 // transverse momentum and pollutant rows are contact waves of speed ubar
 // (Roe averages vbar, Cbar of the transverse velocity and the
-// concentration, weighted by sqrt(h) like ubar).  FX = FLUX_IR_HH: IR-Roe
-// with the Harten-Hyman entropy fix (hh_fix).
+// concentration, weighted by sqrt(h) like ubar).  FLUX_IR_HH / FLUX_ROE_HH:
+// either with the Harten-Hyman entropy fix (hh_fix).
 template <typename T, bool TR, int FX>
 __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, T hR, T sR, T qR, T uR, T tR,
                                       T cR, T zR, T g)
@@ -152,12 +152,12 @@ __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, 
     const T w1 = wminus(lam1), w2 = wminus(lam2);
     T pm0 = w1 * a1 + w2 * a2;
     T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
-    if (FX == FLUX_IR_HH) hh_fix(hL, qL, uL, hR, qR, uR, lam1, lam2, i2c, g, pm0, pm1);
+    if (flux_hh(FX)) hh_fix(hL, qL, uL, hR, qR, uR, lam1, lam2, i2c, g, pm0, pm1);
     o.am = pm0;
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
-    if (FX == FLUX_ROE) {
+    if (flux_classical(FX)) {
         const T wu = wminus(ubar);
         const T vbar = (sL * tL + sR * tR) * isum;
         const T Xt = qR * tR - qL * tL;
@@ -745,7 +745,8 @@ template <int FX, bool RC> static hipError_t cart_batch_fx(swe_ctx *c, int32_t n
 hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
 {
     if (c->path == SWE_PATH_RECOMPUTE) return cart_batch_fx<FLUX_IR, true>(c, nsteps, cfl); // IR-Roe only
-    if (c->classical) return cart_batch_fx<FLUX_ROE, false>(c, nsteps, cfl);
+    if (c->classical) return c->hh ? cart_batch_fx<FLUX_ROE_HH, false>(c, nsteps, cfl)
+                                   : cart_batch_fx<FLUX_ROE, false>(c, nsteps, cfl);
     if (c->hh) return cart_batch_fx<FLUX_IR_HH, false>(c, nsteps, cfl);
     return cart_batch_fx<FLUX_IR, false>(c, nsteps, cfl);
 }

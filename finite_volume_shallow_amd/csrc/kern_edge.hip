@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, 
                 R[3 * l + 1] = qx * nx + qy * ny;
                 R[3 * l + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T, FX == FLUX_ROE>(L, z[a], R, z[b], g, r);
+            f = roe2_interior<T, flux_classical(FX)>(L, z[a], R, z[b], g, r);
         } else {
             f = roe2_wall<T>(L, z[a], g, r);
         }
@@ -211,8 +211,9 @@ template <int FX> static hipError_t edge_step_fx(swe_ctx *c, int64_t step, doubl
 
 hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl)
 {
-    if (c->classical) return edge_step_fx<FLUX_ROE>(c, step, cfl);
-    if (c->hh) return edge_step_fx<FLUX_IR_HH>(c, step, cfl); // one layer only (checked at create)
+    // the entropy fix is one-layer only (checked at create)
+    if (c->classical) return c->hh ? edge_step_fx<FLUX_ROE_HH>(c, step, cfl) : edge_step_fx<FLUX_ROE>(c, step, cfl);
+    if (c->hh) return edge_step_fx<FLUX_IR_HH>(c, step, cfl);
     return edge_step_fx<FLUX_IR>(c, step, cfl);
 }
 

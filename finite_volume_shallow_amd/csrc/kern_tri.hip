@@ -160,7 +160,7 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
                 Rs[3 * l2 + 1] = qx * nx + qy * ny;
                 Rs[3 * l2 + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T, FX == FLUX_ROE>(L, CA.z(), Rs, CB.z(), g, rr);
+            f = roe2_interior<T, flux_classical(FX)>(L, CA.z(), Rs, CB.z(), g, rr);
         } else {
             f = roe2_wall<T>(L, CA.z(), g, rr);
         }
@@ -919,6 +919,11 @@ hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl)
         if (c->classical)
             return f32 ? tri_batch_t<float, 2, false, FLUX_ROE>(c, nsteps, cfl) : tri_batch_t<double, 2, false, FLUX_ROE>(c, nsteps, cfl);
         return f32 ? tri_batch_t<float, 2, false>(c, nsteps, cfl) : tri_batch_t<double, 2, false>(c, nsteps, cfl);
+    }
+    if (c->classical && c->hh) {
+        if (c->ntracers)
+            return f32 ? tri_batch_t<float, 1, true, FLUX_ROE_HH>(c, nsteps, cfl) : tri_batch_t<double, 1, true, FLUX_ROE_HH>(c, nsteps, cfl);
+        return f32 ? tri_batch_t<float, 1, false, FLUX_ROE_HH>(c, nsteps, cfl) : tri_batch_t<double, 1, false, FLUX_ROE_HH>(c, nsteps, cfl);
     }
     if (c->classical) {
         if (c->ntracers)

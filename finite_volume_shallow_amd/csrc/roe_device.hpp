@@ -55,8 +55,10 @@ template <> __device__ __forceinline__ double wminus(double lam)
 }
 
 // Flux variants of the one-layer edge: IR-Roe, the classical Roe flux of
-// the whole edge system, IR-Roe with the Harten-Hyman entropy fix.
-enum : int { FLUX_IR = 0, FLUX_ROE = 1, FLUX_IR_HH = 2 };
+// the whole edge system, and each with the Harten-Hyman entropy fix.
+enum : int { FLUX_IR = 0, FLUX_ROE = 1, FLUX_IR_HH = 2, FLUX_ROE_HH = 3 };
+__host__ __device__ constexpr bool flux_classical(int fx) { return fx == FLUX_ROE || fx == FLUX_ROE_HH; }
+__host__ __device__ constexpr bool flux_hh(int fx) { return fx == FLUX_IR_HH || fx == FLUX_ROE_HH; }
 
 // Harten-Hyman entropy fix of the 2x2 Roe solution ([IR] Sec. 2.2 names the
 // fix of its ref. 25).  b = K^-1 (W_b - W_a) are the waves' state jumps and
@@ -132,13 +134,13 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     const T w1 = wminus(lam1), w2 = wminus(lam2);
     T pm0 = w1 * a1 + w2 * a2;
     T pm1 = w1 * a1 * lam1 + w2 * a2 * lam2;
-    if (FX == FLUX_IR_HH) hh_fix(hL, qnL, uL, hR, qnR, uR, lam1, lam2, i2c, g, pm0, pm1);
+    if (flux_hh(FX)) hh_fix(hL, qnL, uL, hR, qnR, uR, lam1, lam2, i2c, g, pm0, pm1);
     o.am = pm0;
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
     const T utL = qtL * ihL, utR = qtR * ihR;
-    if (FX == FLUX_ROE) {
+    if (flux_classical(FX)) {
         const T wu = wminus(ubar);
         const T vbar = (sL * utL + sR * utR) * isum;
         const T Xt = qnR * utR - qnL * utL;

@@ -71,9 +71,8 @@ int validate(const swe_mesh_desc *d, std::string &err)
     if (d->path < SWE_PATH_AUTO || d->path > SWE_PATH_RECOMPUTE) { err = "bad path"; return SWE_E_INVAL; }
     if (d->scheme != SWE_SCHEME_IR_ROE && d->scheme != SWE_SCHEME_ROE) { err = "bad scheme"; return SWE_E_INVAL; }
     if (d->entropy_fix != SWE_ENTROPY_FIX_NONE && d->entropy_fix != SWE_ENTROPY_FIX_HH) { err = "bad entropy_fix"; return SWE_E_INVAL; }
-    if (d->entropy_fix == SWE_ENTROPY_FIX_HH &&
-        (d->nlayers != 1 || d->scheme != SWE_SCHEME_IR_ROE || d->path == SWE_PATH_RECOMPUTE)) {
-        err = "the entropy fix is available for one layer with the IR-Roe flux on the fused and edge paths";
+    if (d->entropy_fix == SWE_ENTROPY_FIX_HH && (d->nlayers != 1 || d->path == SWE_PATH_RECOMPUTE)) {
+        err = "the entropy fix is available for one layer on the fused and edge paths";
         return SWE_E_INVAL;
     }
     if (!(d->g > 0.0) || !std::isfinite(d->g)) { err = "g must be > 0"; return SWE_E_INVAL; }

@@ -81,7 +81,7 @@ struct swe_ctx {
     int64_t N = 0;
     int nv = 3;
     bool classical = false; // classical Roe flux instead of IR-Roe
-    bool hh = false;        // Harten-Hyman entropy fix (one layer, IR-Roe)
+    bool hh = false;        // Harten-Hyman entropy fix (one layer)
     size_t rs = 8; // bytes per real
     int device = 0;
     hipStream_t stream = nullptr;

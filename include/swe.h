@@ -77,14 +77,15 @@ enum swe_scheme { SWE_SCHEME_IR_ROE = 0, SWE_SCHEME_ROE = 1 };
 
 /* Entropy fix.  [IR] Sec. 2.2 notes that the Roe solution needs one where
  * sonic rarefactions occur and names the Harten-Hyman fix.
- * SWE_ENTROPY_FIX_HH: that fix in its wave-splitting form, on the 2x2 part
- * of the one-layer IR-Roe flux: with b = K^-1 (W_b - W_a) the state jumps of
+ * SWE_ENTROPY_FIX_HH: that fix in its wave-splitting form, on the two
+ * acoustic waves of the one-layer flux (IR-Roe or classical; the classical
+ * flux's contact waves need none): with b = K^-1 (W_b - W_a) the state jumps of
  * the two Roe waves and W* = W_a + b_1 r_1 the state between them, a wave
  * whose characteristic speed changes sign from < 0 on its left state to > 0
  * on its right state is split into a left-moving part at the left speed and
  * a right-moving part at the right speed (fractions chosen so that the
  * wave's total flux jump is kept); the source term is untouched.  Available
- * for one layer with the IR-Roe flux on the FUSED and EDGE paths. */
+ * for one layer on the FUSED and EDGE paths. */
 enum swe_entropy_fix { SWE_ENTROPY_FIX_NONE = 0, SWE_ENTROPY_FIX_HH = 1 };
 
 typedef struct swe_mesh_desc {
@@ -95,7 +96,7 @@ typedef struct swe_mesh_desc {
     int32_t precision;   /* SWE_F64 or SWE_F32: storage and arithmetic type  */
     int32_t path;        /* enum swe_path                                    */
     int32_t scheme;      /* enum swe_scheme                                  */
-    int32_t entropy_fix; /* 0: none; 1: Harten-Hyman (one layer, IR-Roe)     */
+    int32_t entropy_fix; /* 0: none; 1: Harten-Hyman (one layer)             */
     double g;            /* gravity, > 0                                     */
     double r;            /* density ratio rho1/rho2 in (0, 1) (two layers)   */
 
@@ -140,7 +141,7 @@ typedef struct swe_mesh_desc {
  * a triangle with area <= 0, an edge shared by more than two triangles,
  * path, scheme or entropy_fix outside their enums, SWE_PATH_FUSED where no
  * fused path exists, SWE_PATH_RECOMPUTE with the classical scheme, the
- * entropy fix with two layers, the classical scheme or SWE_PATH_RECOMPUTE,
+ * entropy fix with two layers or SWE_PATH_RECOMPUTE,
  * a grid too large for 32-bit byte offsets of a field (fused Cartesian
  * path), a triangle mesh whose blocks cannot be formed (fused path);
  * SWE_E_NOMEM / SWE_E_HIP on allocation or runtime failure.  On error *out

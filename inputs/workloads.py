@@ -54,7 +54,7 @@ class Workload:
     tri: np.ndarray | None = None
     # "ir" (the IR-Roe scheme) or "classical" (full Roe matrix)
     scheme: str = "ir"
-    # 1: Harten-Hyman entropy fix (one layer, IR-Roe)
+    # 1: Harten-Hyman entropy fix (one layer)
     entropy_fix: int = 0
 
     @property

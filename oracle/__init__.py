@@ -45,6 +45,7 @@ def lib():
         L.or_roe1_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
         L.or_roe1c_edge.argtypes = [_D, _D, ctypes.c_double, _D, _D]
         L.or_roe1_edge_fix.argtypes = [_D, _D, ctypes.c_double, ctypes.c_int, _D, _D]
+        L.or_roe1c_edge_fix.argtypes = [_D, _D, ctypes.c_double, ctypes.c_int, _D, _D]
         L.or_roe1_wall.argtypes = [_D, ctypes.c_double, _D, _D]
         L.or_roe2_edge.argtypes = [_D, _D, ctypes.c_double, ctypes.c_double, _D, _D, _D]
         L.or_roe2_wall.argtypes = [_D, ctypes.c_double, ctypes.c_double, _D, _D]
@@ -95,6 +96,16 @@ def roe1_edge_fix(L, R, g=9.81, fix=1):
     L = _f64(L); R = _f64(R)
     phi = np.zeros(4); sp = ctypes.c_double()
     st = lib().or_roe1_edge_fix(_dp(L), _dp(R), g, int(fix), _dp(phi), ctypes.byref(sp))
+    if st:
+        raise OracleError(st)
+    return phi, sp.value
+
+
+def roe1c_edge_fix(L, R, g=9.81, fix=1):
+    """As roe1c_edge, with the Harten-Hyman entropy fix (fix=1)."""
+    L = _f64(L); R = _f64(R)
+    phi = np.zeros(4); sp = ctypes.c_double()
+    st = lib().or_roe1c_edge_fix(_dp(L), _dp(R), g, int(fix), _dp(phi), ctypes.byref(sp))
     if st:
         raise OracleError(st)
     return phi, sp.value
@@ -181,8 +192,8 @@ def run(w, nsteps=None, nthreads=None, check=True):
     L = lib()
     classical = int(getattr(w, "scheme", "ir") == "classical")
     fix = int(getattr(w, "entropy_fix", 0))
-    if fix and (classical or w.nlayers != 1):
-        raise ValueError("the entropy fix is implemented for the one-layer IR-Roe flux")
+    if fix and w.nlayers != 1:
+        raise ValueError("the entropy fix is implemented for one layer")
     if classical and w.kind == "cart" and w.nlayers != 1:
         raise ValueError("two layers run on triangle meshes only")
     if w.kind == "cart":

@@ -33,7 +33,7 @@
  *    the left state when the mass flux is > 0, else the right state.
  *  - No entropy fix by default.  [IR] Sec. 2.2 only says the Harten-Hyman
  *    fix of its ref. [25] can be adapted; the optional one here (one layer,
- *    IR-Roe) is that fix in its wave-splitting form, applied to the
+ *    IR-Roe or classical) is that fix in its wave-splitting form, applied to the
  *    conservative part of each acoustic wave: with b = K^-1 (W_R - W_L) the
  *    state jumps of the Roe waves and W* = W_L + b_1 r_1 the state between
  *    them, a wave k whose characteristic speed is < 0 on its left state and
@@ -202,8 +202,25 @@ static int roe1_ir(const double *L, const double *R, double g, int fix,
  * eigenvalues u - c, u, u, u + c with right eigenvectors
  *   r1 = (1, u - c, v, C), r2 = (0, 0, 1, 0), r3 = (0, 0, 0, 1), r4 = (1, u + c, v, C).
  * X = F(W_R) - F(W_L) - S (H_R - H_L); alpha = K^-1 X; Phi = F(W_L) + P^- X. */
+static int roe1_classical(const double *L, const double *R, double g, int fix,
+                          double *phi, double *speed);
+
 int or_roe1c_edge(const double *L, const double *R, double g, double *phi,
                   double *speed)
+{
+    return roe1_classical(L, R, g, 0, phi, speed);
+}
+
+/* As or_roe1c_edge, with the Harten-Hyman entropy fix on its two acoustic
+ * waves when fix != 0 (the contact waves are linearly degenerate: no fix). */
+int or_roe1c_edge_fix(const double *L, const double *R, double g, int fix,
+                      double *phi, double *speed)
+{
+    return roe1_classical(L, R, g, fix, phi, speed);
+}
+
+static int roe1_classical(const double *L, const double *R, double g, int fix,
+                          double *phi, double *speed)
 {
     double hL = L[0], qL = L[1], tL = L[2], cL = L[3], HL = L[4];
     double hR = R[0], qR = R[1], tR = R[2], cR = R[3], HR = R[4];
@@ -239,6 +256,14 @@ int or_roe1c_edge(const double *L, const double *R, double g, double *phi,
     for (int k = 0; k < 4; ++k) {
         double w = 0.5 * (1.0 - sgn(lam[k]));
         for (int v = 0; v < 4; ++v) phi[v] += w * al[k] * r[k][v];
+    }
+    if (fix) { /* the fix's change of the acoustic waves, along r1 and r4 */
+        double d0 = 0.0, d1 = 0.0;
+        hh_fix(L, R, g, lam[0], lam[3], &d0, &d1);
+        phi[0] += d0;
+        phi[1] += d1;
+        phi[2] += vbar * d0;
+        phi[3] += Cbar * d0;
     }
     *speed = fmax(fabs(lam[0]), fabs(lam[3]));
     return OR_OK;
@@ -688,7 +713,7 @@ int or_run_cart(int nx, int ny, double dx, double dy, int periodic_x,
                     double Rst[5] = {h[m], qx[m] * ex[sd] + qy[m] * ey[sd],
                                      -qx[m] * ey[sd] + qy[m] * ex[sd],
                                      hc ? hc[m] : 0.0, -z[m]};
-                    st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)
+                    st = classical ? roe1_classical(Lst, Rst, g, fix, phi, &sp)
                                    : roe1_ir(Lst, Rst, g, fix, phi, &sp);
                 }
                 if (st > err) err = st;
@@ -833,7 +858,7 @@ int or_run_tri(int64_t nnodes, const double *xy, int64_t ncells,
                 } else {
                     double Rst[5] = {h[m], qx[m] * ex + qy[m] * ey, -qx[m] * ey + qy[m] * ex,
                                      hc ? hc[m] : 0.0, -z[m]};
-                    st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)
+                    st = classical ? roe1_classical(Lst, Rst, g, fix, phi, &sp)
                                    : roe1_ir(Lst, Rst, g, fix, phi, &sp);
                 }
                 if (st > err) err = st;

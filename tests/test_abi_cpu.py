@@ -116,8 +116,8 @@ def test_recompute_path_is_ir_roe_only():
     assert e.value.status == swe.SWE_E_INVAL
 
 
-def test_entropy_fix_is_one_layer_ir_roe_only():
-    for kw in (dict(scheme="classical"), dict(path=swe.SWE_PATH_RECOMPUTE)):
+def test_entropy_fix_is_one_layer_only():
+    for kw in (dict(path=swe.SWE_PATH_RECOMPUTE),):
         d, keep = swe.mesh_desc(kind="cart", nx=8, ny=8, dx=1.0, dy=1.0, entropy_fix=1, **kw)
         with pytest.raises(swe.SweError) as e:
             swe.swe_create_mesh(d)

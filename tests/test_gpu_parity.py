@@ -286,6 +286,10 @@ HH = {
     "hh-tri-circular-30-f32": (lambda: _transonic_tri(30), 60, "f32"),
     "hh-flow-160x96-f32": (_with_fix(CASES["flow-160x96-f32"][0]), 100, "f32"),
     "hh-tri-ragged-19": (_with_fix(CASES["tri-ragged-19"][0]), 25, "f64"),
+    # the classical flux with the fix
+    "hh-classical-dam-break-200x6-f64": (lambda: _classical(lambda: _transonic_cart(200, 6)), 150, "f64"),
+    "hh-classical-tri-circular-24-f64": (lambda: _classical(lambda: _transonic_tri(24)), 80, "f64"),
+    "hh-classical-dam-break-131x5-f32": (lambda: _classical(lambda: _transonic_cart(131, 5)), 100, "f32"),
 }
 
 

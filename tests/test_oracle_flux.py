@@ -549,3 +549,31 @@ def test_entropy_fix_acts_on_transonic_rarefactions_and_stays_conservative():
         assert abs(into_j[3] - phi_ij[3]) < 1e-13 * scale
         assert abs((into_j[1] - phi_ij[1]) - G * h * (R[4] - L[4])) < 1e-12 * scale
     assert changed > 800   # most of these straddle the edge
+
+
+def test_entropy_fix_of_the_classical_flux():
+    # the fix acts on the acoustic waves only: inactive where no wave is
+    # transonic; on transonic states its change of the classical flux is the
+    # IR-Roe flux's change in mass and normal momentum, carried along the
+    # acoustic eigenvectors (1, lam, vbar, Cbar) in the other two rows, and
+    # the two sides of an edge still conserve mass, transverse momentum and
+    # pollutant
+    rng = np.random.default_rng(43)
+    for L, R in _subcritical_small_jumps(rng, 300):
+        assert np.array_equal(oracle.roe1c_edge(L, R, G)[0], oracle.roe1c_edge_fix(L, R, G)[0])
+    for L, R in _transonic_dam_breaks(rng, 300):
+        d_ir = oracle.roe1_edge_fix(L, R, G)[0] - oracle.roe1_edge(L, R, G)[0]
+        d_cl = oracle.roe1c_edge_fix(L, R, G)[0] - oracle.roe1c_edge(L, R, G)[0]
+        A, _ = _classical_matrix(L, R)
+        vbar, Cbar = A[2, 1], A[3, 1]
+        scale = abs(d_ir[:2]).max() + 1e-300
+        assert abs(d_cl[0] - d_ir[0]) <= 1e-12 * scale and abs(d_cl[1] - d_ir[1]) <= 1e-12 * scale
+        assert abs(d_cl[2] - vbar * d_cl[0]) <= 1e-12 * scale * (abs(vbar) + 1)
+        assert abs(d_cl[3] - Cbar * d_cl[0]) <= 1e-12 * scale * (abs(Cbar) + 1)
+        phi_ij, _ = oracle.roe1c_edge_fix(L, R, G)
+        phi_ji, _ = oracle.roe1c_edge_fix(_flip(R, [1, 2]), _flip(L, [1, 2]), G)
+        into_j = np.array([-phi_ji[0], phi_ji[1], phi_ji[2], -phi_ji[3]])
+        s = abs(phi_ij).max() + 1.0
+        assert abs(into_j[0] - phi_ij[0]) < 1e-13 * s
+        assert abs(into_j[2] - phi_ij[2]) < 1e-13 * s
+        assert abs(into_j[3] - phi_ij[3]) < 1e-13 * s

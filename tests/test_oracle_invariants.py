@@ -536,3 +536,21 @@ def test_entropy_fix_on_triangles_is_rotation_invariant_and_conservative():
     assert abs(_fsum(sa[0] * area) - _fsum(w.state[0] * area)) <= 1e-12 * _fsum(w.state[0] * area)
     plain, _, _ = oracle.run(w.copy(entropy_fix=0))
     assert np.abs(plain[0] - sa[0]).max() > 1e-4        # the fix acted
+
+
+def test_entropy_fix_with_the_classical_flux_removes_the_expansion_shock():
+    res = []
+    for nx in (100, 200, 400):
+        def run(fix):
+            w = inputs.dam_break(nx=nx, ny=4)
+            w.dx = w.dy = 100.0 / nx
+            x = (np.arange(nx) + 0.5) * w.dx
+            h0 = np.where(x < 50.0, 1.0, 0.05)
+            w.state = [np.tile(h0, 4), np.zeros(4 * nx), np.zeros(4 * nx), np.tile(h0, 4) * 0.5]
+            w.scheme, w.entropy_fix = "classical", fix
+            st, _, _ = oracle.run(w, nsteps=nx // 2)
+            h = st[0].reshape(4, nx)[0]
+            return np.abs(np.diff(h[nx // 2 - 3:nx // 2 + 3])).max()
+        res.append((run(0), run(1)))
+    assert all(p > 0.1 for p, _ in res)
+    assert res[1][1] < 0.6 * res[0][1] and res[2][1] < 0.6 * res[1][1]

@@ -60,8 +60,8 @@ MUTANTS = [
     ("classical eigenvector rows", "{{1.0, lam[0], vbar, Cbar},", "{{1.0, lam[0], Cbar, vbar},", 1),
     ("classical contact speed", "double lam[4] = {ubar - c, ubar, ubar, ubar + c};",
      "double lam[4] = {ubar - c, 0.0, ubar, ubar + c};", 1),
-    ("classical switch ignored", "st = classical ? or_roe1c_edge(Lst, Rst, g, phi, &sp)",
-     "st = 0 ? or_roe1c_edge(Lst, Rst, g, phi, &sp)", 2),
+    ("classical switch ignored", "st = classical ? roe1_classical(Lst, Rst, g, fix, phi, &sp)",
+     "st = 0 ? roe1_classical(Lst, Rst, g, fix, phi, &sp)", 2),
     # classical Roe, two layers
     ("classical 6x6 average", "double v1 = (s1L * (t1L / h1L) + s1R * (t1R / h1R)) / (s1L + s1R);",
      "double v1 = 0.5 * (t1L / h1L + t1R / h1R);", 1),
@@ -91,6 +91,9 @@ MUTANTS = [
     ("fix: switch ignored", "if (fix) hh_fix(L, R, g, lam1, lam2, &P0, &P1);",
      "if (0) hh_fix(L, R, g, lam1, lam2, &P0, &P1);", 1),
     ("fix: transonic test", "if (l1L < 0.0 && l1R > 0.0) {", "if (l1L < 0.0 || l1R > 0.0) {", 1),
+    ("classical fix: transverse row", "        phi[2] += vbar * d0;", "        phi[2] += Cbar * d0;", 1),
+    ("classical fix: switch ignored", "    if (fix) { /* the fix's change of the acoustic waves, along r1 and r4 */",
+     "    if (0) { /* the fix's change of the acoustic waves, along r1 and r4 */", 1),
 ]
 
 

@@ -309,12 +309,15 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             // <= 512), run by the software-pipelined persistent kernel;
             // failing that (irregular meshes) 288, 192 or 128 cells with one
             // workgroup per block.  Two layers (twice the LDS per cell and
-            // edge, registers for two blocks per CU): 192, else 128 cells.
-            // Blocks keep their LDS within 64 KiB (80 KiB for two layers).
+            // edge): 224 cells with one workgroup per block, else 192 or 128.
+            // Blocks keep their LDS within 64 KiB (one layer) or 96 KiB (two
+            // layers: one 224-cell block per CU, measured 2-3 % faster on the
+            // 1M two-layer mesh than two 192-cell blocks within 80 KiB; 256
+            // cells and more need two rounds of threads, 30-50 % slower).
             c->tb.nt = 512;
-            int B = c->nv == 6 ? 192 : 224;
+            int B = 224;
             bool pipe = c->nv != 6;
-            size_t lds_cap = c->nv == 6 ? 81920 : 65536;
+            size_t lds_cap = c->nv == 6 ? 98304 : 65536;
             if (const char *e = std::getenv("SWE_TRI_B")) { // tuning overrides
                 const int v = std::atoi(e);
                 if (v >= 64 && v <= 512 && v % 32 == 0) B = v;

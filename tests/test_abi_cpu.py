@@ -196,3 +196,16 @@ def test_bench_names_every_workload_with_its_precision():
              "tri-2M": dict(nq=4), "two-layer-1M": dict(nq=4)}
     for name, kw in small.items():
         assert inputs.make_workload(name, **kw).precision == bench.PRECISION[name], name
+
+
+@pytest.mark.parametrize("kw, msg", [
+    (dict(kind="tri", node_xy=np.zeros((3, 2)), tri=np.zeros((0, 3), dtype=np.int32)), "empty"),
+    # the fused grid kernel addresses a field with 32-bit byte offsets
+    (dict(kind="cart", nx=70000, ny=70000, dx=1.0, dy=1.0, precision="f32"), "too large"),
+    (dict(kind="cart", nx=40000, ny=40000, dx=1.0, dy=1.0, precision="f64"), "too large"),
+])
+def test_create_rejects_empty_and_oversized_meshes(kw, msg):
+    d, keep = swe.mesh_desc(**kw)
+    with pytest.raises(swe.SweError) as e:
+        swe.swe_create_mesh(d)
+    assert e.value.status == swe.SWE_E_INVAL and msg in str(e.value)

@@ -49,6 +49,7 @@ CASES = {
     "tri-ragged-19": (lambda: inputs.circular_dam_break(nq=19), 25, "f64"),
     "two-layer-30": (lambda: inputs.two_layer_dam_break(nq=30), 200, "f64"),
     "two-layer-13": (lambda: inputs.two_layer_dam_break(nq=13), 100, "f64"),
+    "two-layer-30-f32": (lambda: inputs.two_layer_dam_break(nq=30), 100, "f32"),
     "tri-shuffled-30": (lambda: _shuffled_tri(30), 60, "f64"),
     "tri-40-f32": (lambda: inputs.circular_dam_break(nq=40), 100, "f32"),
     "flow-periodic-xy-67x40-f64": (lambda: _periodic_xy(67, 40), 60, "f64"),

@@ -77,15 +77,34 @@ def _code_only(text):
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash(path):
-    """Hash of the library's code (comments and layout ignored): counter
-    records taken on other code are not reused."""
+# The sources that make each kernel family: its own file, the mesh
+# preprocessing it consumes, the shared device headers and the host code that
+# picks its launch shape.
+_KERNEL_SOURCES = {"k_cart": ("kern_cart.hip",), "k_tri": ("kern_tri.hip", "mesh_host.cpp"),
+                   "k_edge": ("kern_edge.hip", "mesh_host.cpp")}
+
+
+def kernel_source_hash(path, kernel=None):
+    """Hash of the code (comments and layout ignored) that builds `kernel`
+    (all of the library if None): counter records taken on other code are not
+    reused."""
     h = hashlib.sha256()
     csrc = os.path.join(path, "finite_volume_shallow_amd", "csrc")
+    own = None
+    if kernel is not None:
+        fam = next((k for k in _KERNEL_SOURCES if kernel.startswith(k)), None)
+        if fam is None:
+            raise ValueError(f"no source list for kernel {kernel}")
+        own = _KERNEL_SOURCES[fam]
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(f.encode())
-            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
+        if not f.endswith((".hip", ".hpp", ".cpp")):
+            continue
+        if own is not None and f.startswith("kern_") and f not in own:
+            continue
+        if own is not None and f.endswith(".cpp") and f not in own:
+            continue
+        h.update(f.encode())
+        h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -138,7 +157,7 @@ def ingest_pmc(args):
     key = f"{args.ingest_name}@{args.workload}-{prec}"
     data[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                  "fetch_scale": f_scale, "write_scale": w_scale,
-                 "dispatches": [n_f, n_w], "src_hash": kernel_source_hash(ROOT)}
+                 "dispatches": [n_f, n_w], "src_hash": kernel_source_hash(ROOT, args.ingest_name)}
     os.makedirs(PROFILE_DIR, exist_ok=True)
     json.dump(data, open(path, "w"), indent=1, sort_keys=True)
     print(json.dumps({key: data[key]}))
@@ -294,7 +313,7 @@ def main():
     # one fused launch per step: the average launch duration is the time per
     # step (the batch also holds one small dt-prologue launch)
     achieved = bpc * N / (ms_step / 1e3) / 1e9
-    src_hash = kernel_source_hash(ROOT)
+    src_hash = kernel_source_hash(ROOT, kernel)
     # counters are recorded per kernel instance: the classical-flux kernel is
     # another instance (its own name in the traffic table)
     variant = ("-classical" if args.scheme == "classical" else "") + ("-hh" if args.entropy_fix else "")

@@ -30,7 +30,6 @@
 
 namespace swe {
 
-constexpr int TRI_THREADS = 256;
 constexpr int TRI_XCD = 8;
 constexpr int TRI_NPART = 64;
 
@@ -850,20 +849,24 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
     const size_t lds = tri_lds_bytes(NV, sizeof(T), c->tb.lc_max, c->tb.e_max);
     const int per_xcd = (c->tb.nblocks + TRI_XCD - 1) / TRI_XCD;
     const dim3 grid((unsigned)(per_xcd * TRI_XCD)), block(NT);
-    if (lds > 65536) {
-        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, true, RD, NT>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, FX, RC>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > 65536) { // above the default dynamic LDS limit: opt in per kernel
+        hipError_t e = hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, true, RD, NT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)k_tri_fused<T, NL, TR, false, RD, NT, FX, RC>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
     hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
                        tri_args<T>(c, 0, cfl));
     if constexpr (RD == 1 && !RC) {
         if (c->tb.pipe_wgs != 0) {
-            if (lds > 65536)
-                hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT, FX>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (lds > 65536) {
+                const hipError_t e = hipFuncSetAttribute((const void *)k_tri_pipe<T, NL, TR, NT, FX>,
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+            }
             if (c->tb.pipe_wgs < 0) { // as many workgroups as can be resident at once
                 int per_cu = 0, cus = 0;
                 if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT, FX>, NT, lds) !=

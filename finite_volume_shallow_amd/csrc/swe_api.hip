@@ -353,6 +353,13 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 }
                 B = B > 192 ? 192 : 128;
             }
+            // the fused triangle kernels address these arrays with 32-bit byte offsets
+            const uint64_t lim = (uint64_t)1 << 32;
+            if (hb.e_ab.size() * 4 > lim || hb.halo_ids.size() * 4 > lim || hb.slots.size() * 2 > lim ||
+                hb.e_gx.size() * c->rs > lim || hb.iarea.size() * c->rs > lim) {
+                c->err = "triangle mesh too large for the fused path; use SWE_PATH_EDGE";
+                throw Fail{SWE_E_INVAL};
+            }
             c->tb.pipe_wgs = pipe ? -1 : 0; // -1: size the persistent grid at the first launch
         }
 

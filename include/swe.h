@@ -143,7 +143,8 @@ typedef struct swe_mesh_desc {
  * fused path exists, SWE_PATH_RECOMPUTE with the classical scheme, the
  * entropy fix with two layers or SWE_PATH_RECOMPUTE,
  * a grid too large for 32-bit byte offsets of a field (fused Cartesian
- * path), a triangle mesh whose blocks cannot be formed (fused path);
+ * path), a triangle mesh whose blocks cannot be formed or whose per-block
+ * arrays exceed 32-bit byte offsets (fused and recomputation paths);
  * SWE_E_NOMEM / SWE_E_HIP on allocation or runtime failure.  On error *out
  * is set to NULL and nothing leaks. */
 int swe_create_mesh(const swe_mesh_desc *desc, swe_ctx **out);

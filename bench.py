@@ -231,8 +231,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding design notes); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the sharding design is described, not built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -311,9 +311,10 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             // workgroup per block.  Two layers (twice the LDS per cell and
             // edge): 224 cells with one workgroup per block, else 192 or 128.
             // Blocks keep their LDS within 64 KiB (one layer) or 96 KiB (two
-            // layers: one 224-cell block per CU, measured 2-3 % faster on the
-            // 1M two-layer mesh than two 192-cell blocks within 80 KiB; 256
-            // cells and more need two rounds of threads, 30-50 % slower).
+            // layers: 224-cell blocks, 79 KiB on the 1M two-layer mesh,
+            // measured 2-3 % faster there than 192-cell blocks; 256 cells and
+            // more put many edges in a second round of threads, 30-50 %
+            // slower).
             c->tb.nt = 512;
             int B = 224;
             bool pipe = c->nv != 6;

@@ -122,8 +122,14 @@ template <typename T> void upload_geometry(swe_ctx *c, const HostEdges &h)
 // neighbouring tiles share are then read close together and served from
 // L2).  Smaller grids: 10 rows, halved while there are fewer than 1024
 // tiles, down to 4.  SWE_CART_TY / SWE_CART_ALT override both (tuning and
-// tests).
-void cart_tiling(int64_t nx, int64_t ny, int &ty, int &alt)
+// tests).  With periodic y a tile's march (its rows and two halo rows on
+// either side) wraps once at most, so a tile has fewer rows than the grid.
+static int cart_ty_limit(int64_t ny, bool pery, int ty)
+{
+    return pery ? (int)std::min<int64_t>(ty, std::max<int64_t>(1, ny - 1)) : ty;
+}
+
+void cart_tiling(int64_t nx, int64_t ny, bool pery, int &ty, int &alt)
 {
     const int64_t strips = (nx + 59) / 60;
     if (strips * ((ny + 11) / 12) >= 8192) {
@@ -139,6 +145,7 @@ void cart_tiling(int64_t nx, int64_t ny, int &ty, int &alt)
         if (v >= 4 && v <= 4096) ty = v;
     }
     if (const char *e = std::getenv("SWE_CART_ALT")) alt = std::atoi(e) != 0;
+    ty = cart_ty_limit(ny, pery, ty);
 }
 
 template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
@@ -387,7 +394,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
         } else if (d->mesh_kind == SWE_MESH_CART) {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
-            cart_tiling(d->nx, d->ny, c->cart_ty, c->cart_alt);
+            cart_tiling(d->nx, d->ny, d->bc_y == SWE_BC_PERIODIC, c->cart_ty, c->cart_alt);
         } else {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             if (c->prec == SWE_F32) upload_blocks<float>(c, hb);

@@ -53,6 +53,7 @@ CASES = {
     "tri-shuffled-30": (lambda: _shuffled_tri(30), 60, "f64"),
     "tri-40-f32": (lambda: inputs.circular_dam_break(nq=40), 100, "f32"),
     "flow-periodic-xy-67x40-f64": (lambda: _periodic_xy(67, 40), 60, "f64"),
+    "flow-periodic-xy-8x5-f64": (lambda: _periodic_xy(8, 5), 40, "f64"),
 }
 
 
@@ -65,6 +66,8 @@ TILINGS = {
     "flow-ragged-67x33-f64": [(4, 1), (12, 1)],
     "dam-break-ragged-131x5": [(4, 1)],
     "flow-periodic-xy-67x40-f64": [(4, 1), (8, 1), (12, 1)],
+    # asks for more rows per tile than the periodic grid has: limited to ny - 1
+    "flow-periodic-xy-8x5-f64": [(12, 1), (12, 0)],
 }
 
 

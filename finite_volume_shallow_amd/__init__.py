@@ -101,6 +101,23 @@ def _f64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
+def _expect_fields(ctx, arrays, what):
+    """The library reads or writes ncells values per array and one array
+    per conserved variable: check the caller's arrays before handing them
+    over (raw device pointers cannot be checked and are passed as given)."""
+    n, nv = _lib.swe_ncells(ctx), _lib.swe_nvars(ctx)
+    if n < 0 or nv <= 0:
+        raise ValueError(f"{what}: not a valid context")
+    if len(arrays) != nv:
+        raise ValueError(f"{what}: {nv} arrays expected, got {len(arrays)}")
+    for a in arrays:
+        size = a.numel() if hasattr(a, "numel") else (np.size(a) if isinstance(a, np.ndarray) else None)
+        if size is not None and size != n:
+            raise ValueError(f"{what}: arrays of {n} cells expected, got {size}")
+        if hasattr(a, "is_contiguous") and not a.is_contiguous():
+            raise ValueError(f"{what}: device tensors must be contiguous")
+
+
 # ------------------------------------------------------------------ C names
 
 def swe_create_mesh(desc: swe_mesh_desc):
@@ -114,6 +131,9 @@ def swe_create_mesh(desc: swe_mesh_desc):
 def swe_set_state(ctx, z_bed, cons):
     z = _f64(z_bed)
     arrs = [_f64(a) for a in cons]
+    _expect_fields(ctx, arrs, "swe_set_state")
+    if z.size != _lib.swe_ncells(ctx):
+        raise ValueError(f"swe_set_state: z_bed of {_lib.swe_ncells(ctx)} cells expected, got {z.size}")
     ptrs = (_D * len(arrs))(*[a.ctypes.data_as(_D) for a in arrs])
     _check(_lib.swe_set_state(ctx, z.ctypes.data_as(_D), ptrs), ctx)
 
@@ -123,6 +143,9 @@ def _devptr(x):
 
 
 def swe_set_state_device(ctx, z_bed, cons):
+    _expect_fields(ctx, list(cons), "swe_set_state_device")
+    if hasattr(z_bed, "numel") and z_bed.numel() != _lib.swe_ncells(ctx):
+        raise ValueError(f"swe_set_state_device: z_bed of {_lib.swe_ncells(ctx)} cells expected")
     ptrs = (ctypes.c_void_p * len(cons))(*[_devptr(a) for a in cons])
     _check(_lib.swe_set_state_device(ctx, _devptr(z_bed), ptrs), ctx)
 
@@ -145,6 +168,7 @@ def swe_get_state(ctx):
 
 
 def swe_get_state_device(ctx, outs):
+    _expect_fields(ctx, list(outs), "swe_get_state_device")
     ptrs = (ctypes.c_void_p * len(outs))(*[_devptr(a) for a in outs])
     _check(_lib.swe_get_state_device(ctx, ptrs), ctx)
 
@@ -188,6 +212,10 @@ def mesh_desc(*, kind, nlayers=1, ntracers=0, precision="f64", path=SWE_PATH_AUT
               node_xy=None, tri=None, stream=None):
     """Fill a swe_mesh_desc.  Returns (desc, keepalive) - keep the second
     value referenced until swe_create_mesh returned."""
+    for name, val, allowed in (("kind", kind, ("cart", "tri")), ("precision", precision, ("f32", "f64")),
+                               ("bc_x", bc_x, ("wall", "periodic")), ("bc_y", bc_y, ("wall", "periodic"))):
+        if val not in allowed:
+            raise ValueError(f"{name} must be one of {allowed}, got {val!r}")
     d = swe_mesh_desc()
     d.abi_version = SWE_ABI_VERSION
     d.mesh_kind = SWE_MESH_CART if kind == "cart" else SWE_MESH_TRI

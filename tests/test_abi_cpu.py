@@ -71,12 +71,14 @@ def _cart(**kw):
     (dict(nlayers=2, r=0.5), "two layers"),
     (dict(nlayers=3), "nlayers"),
     (dict(ntracers=2), "ntracers"),
-    (dict(precision="f16"), None),
+    (dict(precision=7), None),
 ])
 def test_create_rejects_bad_cartesian(kw, msg):
+    kw = dict(kw)
+    code = kw.pop("precision", None)  # an out-of-enum code, set past the binding's check
     d, keep = _cart(**kw)
-    if kw.get("precision") == "f16":
-        d.precision = 7
+    if code is not None:
+        d.precision = code
     with pytest.raises(swe.SweError) as e:
         swe.swe_create_mesh(d)
     assert e.value.status == swe.SWE_E_INVAL
@@ -142,6 +144,15 @@ def test_create_rejects_bad_scheme():
     assert e.value.status == swe.SWE_E_INVAL and "scheme" in str(e.value)
     with pytest.raises(ValueError):
         swe.mesh_desc(kind="cart", nx=4, ny=4, dx=1.0, dy=1.0, scheme="hllc")
+
+
+@pytest.mark.parametrize("field,value", [("kind", "hex"), ("precision", "f16"), ("bc_x", "periodc"),
+                                         ("bc_y", "open")])
+def test_mesh_desc_rejects_unknown_names(field, value):
+    kw = dict(kind="cart", nx=4, ny=4, dx=1.0, dy=1.0)
+    kw[field] = value
+    with pytest.raises(ValueError, match=field):
+        swe.mesh_desc(**kw)
 
 
 @pytest.mark.parametrize("case", ["clockwise", "node-range", "triple-edge", "two-layer-tracer", "bad-r"])

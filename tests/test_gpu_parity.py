@@ -500,6 +500,18 @@ def test_error_paths():
         got = swe.swe_get_state(ctx)
         for a, b in zip(got, w.state):
             assert (a == b).all()
+        # the binding checks array counts and lengths before the library
+        # would read past a short array
+        with pytest.raises(ValueError):
+            swe.swe_set_state(ctx, w.z, w.state[:3])
+        with pytest.raises(ValueError):
+            swe.swe_set_state(ctx, w.z, [a[:-1] for a in w.state])
+        with pytest.raises(ValueError):
+            swe.swe_set_state(ctx, w.z[:-1], w.state)
+        import torch
+        dev = [torch.zeros(w.ncells + 1, dtype=torch.float64, device="cuda") for _ in w.state]
+        with pytest.raises(ValueError):
+            swe.swe_get_state_device(ctx, dev)
     finally:
         swe.swe_destroy(ctx)
 

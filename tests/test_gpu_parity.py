@@ -433,6 +433,38 @@ def test_device_state_roundtrip_and_stream():
         assert (o == g).all()
 
 
+def test_two_contexts_interleaved():
+    """Two live contexts, each on its own stream, stepped in alternating
+    batches: each matches its own oracle run (contexts share nothing)."""
+    import torch
+    import finite_volume_shallow_amd as swe
+    say("[ctx] a Cartesian and a triangle context interleaved on two streams")
+    wa = inputs.dam_break(nx=40, ny=24)
+    wb = inputs.circular_dam_break(nq=14)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    da, ka = swe.desc_from_workload(wa, stream=sa)
+    db, kb = swe.desc_from_workload(wb, stream=sb)
+    ca = swe.swe_create_mesh(da)
+    try:
+        cb = swe.swe_create_mesh(db)
+        try:
+            swe.swe_set_state(ca, wa.z, wa.state)
+            swe.swe_set_state(cb, wb.z, wb.state)
+            ta = tb = 0.0
+            for _ in range(3):
+                ta += swe.swe_step(ca, 10, wa.cfl)[0]
+                tb += swe.swe_step(cb, 10, wb.cfl)[0]
+            got_a, got_b = swe.swe_get_state(ca), swe.swe_get_state(cb)
+        finally:
+            swe.swe_destroy(cb)
+    finally:
+        swe.swe_destroy(ca)
+    for w, got, t in ((wa, got_a, ta), (wb, got_b, tb)):
+        ref, rdts = oracle_reference(w, nsteps=30)
+        assert max(field_errors(got, ref, w.g)) <= FP64_TOL
+        assert abs(t - rdts.sum()) <= 1e-12 * rdts.sum()
+
+
 def test_device_state_roundtrip_triangles():
     import torch
     import finite_volume_shallow_amd as swe

@@ -419,6 +419,11 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         free_all(c);
         delete c;
         return f.code;
+    } catch (const std::bad_alloc &) { // host memory for the mesh work
+        g_create_err = "out of host memory";
+        free_all(c);
+        delete c;
+        return SWE_E_NOMEM;
     }
     *out = c;
     return SWE_OK;
@@ -458,6 +463,9 @@ int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
             upload_real(c, (char *)c->state[0] + (size_t)v * c->N * c->rs, ordered(cons[v]), c->N);
     } catch (const Fail &f) {
         return f.code;
+    } catch (const std::bad_alloc &) {
+        c->err = "out of host memory";
+        return SWE_E_NOMEM;
     }
     c->has_state = true;
     c->err.clear();
@@ -491,6 +499,9 @@ int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
         }
     } catch (const Fail &f) {
         return f.code;
+    } catch (const std::bad_alloc &) {
+        c->err = "out of host memory";
+        return SWE_E_NOMEM;
     }
     c->has_state = true;
     c->err.clear();
@@ -544,6 +555,9 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
         std::memcpy(&flags, c->h_pinned + 4, sizeof(unsigned));
     } catch (const Fail &f) {
         return f.code;
+    } catch (const std::bad_alloc &) {
+        c->err = "out of host memory";
+        return SWE_E_NOMEM;
     }
     c->hist_count = nsteps;
     if (t_adv) *t_adv = c->h_pinned[3];
@@ -597,6 +611,9 @@ int swe_get_state(swe_ctx *c, double *const *out)
         }
     } catch (const Fail &f) {
         return f.code;
+    } catch (const std::bad_alloc &) {
+        c->err = "out of host memory";
+        return SWE_E_NOMEM;
     }
     return SWE_OK;
 }
@@ -626,6 +643,9 @@ int swe_get_state_device(swe_ctx *c, void *const *out)
         }
     } catch (const Fail &f) {
         return f.code;
+    } catch (const std::bad_alloc &) {
+        c->err = "out of host memory";
+        return SWE_E_NOMEM;
     }
     return SWE_OK;
 }
@@ -645,6 +665,9 @@ int swe_get_dt_history(swe_ctx *c, double *out, int64_t cap, int64_t *count)
         HIPTRY(hipStreamSynchronize(c->stream));
     } catch (const Fail &f) {
         return f.code;
+    } catch (const std::bad_alloc &) {
+        c->err = "out of host memory";
+        return SWE_E_NOMEM;
     }
     return SWE_OK;
 }

@@ -18,7 +18,8 @@
  * speeds, then a global minimum for dt; (iii) the conserved-variable update.
  *
  * Every entry point returns an int status (SWE_OK = 0 or a negative
- * SWE_E_* code) unless stated otherwise; no C++ exception crosses the ABI.
+ * SWE_E_* code) unless stated otherwise; no C++ exception crosses the ABI
+ * (any call that runs out of host or device memory returns SWE_E_NOMEM).
  * A context is not thread-safe; separate contexts are independent.
  * All GPU work of a context is ordered on one HIP stream.
  */

@@ -209,6 +209,15 @@ def test_bench_names_every_workload_with_its_precision():
         assert inputs.make_workload(name, **kw).precision == bench.PRECISION[name], name
 
 
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    root = os.path.join(os.path.dirname(__file__), "..")
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
+    assert r.stdout.strip() == ""  # no JSON line for a run that did not happen
+
+
 @pytest.mark.parametrize("kw, msg", [
     (dict(kind="tri", node_xy=np.zeros((3, 2)), tri=np.zeros((0, 3), dtype=np.int32)), "empty"),
     # the fused grid kernel addresses a field with 32-bit byte offsets

@@ -306,8 +306,8 @@ def main():
     if used_path != "edge":
         # one-layer triangle meshes of regular size run the pipelined kernel
         kernel = "k_cart_fused" if w.kind == "cart" else ("k_tri_pipe" if w.nlayers == 1 else "k_tri_fused")
-        if used_path == "recompute":
-            kernel += "-recompute"
+        if used_path == "recompute":  # one workgroup per block on triangles
+            kernel = ("k_cart_fused" if w.kind == "cart" else "k_tri_fused") + "-recompute"
     else:
         kernel = "k_edge_flux+k_cell_dt+k_cell_update"
     # one fused launch per step: the average launch duration is the time per

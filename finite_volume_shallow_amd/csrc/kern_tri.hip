@@ -269,8 +269,12 @@ __device__ __forceinline__ uint32_t tri_unpack(double x) { return (uint32_t)x; }
 // three of its edges itself (interior edges twice over), for the fluxes and
 // for the Eq. (5) speeds; the LDS edge records then hold the edges' cell
 // pair and geometry.  Same inputs per edge, same accumulation order.
+// Two layers (shared edges): at least four waves per SIMD, so that two
+// 512-thread workgroups fit a CU (LDS allows two 224-cell blocks); the
+// classical flux would otherwise take 142 VGPRs and leave room for one.
 template <typename T, int NL, bool TR, bool DT0, int RD, int NT, int FX = FLUX_IR, bool RC = false>
-__global__ __launch_bounds__(NT) void k_tri_fused(TriArgs<T> A)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NL == 2 && !RC ? 4 : 1))) void
+k_tri_fused(TriArgs<T> A)
 {
     constexpr int NV = NL == 2 ? 6 : (TR ? 4 : 3);
     using Rec = TriRec<NL, NV>;

@@ -6,13 +6,17 @@
 //                Roe flux fluctuations for both sides and the edge's largest
 //                wave speed, rotates back (step 4) and writes
 //                |G| T^-1 (fluctuation) for each side plus |G| ||D||_inf.
-//   k_cell_dt    one thread per cell: sums |G| ||D||_inf over the cell's
-//                edges and forms dt_i = 2 gamma |V_i| / sum ([IR] Eq. (5));
-//                a wavefront shuffle min, a block min and one atomic min per
-//                block on the bit pattern of the (non-negative) double.
+//   k_cell_dt    grid-stride over the cells: sums |G| ||D||_inf over each
+//                cell's edges and forms dt_i = 2 gamma |V_i| / sum ([IR]
+//                Eq. (5)); a wavefront min, a block min and one atomic min
+//                per block on the bit pattern of the (non-negative) double.
+//                At most DT_BLOCKS blocks, so that the atomics on the one
+//                dt slot stay few.
 //   k_cell_update one thread per cell: gathers its edges' fluctuations in a
 //                fixed order (no atomics, deterministic) and applies Eq. (4)
 //                with the global dt.
+#include <algorithm>
+
 #include "dt_reduce.hpp"
 #include "roe_device.hpp"
 #include "swe_internal.hpp"
@@ -102,18 +106,22 @@ __global__ __launch_bounds__(256) void k_edge_flux(int64_t E, EdgeArrays<T> ed, 
     out[(int64_t)(2 * NV) * E + e] = len * speed;
 }
 
+// Blocks of k_cell_dt at most: every block ends in one atomic min on the
+// same address, and one per 256 cells serialised them (65,536 per step on a
+// 4096^2 grid).
+constexpr int64_t DT_BLOCKS = 1024;
+
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void k_cell_dt(int64_t N, int64_t E, const int32_t *__restrict__ off,
                                                  const int32_t *__restrict__ ce, const T *__restrict__ area,
                                                  const T *__restrict__ out, T cfl, double *slot)
 {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const T *sp = out + (int64_t)(2 * NV) * E;
     double dti = __builtin_inf();
-    if (c < N) {
-        const T *sp = out + (int64_t)(2 * NV) * E;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < N; c += (int64_t)gridDim.x * blockDim.x) {
         T S = T(0);
         for (int32_t k = off[c]; k < off[c + 1]; ++k) S += sp[ce[k] >> 1];
-        dti = (double)(T(2) * cfl * area[c] / S);
+        dti = fmin(dti, (double)(T(2) * cfl * area[c] / S));
     }
     block_min_to_slot(dti, slot);
 }
@@ -192,9 +200,10 @@ static hipError_t edge_step_t(swe_ctx *c, int64_t step, double cfl)
     StatePtrs<T> W = state_ptrs<T>(c);
     T *out = (T *)c->e_out;
     const dim3 ge((unsigned)((c->E + bs - 1) / bs)), gc((unsigned)((c->N + bs - 1) / bs));
+    const dim3 gd((unsigned)std::min<int64_t>((c->N + bs - 1) / bs, DT_BLOCKS));
     hipLaunchKernelGGL((k_edge_flux<T, NL, TR, FX>), ge, dim3(bs), 0, c->stream, c->E, ed, W,
                        (const T *)c->zbed, (T)c->g, (T)c->r, out, c->book.flags);
-    hipLaunchKernelGGL((k_cell_dt<T, NV>), gc, dim3(bs), 0, c->stream, c->N, c->E, c->c_off, c->c_edge,
+    hipLaunchKernelGGL((k_cell_dt<T, NV>), gd, dim3(bs), 0, c->stream, c->N, c->E, c->c_off, c->c_edge,
                        (const T *)c->c_area, (const T *)out, (T)cfl, c->book.slots + (step % 3));
     hipLaunchKernelGGL((k_cell_update<T, NV>), gc, dim3(bs), 0, c->stream, c->N, c->E, c->c_off,
                        c->c_edge, (const T *)c->c_iarea, (const T *)out, W, c->book, step, c->nlayers);

@@ -69,7 +69,8 @@ template <typename T, bool TR> struct CartArgs {
     int per_xcd;   // tiles per XCD band
     double *part;  // [3][NPART] partial minima
     StepBook book;
-    int64_t step;
+    int64_t step;  // index of the step within the batch (dt history)
+    int bank0;     // partial-minimum bank of the batch's first step
 };
 
 // ---------------------------------------------------------------- math
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     const int tile = (w % NUM_XCD) * A.per_xcd + w / NUM_XCD;
 
     // dt^n from the partial minima of the previous launch
-    const int bank = (int)(A.step % 3);
+    const int bank = (int)((A.step + A.bank0) % 3);
     double dtd = A.part[bank * NPART + lane];
     dtd = wave_min(dtd);
     if (w == 0) {
@@ -669,10 +670,14 @@ __global__ __launch_bounds__(256) void k_cart_dt0(const T *__restrict__ h, const
     }
 }
 
-__global__ void k_cart_init(double *part, StepBook book)
+// Batch start: elapsed time and error flags to zero; the partial minima
+// too when the batch starts from a fresh state (else the previous batch's
+// last launch left dt of the current state in bank bank0).
+__global__ void k_cart_init(double *part, StepBook book, int reset_part)
 {
     const int t = threadIdx.x;
-    for (int k = t; k < 3 * NPART; k += blockDim.x) part[k] = __builtin_inf();
+    if (reset_part)
+        for (int k = t; k < 3 * NPART; k += blockDim.x) part[k] = __builtin_inf();
     if (t == 0) {
         book.t[0] = 0.0;
         book.flags[0] = 0u;
@@ -712,20 +717,27 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     A.part = c->cart_part;
     A.book = c->book;
     A.step = step;
+    A.bank0 = c->bank0;
     return A;
 }
 
 template <typename T, bool TR, int FX = FLUX_IR, bool RC = false>
 static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
 {
-    hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
-    const T *src = (const T *)c->state[c->cur];
-    const int64_t N = c->N;
-    const unsigned nb0 = (unsigned)((N + 255) / 256);
-    hipLaunchKernelGGL((k_cart_dt0<T>), dim3(nb0), dim3(256), 0, c->stream, src, src + N, src + 2 * N,
-                       (int)c->nx, (int)c->ny, (int)(c->bc_x == SWE_BC_PERIODIC),
-                       (int)(c->bc_y == SWE_BC_PERIODIC), (T)c->dx, (T)c->dy, (T)c->g, (T)cfl,
-                       c->cart_part);
+    // dt of the current state: left by the previous batch (same state, same
+    // cfl), else computed here into bank 0
+    const bool fresh = !c->dt_ready || c->dt_cfl != cfl;
+    if (fresh) c->bank0 = 0;
+    hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book, fresh ? 1 : 0);
+    if (fresh) {
+        const T *src = (const T *)c->state[c->cur];
+        const int64_t N = c->N;
+        const unsigned nb0 = (unsigned)((N + 255) / 256);
+        hipLaunchKernelGGL((k_cart_dt0<T>), dim3(nb0), dim3(256), 0, c->stream, src, src + N, src + 2 * N,
+                           (int)c->nx, (int)c->ny, (int)(c->bc_x == SWE_BC_PERIODIC),
+                           (int)(c->bc_y == SWE_BC_PERIODIC), (T)c->dx, (T)c->dy, (T)c->g, (T)cfl,
+                           c->cart_part);
+    }
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
         const unsigned grid = (unsigned)(A.per_xcd * NUM_XCD);

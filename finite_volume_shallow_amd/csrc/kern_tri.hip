@@ -47,7 +47,8 @@ template <typename T> struct TriArgs {
     T g, r, cfl;
     double *part;
     StepBook book;
-    int64_t step;
+    int64_t step;  // index of the step within the batch (dt history)
+    int bank0;     // partial-minimum bank of the batch's first step
 };
 
 // Largest |eigenvalue| of the two-layer Roe matrix (the outer roots of the
@@ -288,7 +289,7 @@ k_tri_fused(TriArgs<T> A)
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = blockIdx.x;
     const int blk = (w % TRI_XCD) * A.per_xcd + w / TRI_XCD;
-    const int bank = (int)(A.step % 3);
+    const int bank = (int)((A.step + A.bank0) % 3);
     // the partial minima of dt^n: loaded now, reduced when the update needs
     // them, so their latency overlaps the block's own loads
     const double dpart = DT0 ? 0.0 : A.part[bank * TRI_NPART + lane];
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
     const int xcd = w % TRI_XCD, G = (int)gridDim.x / TRI_XCD;
     const int bend = min((xcd + 1) * A.per_xcd, A.nblocks);
     int blk = xcd * A.per_xcd + w / TRI_XCD;
-    const int bank = (int)(A.step % 3);
+    const int bank = (int)((A.step + A.bank0) % 3);
     const double dpart = A.part[bank * TRI_NPART + lane];
     const T g = A.g, rr = A.r;
     unsigned bad = 0;
@@ -776,10 +777,13 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
     if (w == 0) tri_book(A, bank, tid, dtd);
 }
 
-__global__ void k_tri_init(double *part, StepBook book)
+// Batch start: elapsed time and error flags to zero; the partial minima
+// too when the batch starts from a fresh state (as k_cart_init).
+__global__ void k_tri_init(double *part, StepBook book, int reset_part)
 {
     const int t = threadIdx.x;
-    for (int k = t; k < 3 * TRI_NPART; k += blockDim.x) part[k] = __builtin_inf();
+    if (reset_part)
+        for (int k = t; k < 3 * TRI_NPART; k += blockDim.x) part[k] = __builtin_inf();
     if (t == 0) {
         book.t[0] = 0.0;
         book.flags[0] = 0u;
@@ -841,6 +845,7 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     A.part = c->cart_part;
     A.book = c->book;
     A.step = step;
+    A.bank0 = c->bank0;
     return A;
 }
 
@@ -861,9 +866,14 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book);
-    hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
-                       tri_args<T>(c, 0, cfl));
+    // dt of the current state: left by the previous batch (same state, same
+    // cfl), else computed here into bank 0 (the prologue writes bank 0)
+    const bool fresh = !c->dt_ready || c->dt_cfl != cfl;
+    if (fresh) c->bank0 = 0;
+    hipLaunchKernelGGL(k_tri_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book, fresh ? 1 : 0);
+    if (fresh)
+        hipLaunchKernelGGL((k_tri_fused<T, NL, TR, true, RD, NT>), grid, block, lds, c->stream,
+                           tri_args<T>(c, 0, cfl));
     if constexpr (RD == 1 && !RC) {
         if (c->tb.pipe_wgs != 0) {
             if (lds > 65536) {

@@ -440,6 +440,7 @@ void swe_destroy(swe_ctx *c)
 int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
 {
     if (!c) return SWE_E_INVAL;
+    c->dt_ready = false; // a new state: the next batch computes its dt first
     if (!z || !cons) {
         c->err = "NULL argument";
         return SWE_E_INVAL;
@@ -475,6 +476,7 @@ int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
 int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
 {
     if (!c) return SWE_E_INVAL;
+    c->dt_ready = false;
     if (!z || !cons) {
         c->err = "NULL argument";
         return SWE_E_INVAL;
@@ -544,6 +546,11 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
             if (c->kind == SWE_MESH_CART) HIPTRY(launch_cart_batch(c, nsteps, cfl));
             else HIPTRY(launch_tri_batch(c, nsteps, cfl));
             c->cur ^= (nsteps & 1); // ping-pong: the last launch wrote the other buffer
+            // the last launch left dt of the new state in the next bank: a
+            // following batch with the same cfl starts from it
+            c->bank0 = (int)((c->bank0 + nsteps) % 3);
+            c->dt_ready = true;
+            c->dt_cfl = cfl;
         } else {
             HIPTRY(launch_batch_init(c));
             for (int64_t s = 0; s < nsteps; ++s) HIPTRY(launch_edge_step(c, s, cfl));
@@ -554,6 +561,7 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
         HIPTRY(hipStreamSynchronize(c->stream));
         std::memcpy(&flags, c->h_pinned + 4, sizeof(unsigned));
     } catch (const Fail &f) {
+        c->dt_ready = false;
         return f.code;
     } catch (const std::bad_alloc &) {
         c->err = "out of host memory";
@@ -563,7 +571,10 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
     if (t_adv) *t_adv = c->h_pinned[3];
     if (last_dt) *last_dt = c->h_pinned[5];
     const int st = status_from_flags(flags);
-    if (st != SWE_OK) c->err = swe_strerror(st);
+    if (st != SWE_OK) {
+        c->err = swe_strerror(st);
+        c->dt_ready = false;
+    }
     return st;
 }
 

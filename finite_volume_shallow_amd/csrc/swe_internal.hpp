@@ -103,6 +103,11 @@ struct swe_ctx {
     void *e_out = nullptr; // (2 nv + 1) * E reals
 
     // fused Cartesian path
+    // fused paths: dt of the current state is already in the partial-minimum
+    // bank bank0 when dt_ready (left by the previous batch, for cfl dt_cfl)
+    bool dt_ready = false;
+    int bank0 = 0;
+    double dt_cfl = 0.0;
     int cart_ty = 64;            // rows per tile
     int cart_alt = 0;            // odd row blocks of tiles march downward
     double *cart_part = nullptr; // [3][64] partial dt minima (both fused paths)

@@ -168,7 +168,12 @@ int swe_set_state_device(swe_ctx *ctx, const void *z_bed, const void *const *con
  * taken from the state at the start of each step.  The steps run on the
  * context stream without host round trips; the call returns after the last
  * one finished.  t_advanced (nullable) receives the sum of the dt taken,
- * last_dt (nullable) the last one.  nsteps = 0 is a no-op.
+ * last_dt (nullable) the last one.  nsteps = 0 is a no-op.  Consecutive
+ * calls continue one time stepping: on the fused paths a call with the same
+ * cfl as the previous call starts from the dt that call's last step already
+ * computed for the state it left (no separate dt pass), so n calls of one
+ * step give bit for bit the result of one call of n steps; the first call
+ * after a set_state, or with another cfl, computes dt of the state first.
  * Errors: SWE_E_INVAL for nsteps < 0 or cfl outside (0, 1];
  * SWE_E_NOSTATE before any set_state; SWE_E_DEPTH / SWE_E_NONFINITE /
  * SWE_E_NONHYPERBOLIC when a step produced such a state (the state is then

@@ -571,3 +571,73 @@ def test_degenerate_meshes(case):
     ref, rdts = oracle_reference(w, nsteps=10, precision="f64")
     assert max(field_errors(got, ref)) <= FP64_TOL
     assert np.abs(dts - rdts).max() <= 1e-12 * rdts.max()
+
+
+# Consecutive swe_step calls continue one time stepping: a call with the same
+# cfl starts from the dt the previous call's last step computed, so several
+# calls equal one call of the summed step count bit for bit.
+SPLIT = {"dam-break-64x64": {}, "flow-160x96-f32": {}, "tri-36": {}, "tri-36-per-block": {"SWE_TRI_PIPE": "0"},
+         "two-layer-13": {}, "tri-40-f32": {}}
+
+
+@pytest.mark.parametrize("path", ["auto", "recompute"])
+@pytest.mark.parametrize("name", list(SPLIT))
+def test_consecutive_calls_continue_one_stepping(name, path, monkeypatch):
+    import finite_volume_shallow_amd as swe
+    for k, v in SPLIT[name].items():
+        monkeypatch.setenv(k, v)
+    make, _, prec = CASES[name.replace("-per-block", "")]
+    w = make()
+    p = swe.SWE_PATH_RECOMPUTE if path == "recompute" else swe.SWE_PATH_AUTO
+    say(f"[split calls] {name} path={path}")
+    whole, whole_dts, whole_t = gpu_run(w, nsteps=23, path=p, precision=prec)
+    desc, keep = swe.desc_from_workload(w, path=p, precision=prec)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        swe.swe_set_state(ctx, w.z, w.state)
+        dts, t = [], 0.0
+        for n in (1, 1, 5, 16):
+            t += swe.swe_step(ctx, n, w.cfl)[0]
+            dts.append(swe.swe_get_dt_history(ctx))
+        got = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    assert (np.concatenate(dts) == whole_dts).all()
+    for a, b in zip(got, whole):
+        assert (a == b).all()
+    assert abs(t - whole_t) <= 1e-14 * whole_t
+
+
+@pytest.mark.parametrize("name", ["dam-break-64x64", "tri-36", "flow-160x96-f32"])
+def test_cfl_change_and_new_state_between_calls(name):
+    """A call with another cfl, and a call after a new set_state, start by
+    computing dt of the state they find: matches the oracle run in the same
+    segments."""
+    import finite_volume_shallow_amd as swe
+    make, _, prec = CASES[name]
+    w = make()
+    say(f"[cfl change] {name}")
+    desc, keep = swe.desc_from_workload(w, precision=prec)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        swe.swe_set_state(ctx, w.z, w.state)
+        swe.swe_step(ctx, 10, 0.9)
+        swe.swe_step(ctx, 10, 0.5)
+        seg = swe.swe_get_dt_history(ctx)
+        got = swe.swe_get_state(ctx)
+        # a new state: the next call must not reuse the old dt
+        swe.swe_set_state(ctx, w.z, w.state)
+        swe.swe_step(ctx, 10, 0.9)
+        again = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    w1 = w.copy()
+    w1.cfl = 0.9
+    mid, d1 = oracle_reference(w1, nsteps=10, precision=prec)
+    w2 = w.copy(state=[np.asarray(a, dtype=np.float64) for a in mid], precision="f64")
+    w2.cfl = 0.5
+    ref, d2 = oracle_reference(w2, nsteps=10)
+    tol = FP64_TOL if prec == "f64" else FP32_TOL
+    assert max(field_errors(got, ref, w.g)) <= tol
+    assert np.abs(seg - d2).max() <= (1e-12 if prec == "f64" else 1e-5) * d2.max()
+    assert max(field_errors(again, mid, w.g)) <= tol

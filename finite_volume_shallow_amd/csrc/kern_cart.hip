@@ -623,7 +623,8 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
 }
 
 // Eq. (5) wave speed of an edge between a and b along qn: |u_Roe| + c
-// (IEEE arithmetic; used once per batch for dt of the initial state).
+// (IEEE arithmetic; used for dt of the initial state, in the first batch
+// after a new state or a cfl change).
 template <typename T> __device__ __forceinline__ T roe_speed(T ha, T qa, T hb, T qb, T g)
 {
     const T sa = sqrt(ha), sb = sqrt(hb);

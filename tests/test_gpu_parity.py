@@ -580,7 +580,7 @@ SPLIT = {"dam-break-64x64": {}, "flow-160x96-f32": {}, "tri-36": {}, "tri-36-per
          "two-layer-13": {}, "tri-40-f32": {}}
 
 
-@pytest.mark.parametrize("path", ["auto", "recompute"])
+@pytest.mark.parametrize("path", ["auto", "recompute", "edge"])
 @pytest.mark.parametrize("name", list(SPLIT))
 def test_consecutive_calls_continue_one_stepping(name, path, monkeypatch):
     import finite_volume_shallow_amd as swe
@@ -588,7 +588,7 @@ def test_consecutive_calls_continue_one_stepping(name, path, monkeypatch):
         monkeypatch.setenv(k, v)
     make, _, prec = CASES[name.replace("-per-block", "")]
     w = make()
-    p = swe.SWE_PATH_RECOMPUTE if path == "recompute" else swe.SWE_PATH_AUTO
+    p = {"auto": swe.SWE_PATH_AUTO, "recompute": swe.SWE_PATH_RECOMPUTE, "edge": swe.SWE_PATH_EDGE}[path]
     say(f"[split calls] {name} path={path}")
     whole, whole_dts, whole_t = gpu_run(w, nsteps=23, path=p, precision=prec)
     desc, keep = swe.desc_from_workload(w, path=p, precision=prec)

@@ -159,8 +159,11 @@ int swe_create_mesh(const swe_mesh_desc *desc, swe_ctx **out);
  * Errors: SWE_E_INVAL for NULL pointers; SWE_E_HIP on a copy failure. */
 int swe_set_state(swe_ctx *ctx, const double *z_bed, const double *const *cons);
 
-/* The same from device memory of the context's precision (float or double),
- * caller cell order, ordered on the context stream (no host sync). */
+/* The bed and the state W of [IR] Eq. (1), as swe_set_state, from device
+ * arrays of the context's precision (float or double), caller cell order,
+ * ordered on the context stream (no host sync; the caller keeps its arrays
+ * unchanged until the stream has passed this call).
+ * Errors: SWE_E_INVAL for NULL pointers; SWE_E_HIP. */
 int swe_set_state_device(swe_ctx *ctx, const void *z_bed, const void *const *cons);
 
 /* Advance nsteps explicit steps ([IR] Eq. (4)) with CFL number cfl = gamma
@@ -181,21 +184,29 @@ int swe_set_state_device(swe_ctx *ctx, const void *z_bed, const void *const *con
 int swe_step(swe_ctx *ctx, int32_t nsteps, double cfl, double *t_advanced,
              double *last_dt);
 
-/* Download the conserved state into caller-allocated host arrays of ncells
- * doubles (layout as in swe_set_state).  Synchronous.
+/* Download the conserved state W of [IR] Eq. (1) (after the steps taken so
+ * far, W^n of Eq. (4)) into caller-allocated host arrays of ncells doubles
+ * (layout as in swe_set_state).  Synchronous.
  * Errors: SWE_E_INVAL for NULL pointers; SWE_E_NOSTATE; SWE_E_HIP. */
 int swe_get_state(swe_ctx *ctx, double *const *cons_out);
 
-/* The same into device arrays of the context's precision, ordered on the
- * context stream (no host sync). */
+/* The state W of [IR] Eq. (1), as swe_get_state, into device arrays of the
+ * context's precision (float or double), caller cell order, ordered on the
+ * context stream (no host sync).  The caller owns the arrays; they must hold
+ * ncells values each.
+ * Errors: SWE_E_INVAL for NULL pointers; SWE_E_NOSTATE; SWE_E_HIP. */
 int swe_get_state_device(swe_ctx *ctx, void *const *cons_out);
 
-/* The dt of every step of the last swe_step call, in order.  Copies at most
- * cap values into out and stores the number of steps in *count.
+/* The dt of every step of the last swe_step call, in order: the global
+ * minimum of [IR] Eq. (5) that each step of Eq. (4) used.  Copies at most
+ * cap values into the caller's host array out and stores the number of steps
+ * in *count.
  * Errors: SWE_E_INVAL for NULL pointers or cap < 0; SWE_E_HIP. */
 int swe_get_dt_history(swe_ctx *ctx, double *out, int64_t cap, int64_t *count);
 
-/* Release every resource of the context.  NULL is a no-op. */
+/* Release every resource of the context (the mesh of [IR] Sec. 3 built by
+ * swe_create_mesh, both state copies and the step bookkeeping); waits for the
+ * context's outstanding work first.  NULL is a no-op. */
 void swe_destroy(swe_ctx *ctx);
 
 /* Static description of a status code (never NULL). */
@@ -206,7 +217,9 @@ const char *swe_strerror(int status);
  * swe_create_mesh. */
 const char *swe_last_error(const swe_ctx *ctx);
 
-/* Number of conserved variables per cell (3, 4 or 6); -1 for NULL. */
+/* Number of conserved variables per cell, the components of W in [IR]
+ * Eq. (1): 3 (h, qx, qy), 4 (with the pollutant h c of [MG]) or 6 (two
+ * layers); -1 for NULL. */
 int swe_nvars(const swe_ctx *ctx);
 
 /* Number of cells; -1 for NULL. */

@@ -51,13 +51,38 @@ def gpu_run(w, nsteps=None, path=0, precision=None, stream=None):
     return st, dts, t
 
 
-def oracle_reference(w, nsteps=None, precision=None):
+def oracle_reference(w, nsteps=None, precision=None, chunk=None):
     """Oracle run on the inputs the GPU actually starts from (float32-rounded
-    for a float32 run)."""
+    for a float32 run).  With ``chunk``, the run is taken ``chunk`` steps at
+    a time (each piece restarts from the state the previous one left, so the
+    result is the same) and a progress line is printed after each piece."""
     prec = precision or w.precision
     src = inputs.round_to_f32(w) if prec == "f32" else w
-    st, dts, _ = oracle.run(src, nsteps=nsteps)
-    return st, dts
+    nsteps = w.nsteps if nsteps is None else nsteps
+    if not chunk or chunk >= nsteps:
+        st, dts, _ = oracle.run(src, nsteps=nsteps)
+        return st, dts
+    parts, done, cur = [], 0, src
+    while done < nsteps:
+        k = min(chunk, nsteps - done)
+        st, dts, _ = oracle.run(cur, nsteps=k)
+        parts.append(dts)
+        done += k
+        say(f"    oracle: {done}/{nsteps} steps")
+        cur = cur.copy(state=st)
+    return st, np.concatenate(parts)
+
+
+_ORACLE_CACHE = {}
+
+
+def oracle_reference_cached(key, w, nsteps, precision, chunk=None):
+    """oracle_reference, remembered under ``key`` for the rest of the test
+    session (a long run that several tests compare against is taken once)."""
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = oracle_reference(w, nsteps=nsteps, precision=precision, chunk=chunk)
+    st, dts = _ORACLE_CACHE[key]
+    return [np.array(a, copy=True) for a in st], np.array(dts, copy=True)
 
 
 def fsum(a):

@@ -554,3 +554,20 @@ def test_entropy_fix_with_the_classical_flux_removes_the_expansion_shock():
         res.append((run(0), run(1)))
     assert all(p > 0.1 for p, _ in res)
     assert res[1][1] < 0.6 * res[0][1] and res[2][1] < 0.6 * res[1][1]
+
+
+@pytest.mark.parametrize("layers", [1, 2])
+def test_oracle_in_pieces_equals_one_run(layers):
+    """The long two-layer reference run is taken in pieces (each restarting
+    from the state the previous one left): the pieces give one run's states
+    and time steps bit for bit."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from helpers import oracle_reference
+    w = (inputs.two_layer_dam_break(nq=24, nsteps=10) if layers == 2
+         else inputs.circular_dam_break(nq=24, nsteps=10))
+    st1, dt1 = oracle_reference(w, nsteps=10)
+    st2, dt2 = oracle_reference(w, nsteps=10, chunk=4)
+    assert np.array_equal(dt1, dt2)
+    for a, b in zip(st1, st2):
+        assert np.array_equal(a, b)

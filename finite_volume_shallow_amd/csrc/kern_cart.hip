@@ -597,6 +597,7 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
         A.part[((bank + 2) % 3) * NPART + lane] = __builtin_inf();
         if (lane == 0) {
             A.book.hist[A.step] = dtd;
+            A.book.last[0] = dtd;
             A.book.t[0] += dtd;
         }
     }
@@ -622,53 +623,129 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     if (bad) atomicOr(A.book.flags, bad);
 }
 
-// Eq. (5) wave speed of an edge between a and b along qn: |u_Roe| + c
-// (IEEE arithmetic; used for dt of the initial state, in the first batch
-// after a new state or a cfl change).
-template <typename T> __device__ __forceinline__ T roe_speed(T ha, T qa, T hb, T qb, T g)
+// dt of the initial state (Eq. (5) on W^0), in the first batch after a new
+// state or a cfl change: one wavefront per tile of DT0_COLS columns (lanes
+// 1..DT0_COLS; lanes 0 and 63 are the halo columns) by DT0_ROWS rows,
+// marching up its rows like the fused kernel: a row of each field is one
+// coalesced load, the x-neighbour is the next lane and the y-neighbour the
+// previous row in registers.  Each edge speed is evaluated once, with the
+// arithmetic the fused kernel applies to W^{n+1} (espeed, and sqrt(g h) at a
+// wall), so every step's dt comes from the same formula.  Four wavefronts
+// per workgroup, one atomic min per workgroup into bank 0.
+constexpr int DT0_COLS = 62;
+constexpr int DT0_ROWS = 16;
+constexpr int DT0_WAVES = 4;
+
+struct Dt0Args {
+    const void *h, *qx, *qy;
+    int nx, ny, perx, pery;
+    double dx, dy, g, cfl;
+    int nstrips, ntiles;
+    double *part;
+};
+
+// CHECK: the tile's rows or columns reach beyond the grid (wrap or wall).
+template <typename T, bool CHECK>
+__device__ __forceinline__ T dt0_tile(const Dt0Args &A, int tile, int lane)
 {
-    const T sa = sqrt(ha), sb = sqrt(hb);
-    const T ubar = (qa / sa + qb / sb) / (sa + sb);
-    return fabs(ubar) + sqrt(g * T(0.5) * (ha + hb));
+    const T *H = (const T *)A.h, *QX = (const T *)A.qx, *QY = (const T *)A.qy;
+    const int strip = tile % A.nstrips, rb = tile / A.nstrips;
+    const int i = strip * DT0_COLS - 1 + lane;
+    const int j0 = rb * DT0_ROWS, jend = min(j0 + DT0_ROWS, A.ny);
+    // index inside the grid (periodic) or flagged outside (wall); a tile's
+    // columns may pass a narrow periodic grid more than once
+    auto wrap = [](int c, int n, int per, bool &ok) {
+        ok = true;
+        if (c < 0 || c >= n) {
+            if (per) c = ((c % n) + n) % n;
+            else ok = false;
+        }
+        return c;
+    };
+    bool colok = true, nxtok = true;
+    int col = i;
+    if (CHECK) {
+        col = wrap(i, A.nx, A.perx, colok);
+        (void)wrap(i + 1, A.nx, A.perx, nxtok);
+    }
+    const bool xwall_lane = colok != nxtok; // the lane's right edge is a wall
+    const bool wlane = lane >= 1 && lane <= DT0_COLS && i < A.nx;
+    const T g = (T)A.g, lx = (T)A.dy, ly = (T)A.dx;
+
+    // a row of h, qx, qy for this lane (placeholders outside a wall)
+    struct Row {
+        T h, qx, qy;
+        bool ok;
+    };
+    auto load = [&](int r) {
+        Row w;
+        w.ok = true;
+        int row = r;
+        if (CHECK) row = wrap(r, A.ny, A.pery, w.ok);
+        w.h = T(1);
+        w.qx = w.qy = T(0);
+        if (!CHECK || (w.ok && colok)) {
+            const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
+            w.h = at(H, k);
+            w.qx = at(QX, k);
+            w.qy = at(QY, k);
+        }
+        return w;
+    };
+
+    T smax = T(0);
+    T ph = T(1), ps = T(1), pb = T(0), psx = T(0), pyb = T(0);
+    bool prow = false;
+    // row r of the march (j0-1 .. jend): speeds of its x-edges, the y-edge
+    // below it, and the closed speed sum of row r-1
+    auto step = [&](const Row &w, int r) {
+        const T h = w.h, qx = w.qx, qy = w.qy;
+        const T rq = FM<T>::rsq(h);
+        const T s = h * rq, a = qx * rq, b = qy * rq;
+        const T Nh = nxt(h), Ns = nxt(s), Na = nxt(a);
+        T exs = espeed(h, s, a, Nh, Ns, Na, g);
+        if (CHECK && xwall_lane) exs = FM<T>::sqrt(g * (colok ? h : Nh));
+        const T sx = lx * (exs + prv(exs));
+        if (r >= j0) {
+            // the y-edge (r-1, r): row r-1's top edge and row r's bottom edge
+            T eys;
+            if (!CHECK || (prow && w.ok)) eys = espeed(ph, ps, pb, h, s, b, g);
+            else eys = FM<T>::sqrt(g * (prow ? ph : h));
+            eys *= ly;
+            if (r - 1 >= j0 && wlane) smax = fmax(smax, psx + pyb + eys);
+            pyb = eys;
+        }
+        ph = h;
+        ps = s;
+        pb = b;
+        psx = sx;
+        prow = w.ok;
+    };
+    // every row of the march (j0-1 .. j0+DT0_ROWS) is requested before the
+    // first is used: a short tile's loads are all in flight at once
+    Row w[DT0_ROWS + 2];
+#pragma unroll
+    for (int k = 0; k < DT0_ROWS + 2; ++k) w[k] = load(min(j0 - 1 + k, jend));
+#pragma unroll
+    for (int k = 0; k < DT0_ROWS + 2; ++k)
+        if (j0 - 1 + k <= jend) step(w[k], j0 - 1 + k);
+    return smax;
 }
 
-// dt of the initial state (step 0) into bank 0, one thread per cell.
-template <typename T>
-__global__ __launch_bounds__(256) void k_cart_dt0(const T *__restrict__ h, const T *__restrict__ qx,
-                                                  const T *__restrict__ qy, int nx, int ny, int perx,
-                                                  int pery, T dx, T dy, T g, T cfl, double *part)
+template <typename T> __global__ __launch_bounds__(64 * DT0_WAVES) void k_cart_dt0(Dt0Args A)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    double cand = __builtin_inf();
-    if (k < (int64_t)nx * ny) {
-        const int i = (int)(k % nx), j = (int)(k / nx);
-        const T hk = h[k], qxk = qx[k], qyk = qy[k];
-        T S = T(0);
-        // left, right (length dy) and bottom, top (length dx)
-        for (int s = 0; s < 4; ++s) {
-            int ii = i + (s == 0 ? -1 : s == 1 ? 1 : 0);
-            int jj = j + (s == 2 ? -1 : s == 3 ? 1 : 0);
-            bool ok = true;
-            if (ii < 0 || ii >= nx) { if (perx) ii = (ii + nx) % nx; else ok = false; }
-            if (jj < 0 || jj >= ny) { if (pery) jj = (jj + ny) % ny; else ok = false; }
-            const T len = s < 2 ? dy : dx;
-            if (!ok) { S += len * sqrt(g * hk); continue; }
-            const int64_t m = (int64_t)jj * nx + ii;
-            const T qa = s < 2 ? qxk : qyk, qb = s < 2 ? qx[m] : qy[m];
-            S += len * roe_speed(hk, qa, h[m], qb, g);
-        }
-        cand = (double)(T(2) * cfl * dx * dy / S);
+    const int lane = threadIdx.x & 63;
+    const int tile = blockIdx.x * DT0_WAVES + (threadIdx.x >> 6);
+    T smax = T(0);
+    if (tile < A.ntiles) { // uniform over the wavefront
+        const int strip = tile % A.nstrips, rb = tile / A.nstrips;
+        const int i0 = strip * DT0_COLS - 1, j0 = rb * DT0_ROWS;
+        const bool edge = i0 < 0 || i0 + 64 > A.nx || j0 - 1 < 0 || j0 + DT0_ROWS + 1 > A.ny;
+        smax = edge ? dt0_tile<T, true>(A, tile, lane) : dt0_tile<T, false>(A, tile, lane);
     }
-    __shared__ double red[4];
-    double v = wave_min(cand);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        v = fmin(fmin(red[0], red[1]), fmin(red[2], red[3]));
-        if (v >= 0.0 && v < __builtin_inf())
-            atomicMin(reinterpret_cast<unsigned long long *>(part + (blockIdx.x % NPART)),
-                      (unsigned long long)__double_as_longlong(v));
-    }
+    const T two_cfl_area = T(2) * (T)A.cfl * (T)A.dx * (T)A.dy;
+    const double cand = smax > T(0) ? (double)(two_cfl_area / smax) : __builtin_inf();
+    block_min_to_slot(cand, A.part + (blockIdx.x % NPART));
 }
 
 // Batch start: elapsed time and error flags to zero; the partial minima
@@ -731,13 +808,25 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     if (fresh) c->bank0 = 0;
     hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book, fresh ? 1 : 0);
     if (fresh) {
-        const T *src = (const T *)c->state[c->cur];
-        const int64_t N = c->N;
-        const unsigned nb0 = (unsigned)((N + 255) / 256);
-        hipLaunchKernelGGL((k_cart_dt0<T>), dim3(nb0), dim3(256), 0, c->stream, src, src + N, src + 2 * N,
-                           (int)c->nx, (int)c->ny, (int)(c->bc_x == SWE_BC_PERIODIC),
-                           (int)(c->bc_y == SWE_BC_PERIODIC), (T)c->dx, (T)c->dy, (T)c->g, (T)cfl,
-                           c->cart_part);
+        const char *src = (const char *)c->state[c->cur];
+        const size_t fb = (size_t)c->N * sizeof(T);
+        Dt0Args D;
+        D.h = src;
+        D.qx = src + fb;
+        D.qy = src + 2 * fb;
+        D.nx = (int)c->nx;
+        D.ny = (int)c->ny;
+        D.perx = c->bc_x == SWE_BC_PERIODIC;
+        D.pery = c->bc_y == SWE_BC_PERIODIC;
+        D.dx = c->dx;
+        D.dy = c->dy;
+        D.g = c->g;
+        D.cfl = cfl;
+        D.nstrips = (int)((c->nx + DT0_COLS - 1) / DT0_COLS);
+        D.ntiles = D.nstrips * (int)((c->ny + DT0_ROWS - 1) / DT0_ROWS);
+        D.part = c->cart_part; // bank 0
+        const unsigned nb0 = (unsigned)((D.ntiles + DT0_WAVES - 1) / DT0_WAVES);
+        hipLaunchKernelGGL(k_cart_dt0<T>, dim3(nb0), dim3(64 * DT0_WAVES), 0, c->stream, D);
     }
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);

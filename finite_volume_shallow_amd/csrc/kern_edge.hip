@@ -139,6 +139,7 @@ __global__ __launch_bounds__(256) void k_cell_update(int64_t N, int64_t E, const
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         book.slots[(s + 1) % 3] = __builtin_inf();
         book.hist[step] = dtd;
+        book.last[0] = dtd;
         book.t[0] += dtd;
     }
     if (c >= N) return;

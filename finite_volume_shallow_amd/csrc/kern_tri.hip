@@ -249,6 +249,7 @@ template <typename T> __device__ __forceinline__ void tri_book(const TriArgs<T> 
         A.part[((bank + 2) % 3) * TRI_NPART + tid] = __builtin_inf();
         if (tid == 0) {
             A.book.hist[A.step] = dtd;
+            A.book.last[0] = dtd;
             A.book.t[0] += dtd;
         }
     }

@@ -411,6 +411,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         c->book.slots = bk;
         c->book.t = bk + 3;
         c->book.flags = reinterpret_cast<unsigned *>(bk + 4);
+        c->book.last = bk + 5;
         c->hist_cap = 1024;
         c->book.hist = (double *)dev_alloc(c, c->hist_cap * sizeof(double));
         HIPTRY(hipHostMalloc((void **)&c->h_pinned, 8 * sizeof(double), hipHostMallocDefault));
@@ -555,9 +556,8 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
             HIPTRY(launch_batch_init(c));
             for (int64_t s = 0; s < nsteps; ++s) HIPTRY(launch_edge_step(c, s, cfl));
         }
+        // slots, t, flags and the last dt in one copy
         HIPTRY(hipMemcpyAsync(c->h_pinned, c->book.slots, 8 * sizeof(double), hipMemcpyDeviceToHost, c->stream));
-        HIPTRY(hipMemcpyAsync(c->h_pinned + 5, c->book.hist + (nsteps - 1), sizeof(double),
-                              hipMemcpyDeviceToHost, c->stream));
         HIPTRY(hipStreamSynchronize(c->stream));
         std::memcpy(&flags, c->h_pinned + 4, sizeof(unsigned));
     } catch (const Fail &f) {

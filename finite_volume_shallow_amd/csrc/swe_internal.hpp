@@ -61,11 +61,14 @@ template <typename T> struct StatePtrs {
 };
 
 // Per-batch bookkeeping on the device: three dt slots used round-robin,
-// the accumulated time, error flags and the dt history of the batch.
+// the accumulated time, error flags, the dt of the latest step and the dt
+// history of the batch.  slots, t, flags and last lie in one 8-double
+// record (slots[0..2], t, flags, last) that the host reads back in one copy.
 struct StepBook {
     double *slots;   // [3], non-negative doubles compared as uint64 bits
     double *t;       // [1]
     unsigned *flags; // [1]
+    double *last;    // [1]
     double *hist;    // [hist_cap]
 };
 
@@ -128,7 +131,7 @@ struct swe_ctx {
     } tb;
 
     // step bookkeeping
-    swe::StepBook book{nullptr, nullptr, nullptr, nullptr};
+    swe::StepBook book{nullptr, nullptr, nullptr, nullptr, nullptr};
     int64_t hist_cap = 0, hist_count = 0;
     double *h_pinned = nullptr; // t, last dt, flags
 

@@ -51,19 +51,14 @@ constexpr int NUM_XCD = 8;
 constexpr int NPART = 64;     // partial dt slots per bank
 
 template <typename T, bool TR> struct CartArgs {
-    const T *__restrict__ h;
-    const T *__restrict__ qx;
-    const T *__restrict__ qy;
-    const T *__restrict__ hc;
+    const T *__restrict__ in0, *__restrict__ in1; // W^n: the record planes (cart_plane)
     const T *__restrict__ z;
-    T *__restrict__ oh;
-    T *__restrict__ oqx;
-    T *__restrict__ oqy;
-    T *__restrict__ ohc;
+    T *__restrict__ out0, *__restrict__ out1;     // W^{n+1}, planes as `in`
     int nx, ny, perx, pery;
     T dx, dy, g, cfl;
     int ty;        // rows per tile
     int alt;       // odd row blocks march downward
+    int nt;        // non-temporal state stores (st_w)
     int nstrips;   // tiles across x
     int ntiles;    // tiles in total
     int per_xcd;   // tiles per XCD band
@@ -218,6 +213,99 @@ template <typename T> __device__ __forceinline__ T &at(T *base, uint32_t k)
     return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + (uint32_t)(k * (uint32_t)sizeof(T)));
 }
 
+// The state of a structured grid is stored interleaved, in planes of
+// 16-byte records: float32 cells are one record (h, qx, qy, hc) (or
+// (h, qx, qy), 12 bytes, without the pollutant); float64 cells are a record
+// (h, qx) in plane 0 and (qy, hc) (or qy alone) in plane 1, which starts
+// after the N records of plane 0.  A wavefront's row of a plane is one
+// contiguous access (1 KB with 16-byte records) instead of a separate
+// 256-byte (float32) or 512-byte (float64) piece per variable; the memory
+// system serves the wide accesses markedly faster when thousands of
+// wavefronts march different rows at once.  The bed z stays a plain array.
+// cart_plane (host) lays out the same planes.
+template <typename T, int W> struct CVec {
+    typedef T V __attribute__((ext_vector_type(W)));
+};
+
+// Element k of plane `base` with W reals per record (W = 1, 2 or 4 load as
+// one instruction; W = 3 as three adjacent reals), 32-bit byte offsets.
+template <typename T, int W> __device__ __forceinline__ void ld_w(const T *base, uint32_t k, T (&o)[W])
+{
+    const char *p = reinterpret_cast<const char *>(base) + (uint32_t)(k * (uint32_t)(W * sizeof(T)));
+    if constexpr (W == 2 || W == 4) {
+        const typename CVec<T, W>::V v = *reinterpret_cast<const typename CVec<T, W>::V *>(p);
+#pragma unroll
+        for (int i = 0; i < W; ++i) o[i] = v[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < W; ++i) o[i] = reinterpret_cast<const T *>(p)[i];
+    }
+}
+// NT: a non-temporal store.  W^{n+1} is not read again in the launch that
+// writes it; on grids whose state exceeds the last-level cache, streaming it
+// past the caches pays (a memory-only copy of the 4096^2 march: 108 instead
+// of 121-127 us), while a grid whose two state copies stay cached reads it
+// back faster from the cache in the next launch.
+template <typename T, int W>
+__device__ __forceinline__ void st_w(T *base, uint32_t k, const T (&x)[W], bool nt)
+{
+    char *p = reinterpret_cast<char *>(base) + (uint32_t)(k * (uint32_t)(W * sizeof(T)));
+    if constexpr (W == 2 || W == 4) {
+        typename CVec<T, W>::V v;
+#pragma unroll
+        for (int i = 0; i < W; ++i) v[i] = x[i];
+        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<typename CVec<T, W>::V *>(p));
+        else *reinterpret_cast<typename CVec<T, W>::V *>(p) = v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            if (nt) __builtin_nontemporal_store(x[i], reinterpret_cast<T *>(p) + i);
+            else reinterpret_cast<T *>(p)[i] = x[i];
+        }
+    }
+}
+
+// Cell k of the state (NR = 3 or 4 variables) from / to its planes.
+template <typename T, int NR>
+__device__ __forceinline__ void ld_rec(const T *p0, const T *p1, uint32_t k, T &h, T &qx, T &qy, T &c)
+{
+    if constexpr (sizeof(T) == 4) {
+        T a[NR];
+        ld_w<T, NR>(p0, k, a);
+        h = a[0];
+        qx = a[1];
+        qy = a[2];
+        c = NR == 4 ? a[NR - 1] : T(0);
+    } else {
+        T a[2], b[NR - 2];
+        ld_w<T, 2>(p0, k, a);
+        ld_w<T, NR - 2>(p1, k, b);
+        h = a[0];
+        qx = a[1];
+        qy = b[0];
+        c = NR == 4 ? b[NR - 3] : T(0);
+    }
+}
+template <typename T, int NR>
+__device__ __forceinline__ void st_rec(T *p0, T *p1, uint32_t k, T h, T qx, T qy, T c, bool nt = false)
+{
+    if constexpr (sizeof(T) == 4) {
+        T a[NR];
+        a[0] = h;
+        a[1] = qx;
+        a[2] = qy;
+        if constexpr (NR == 4) a[3] = c;
+        st_w<T, NR>(p0, k, a, nt);
+    } else {
+        const T a[2] = {h, qx};
+        T b[NR - 2];
+        b[0] = qy;
+        if constexpr (NR == 4) b[1] = c;
+        st_w<T, 2>(p0, k, a, nt);
+        st_w<T, NR - 2>(p1, k, b, nt);
+    }
+}
+
 // Load a row of W^n for this lane.  CHECK: the row or the column may lie
 // outside the domain (walls); such cells get benign placeholder values.
 // `row` is the grid row.  The values are raw: a downward-marching tile
@@ -234,10 +322,7 @@ __device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int 
     }
     if (!CHECK || (rowok && colok)) {
         const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
-        h = at(A.h, k);
-        qx = at(A.qx, k);
-        qy = at(A.qy, k);
-        c = TR ? at(A.hc, k) : T(0);
+        ld_rec<T, TR ? 4 : 3>(A.in0, A.in1, k, h, qx, qy, c);
         z = at(A.z, k);
     } else {
         h = T(1);
@@ -457,10 +542,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         const int wr = r - 1;
         if (wr >= K.rs0 && wr < K.rs1 && K.wlane) {
             const uint32_t k = (uint32_t)(DN ? K.rbase - wr : wr) * (uint32_t)A.nx + (uint32_t)K.i;
-            at(A.oh, k) = h1;
-            at(A.oqx, k) = qx1;
-            at(A.oqy, k) = DN ? -qy1 : qy1;
-            if (TR) at(A.ohc, k) = c1;
+            st_rec<T, TR ? 4 : 3>(A.out0, A.out1, k, h1, qx1, DN ? -qy1 : qy1, c1, A.nt);
             bad_depth |= !(h1 > T(0));
             bad_val |= !isfinite(h1 + qx1 + qy1 + c1);
         }
@@ -637,7 +719,7 @@ constexpr int DT0_ROWS = 16;
 constexpr int DT0_WAVES = 4;
 
 struct Dt0Args {
-    const void *h, *qx, *qy;
+    const void *rec0, *rec1; // W^0, the record planes
     int nx, ny, perx, pery;
     double dx, dy, g, cfl;
     int nstrips, ntiles;
@@ -645,10 +727,10 @@ struct Dt0Args {
 };
 
 // CHECK: the tile's rows or columns reach beyond the grid (wrap or wall).
-template <typename T, bool CHECK>
+template <typename T, int NR, bool CHECK>
 __device__ __forceinline__ T dt0_tile(const Dt0Args &A, int tile, int lane)
 {
-    const T *H = (const T *)A.h, *QX = (const T *)A.qx, *QY = (const T *)A.qy;
+    const T *W0 = (const T *)A.rec0, *W1 = (const T *)A.rec1;
     const int strip = tile % A.nstrips, rb = tile / A.nstrips;
     const int i = strip * DT0_COLS - 1 + lane;
     const int j0 = rb * DT0_ROWS, jend = min(j0 + DT0_ROWS, A.ny);
@@ -686,9 +768,8 @@ __device__ __forceinline__ T dt0_tile(const Dt0Args &A, int tile, int lane)
         w.qx = w.qy = T(0);
         if (!CHECK || (w.ok && colok)) {
             const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
-            w.h = at(H, k);
-            w.qx = at(QX, k);
-            w.qy = at(QY, k);
+            T c;
+            ld_rec<T, NR>(W0, W1, k, w.h, w.qx, w.qy, c);
         }
         return w;
     };
@@ -732,7 +813,7 @@ __device__ __forceinline__ T dt0_tile(const Dt0Args &A, int tile, int lane)
     return smax;
 }
 
-template <typename T> __global__ __launch_bounds__(64 * DT0_WAVES) void k_cart_dt0(Dt0Args A)
+template <typename T, int NR> __global__ __launch_bounds__(64 * DT0_WAVES) void k_cart_dt0(Dt0Args A)
 {
     const int lane = threadIdx.x & 63;
     const int tile = blockIdx.x * DT0_WAVES + (threadIdx.x >> 6);
@@ -741,7 +822,7 @@ template <typename T> __global__ __launch_bounds__(64 * DT0_WAVES) void k_cart_d
         const int strip = tile % A.nstrips, rb = tile / A.nstrips;
         const int i0 = strip * DT0_COLS - 1, j0 = rb * DT0_ROWS;
         const bool edge = i0 < 0 || i0 + 64 > A.nx || j0 - 1 < 0 || j0 + DT0_ROWS + 1 > A.ny;
-        smax = edge ? dt0_tile<T, true>(A, tile, lane) : dt0_tile<T, false>(A, tile, lane);
+        smax = edge ? dt0_tile<T, NR, true>(A, tile, lane) : dt0_tile<T, NR, false>(A, tile, lane);
     }
     const T two_cfl_area = T(2) * (T)A.cfl * (T)A.dx * (T)A.dy;
     const double cand = smax > T(0) ? (double)(two_cfl_area / smax) : __builtin_inf();
@@ -766,18 +847,11 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
 {
     CartArgs<T, TR> A;
     const int in = c->cur ^ (int)(step & 1), out = in ^ 1;
-    const T *src = (const T *)c->state[in];
-    T *dst = (T *)c->state[out];
-    const int64_t N = c->N;
-    A.h = src;
-    A.qx = src + N;
-    A.qy = src + 2 * N;
-    A.hc = TR ? src + 3 * N : nullptr;
+    A.in0 = (const T *)c->state[in];
+    A.in1 = A.in0 + cart_plane1(c);
+    A.out0 = (T *)c->state[out];
+    A.out1 = A.out0 + cart_plane1(c);
     A.z = (const T *)c->zbed;
-    A.oh = dst;
-    A.oqx = dst + N;
-    A.oqy = dst + 2 * N;
-    A.ohc = TR ? dst + 3 * N : nullptr;
     A.nx = (int)c->nx;
     A.ny = (int)c->ny;
     A.perx = c->bc_x == SWE_BC_PERIODIC;
@@ -788,6 +862,7 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     A.cfl = (T)cfl;
     A.ty = c->cart_ty;
     A.alt = c->cart_alt;
+    A.nt = c->cart_nt;
     A.nstrips = (int)((c->nx + CART_COLS - 1) / CART_COLS);
     const int nrb = (int)((c->ny + A.ty - 1) / A.ty);
     A.ntiles = A.nstrips * nrb;
@@ -808,12 +883,9 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     if (fresh) c->bank0 = 0;
     hipLaunchKernelGGL(k_cart_init, dim3(1), dim3(64), 0, c->stream, c->cart_part, c->book, fresh ? 1 : 0);
     if (fresh) {
-        const char *src = (const char *)c->state[c->cur];
-        const size_t fb = (size_t)c->N * sizeof(T);
         Dt0Args D;
-        D.h = src;
-        D.qx = src + fb;
-        D.qy = src + 2 * fb;
+        D.rec0 = c->state[c->cur];
+        D.rec1 = (const T *)c->state[c->cur] + cart_plane1(c);
         D.nx = (int)c->nx;
         D.ny = (int)c->ny;
         D.perx = c->bc_x == SWE_BC_PERIODIC;
@@ -826,7 +898,7 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
         D.ntiles = D.nstrips * (int)((c->ny + DT0_ROWS - 1) / DT0_ROWS);
         D.part = c->cart_part; // bank 0
         const unsigned nb0 = (unsigned)((D.ntiles + DT0_WAVES - 1) / DT0_WAVES);
-        hipLaunchKernelGGL(k_cart_dt0<T>, dim3(nb0), dim3(64 * DT0_WAVES), 0, c->stream, D);
+        hipLaunchKernelGGL((k_cart_dt0<T, TR ? 4 : 3>), dim3(nb0), dim3(64 * DT0_WAVES), 0, c->stream, D);
     }
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
@@ -842,6 +914,51 @@ template <int FX, bool RC> static hipError_t cart_batch_fx(swe_ctx *c, int32_t n
     if (c->ntracers)
         return f32 ? cart_batch_t<float, true, FX, RC>(c, nsteps, cfl) : cart_batch_t<double, true, FX, RC>(c, nsteps, cfl);
     return f32 ? cart_batch_t<float, false, FX, RC>(c, nsteps, cfl) : cart_batch_t<double, false, FX, RC>(c, nsteps, cfl);
+}
+
+// The caller's separate arrays (one per variable) <-> the record planes of
+// the structured path, for the device-memory set and get calls.
+template <typename T, int NR>
+__global__ void k_cart_pack(const T *__restrict__ a0, const T *__restrict__ a1, const T *__restrict__ a2,
+                            const T *__restrict__ a3, T *__restrict__ p0, T *__restrict__ p1, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    st_rec<T, NR>(p0, p1, (uint32_t)i, a0[i], a1[i], a2[i], NR == 4 ? a3[i] : T(0));
+}
+template <typename T, int NR>
+__global__ void k_cart_unpack(const T *__restrict__ p0, const T *__restrict__ p1, T *__restrict__ a0,
+                              T *__restrict__ a1, T *__restrict__ a2, T *__restrict__ a3, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    T h, qx, qy, c;
+    ld_rec<T, NR>(p0, p1, (uint32_t)i, h, qx, qy, c);
+    a0[i] = h;
+    a1[i] = qx;
+    a2[i] = qy;
+    if (NR == 4) a3[i] = c;
+}
+
+template <typename T, int NR> static hipError_t cart_pack_t(swe_ctx *c, const void *const *soa, void *rec, int pack)
+{
+    const unsigned nb = (unsigned)((c->N + 255) / 256);
+    T *v[4];
+    for (int k = 0; k < 4; ++k) v[k] = k < NR ? (T *)soa[k] : nullptr;
+    T *p0 = (T *)rec, *p1 = p0 + cart_plane1(c);
+    if (pack)
+        hipLaunchKernelGGL((k_cart_pack<T, NR>), dim3(nb), dim3(256), 0, c->stream, v[0], v[1], v[2], v[3], p0, p1,
+                           c->N);
+    else
+        hipLaunchKernelGGL((k_cart_unpack<T, NR>), dim3(nb), dim3(256), 0, c->stream, p0, p1, v[0], v[1], v[2],
+                           v[3], c->N);
+    return hipGetLastError();
+}
+
+hipError_t launch_cart_pack(swe_ctx *c, const void *const *soa, void *rec, int pack)
+{
+    if (c->prec == SWE_F32) return c->nv == 4 ? cart_pack_t<float, 4>(c, soa, rec, pack) : cart_pack_t<float, 3>(c, soa, rec, pack);
+    return c->nv == 4 ? cart_pack_t<double, 4>(c, soa, rec, pack) : cart_pack_t<double, 3>(c, soa, rec, pack);
 }
 
 hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)

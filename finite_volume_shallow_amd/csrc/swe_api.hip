@@ -118,9 +118,10 @@ template <typename T> void upload_geometry(swe_ctx *c, const HostEdges &h)
 
 // Rows per tile of the fused Cartesian kernel (one 64-lane wavefront per
 // tile of 60 columns) and whether odd row blocks march downward.  Large
-// grids: 12 rows, alternating (measured on 4096^2: the halo rows two
-// neighbouring tiles share are then read close together and served from
-// L2).  Smaller grids: 10 rows, halved while there are fewer than 1024
+// grids: 20 rows, alternating (measured on 4096^2 with the interleaved
+// state: 133.2 us per step against 134.0 at 16 rows, 135.4 at 24 and 138.0
+// at 12; the halo rows two neighbouring tiles share are read close together
+// and served from L2).  Smaller grids: 10 rows, halved while there are fewer than 1024
 // tiles, down to 4.  SWE_CART_TY / SWE_CART_ALT override both (tuning and
 // tests).  With periodic y a tile's march (its rows and two halo rows on
 // either side) wraps once at most, so a tile has fewer rows than the grid.
@@ -133,7 +134,7 @@ void cart_tiling(int64_t nx, int64_t ny, bool pery, int &ty, int &alt)
 {
     const int64_t strips = (nx + 59) / 60;
     if (strips * ((ny + 11) / 12) >= 8192) {
-        ty = 12;
+        ty = 20;
         alt = 1;
     } else {
         ty = 10;
@@ -278,13 +279,16 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             }
             c->path = SWE_PATH_RECOMPUTE;
         }
-        // the fused kernel addresses a field with 32-bit byte offsets
+        // the fused kernel addresses the state (nv interleaved reals per
+        // cell) and the bed with 32-bit byte offsets
         if (d->mesh_kind == SWE_MESH_CART &&
             (d->nx > (int64_t)1 << 30 || d->ny > (int64_t)1 << 30 ||
-             d->nx * d->ny * (d->precision == SWE_F32 ? 4 : 8) >= (int64_t)1 << 32)) {
+             (double)d->nx * (double)d->ny * (d->precision == SWE_F32 ? 4 : 8) *
+                     (c->path == SWE_PATH_EDGE ? 1 : c->nv) >= 4294967296.0)) {
             c->err = "grid too large";
             throw Fail{SWE_E_INVAL};
         }
+        c->interleaved = d->mesh_kind == SWE_MESH_CART && c->path != SWE_PATH_EDGE;
         c->N = d->mesh_kind == SWE_MESH_CART ? d->nx * d->ny : d->ncells;
 
         // host-side mesh work first: mesh errors are reported without
@@ -395,6 +399,12 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         } else if (d->mesh_kind == SWE_MESH_CART) {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             cart_tiling(d->nx, d->ny, d->bc_y == SWE_BC_PERIODIC, c->cart_ty, c->cart_alt);
+            // non-temporal state stores where the two state copies and the
+            // bed exceed the 256 MB last-level cache (measured: 4096^2 float32,
+            // 604 MB, 133.2 -> 131.0 us per step; 1024^2 float64, 75 MB,
+            // 24.1 -> 25.7 us)
+            c->cart_nt = (double)c->N * c->rs * (2 * c->nv + 1) > 256.0 * (1 << 20);
+            if (const char *e = std::getenv("SWE_CART_NT")) c->cart_nt = std::atoi(e) != 0;
         } else {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             if (c->prec == SWE_F32) upload_blocks<float>(c, hb);
@@ -461,8 +471,15 @@ int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
             return tmp.data();
         };
         upload_real(c, c->zbed, ordered(z), c->N);
-        for (int v = 0; v < c->nv; ++v)
-            upload_real(c, (char *)c->state[0] + (size_t)v * c->N * c->rs, ordered(cons[v]), c->N);
+        if (c->interleaved) { // record planes (cart_plane_offset)
+            std::vector<double> rec((size_t)c->nv * c->N);
+            for (int64_t i = 0; i < c->N; ++i)
+                for (int v = 0; v < c->nv; ++v) rec[cart_plane_offset(c, v, i)] = cons[v][i];
+            upload_real(c, c->state[0], rec.data(), (int64_t)c->nv * c->N);
+        } else {
+            for (int v = 0; v < c->nv; ++v)
+                upload_real(c, (char *)c->state[0] + (size_t)v * c->N * c->rs, ordered(cons[v]), c->N);
+        }
     } catch (const Fail &f) {
         return f.code;
     } catch (const std::bad_alloc &) {
@@ -496,9 +513,13 @@ int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
                 HIPTRY(launch_permute(c, cons[v], (char *)c->state[0] + v * bytes, 1));
         } else {
             HIPTRY(hipMemcpyAsync(c->zbed, z, bytes, hipMemcpyDeviceToDevice, c->stream));
-            for (int v = 0; v < c->nv; ++v)
-                HIPTRY(hipMemcpyAsync((char *)c->state[0] + v * bytes, cons[v], bytes, hipMemcpyDeviceToDevice,
-                                      c->stream));
+            if (c->interleaved) {
+                HIPTRY(launch_cart_pack(c, cons, c->state[0], 1));
+            } else {
+                for (int v = 0; v < c->nv; ++v)
+                    HIPTRY(hipMemcpyAsync((char *)c->state[0] + v * bytes, cons[v], bytes, hipMemcpyDeviceToDevice,
+                                          c->stream));
+            }
         }
     } catch (const Fail &f) {
         return f.code;
@@ -598,6 +619,22 @@ int swe_get_state(swe_ctx *c, double *const *out)
         const char *base = (const char *)c->state[c->cur];
         std::vector<double> d64;
         std::vector<float> f32;
+        if (c->interleaved) { // record planes (cart_plane_offset)
+            const size_t n = (size_t)c->nv * c->N;
+            d64.resize(n);
+            if (c->prec == SWE_F64) {
+                HIPTRY(hipMemcpyAsync(d64.data(), base, n * 8, hipMemcpyDeviceToHost, c->stream));
+                HIPTRY(hipStreamSynchronize(c->stream));
+            } else {
+                f32.resize(n);
+                HIPTRY(hipMemcpyAsync(f32.data(), base, n * 4, hipMemcpyDeviceToHost, c->stream));
+                HIPTRY(hipStreamSynchronize(c->stream));
+                for (size_t i = 0; i < n; ++i) d64[i] = f32[i];
+            }
+            for (int64_t i = 0; i < c->N; ++i)
+                for (int v = 0; v < c->nv; ++v) out[v][i] = d64[cart_plane_offset(c, v, i)];
+            return SWE_OK;
+        }
         for (int v = 0; v < c->nv; ++v) {
             const double *src;
             if (c->prec == SWE_F64) {
@@ -647,6 +684,10 @@ int swe_get_state_device(swe_ctx *c, void *const *out)
     }
     try {
         const size_t bytes = (size_t)c->N * c->rs;
+        if (c->interleaved) {
+            HIPTRY(launch_cart_pack(c, (const void *const *)out, c->state[c->cur], 0));
+            return SWE_OK;
+        }
         for (int v = 0; v < c->nv; ++v) {
             const char *src = (const char *)c->state[c->cur] + v * bytes;
             if (c->perm) HIPTRY(launch_permute(c, src, out[v], 0));

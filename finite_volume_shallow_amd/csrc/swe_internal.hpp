@@ -92,8 +92,11 @@ struct swe_ctx {
     std::string err;
     bool has_state = false;
 
-    // state: two SoA copies (ping-pong), nv arrays of N reals each
+    // state: two copies (ping-pong) of nv * N reals each: nv arrays of N
+    // reals (edge and triangle paths), or N interleaved records of nv reals
+    // (fused structured path, `interleaved`)
     void *state[2] = {nullptr, nullptr};
+    bool interleaved = false;
     int cur = 0;
     void *zbed = nullptr;
 
@@ -113,6 +116,7 @@ struct swe_ctx {
     double dt_cfl = 0.0;
     int cart_ty = 64;            // rows per tile
     int cart_alt = 0;            // odd row blocks of tiles march downward
+    int cart_nt = 0;             // non-temporal state stores
     double *cart_part = nullptr; // [3][64] partial dt minima (both fused paths)
 
     // fused triangle path: cells in internal (Morton) order
@@ -146,7 +150,24 @@ hipError_t launch_edge_step(swe_ctx *c, int64_t step, double cfl);
 hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl);
 hipError_t launch_tri_batch(swe_ctx *c, int32_t nsteps, double cfl);
 hipError_t launch_permute(swe_ctx *c, const void *src, void *dst, int to_internal);
+// Structured fused path: pack = 1 interleaves the nv device arrays soa[] into
+// the record planes at rec (cart_plane); pack = 0 splits them.
+hipError_t launch_cart_pack(swe_ctx *c, const void *const *soa, void *rec, int pack);
+
+// Record planes of the structured fused path: float32, one plane of nv
+// reals per cell; float64, plane 0 holds (h, qx) and plane 1 the remaining
+// nv - 2 reals per cell.  Offset, in reals from the state's start, of
+// variable v of cell k, and the start of plane 1.
+inline int64_t cart_plane1(const swe_ctx *c);
+inline int64_t cart_plane_offset(const swe_ctx *c, int v, int64_t k);
 size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max);
 int tri_edge_rec(int nv);
 
 } // namespace swe
+
+inline int64_t swe::cart_plane1(const swe_ctx *c) { return c->rs == 4 ? 0 : 2 * c->N; }
+inline int64_t swe::cart_plane_offset(const swe_ctx *c, int v, int64_t k)
+{
+    if (c->rs == 4) return k * c->nv + v;
+    return v < 2 ? 2 * k + v : 2 * c->N + k * (c->nv - 2) + (v - 2);
+}

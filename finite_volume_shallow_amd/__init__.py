@@ -47,7 +47,9 @@ class swe_mesh_desc(ctypes.Structure):
     ]
 
 
-EXPORTS = ["swe_create_mesh", "swe_set_state", "swe_set_state_device", "swe_step",
+SWE_NOALLOC_MAX_STEPS = 1024
+
+EXPORTS = ["swe_create_mesh", "swe_set_state", "swe_set_state_device", "swe_step", "swe_step_noalloc",
            "swe_get_state", "swe_get_state_device", "swe_get_dt_history", "swe_destroy",
            "swe_strerror", "swe_last_error", "swe_nvars", "swe_ncells", "swe_path"]
 
@@ -66,6 +68,7 @@ def _load():
     L.swe_set_state.argtypes = [P, _D, ctypes.POINTER(_D)]
     L.swe_set_state_device.argtypes = [P, P, ctypes.POINTER(P)]
     L.swe_step.argtypes = [P, ctypes.c_int32, ctypes.c_double, _D, _D]
+    L.swe_step_noalloc.argtypes = [P, ctypes.c_int32, ctypes.c_double, _D, _D]
     L.swe_get_state.argtypes = [P, ctypes.POINTER(_D)]
     L.swe_get_state_device.argtypes = [P, ctypes.POINTER(P)]
     L.swe_get_dt_history.argtypes = [P, _D, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
@@ -155,6 +158,15 @@ def swe_step(ctx, nsteps, cfl):
     t = ctypes.c_double()
     d = ctypes.c_double()
     _check(_lib.swe_step(ctx, int(nsteps), float(cfl), ctypes.byref(t), ctypes.byref(d)), ctx)
+    return t.value, d.value
+
+
+def swe_step_noalloc(ctx, nsteps, cfl):
+    """swe_step without any allocation (at most SWE_NOALLOC_MAX_STEPS steps);
+    returns (t_advanced, last_dt)."""
+    t = ctypes.c_double()
+    d = ctypes.c_double()
+    _check(_lib.swe_step_noalloc(ctx, int(nsteps), float(cfl), ctypes.byref(t), ctypes.byref(d)), ctx)
     return t.value, d.value
 
 

@@ -3,6 +3,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -201,6 +202,52 @@ void free_all(swe_ctx *c)
     c->stream = nullptr;
 }
 
+// ---- scratch of swe_step_noalloc
+// The per-batch bookkeeping of a batch that swe_step_noalloc runs: three
+// banks of 64 partial dt minima, the 8-double step record (dt slots, time,
+// flags, last dt) and the dt history of up to SWE_NOALLOC_MAX_STEPS steps,
+// in a file-scope device array (about 9.6 KB per GPU, held until the
+// process ends).  Host code never passes `scratch` itself to a kernel or a
+// copy: its name is a host-side stand-in.  The device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept in g_scratch_dev.
+constexpr int NA_PART = 3 * 64;
+constexpr int NA_BOOK = 8;
+constexpr int NA_DOUBLES = NA_PART + NA_BOOK + SWE_NOALLOC_MAX_STEPS;
+static __device__ __align__(256) double scratch[NA_DOUBLES];
+
+std::mutex g_scratch_mu;
+std::vector<double *> g_scratch_dev; // per device id; nullptr until taken
+
+// The device address of `scratch` on the current device (cached per device).
+hipError_t scratch_address(int device, double **out)
+{
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (device < 0) return hipErrorInvalidDevice;
+    if ((size_t)device >= g_scratch_dev.size()) g_scratch_dev.resize((size_t)device + 1, nullptr);
+    if (!g_scratch_dev[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_dev[device] = static_cast<double *>(p);
+    }
+    *out = g_scratch_dev[device];
+    return hipSuccess;
+}
+
+// n doubles from src to dst, ordered on the stream (a kernel rather than a
+// memory copy node, so that a captured graph holds kernels only).
+__global__ void k_copy_doubles(const double *__restrict__ src, double *__restrict__ dst, int n)
+{
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+}
+
+hipError_t copy_doubles(hipStream_t st, const double *src, double *dst, int n)
+{
+    hipLaunchKernelGGL(k_copy_doubles, dim3(1), dim3(256), 0, st, src, dst, n);
+    return hipGetLastError();
+}
+
 int status_from_flags(unsigned f)
 {
     if (f & FLAG_NONHYPERBOLIC) return SWE_E_NONHYPERBOLIC;
@@ -376,6 +423,10 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         }
 
         HIPTRY(hipGetDevice(&c->device));
+        // the scratch of swe_step_noalloc on this device (its address is
+        // taken here, with the device current, so the call itself needs
+        // no set-up)
+        HIPTRY(scratch_address(c->device, &c->na_scratch));
         if (d->hip_stream) {
             c->stream = (hipStream_t)d->hip_stream;
         } else {
@@ -532,11 +583,24 @@ int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
     return SWE_OK;
 }
 
-int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last_dt)
+} // extern "C"
+
+namespace {
+
+// The batch of swe_step and swe_step_noalloc.  With `na`, the batch's
+// bookkeeping lives in the scratch array instead of the context's own
+// buffers: the context's partial-minimum banks (dt of the current state,
+// fused paths) are copied in first, and the banks and the dt history are
+// copied back afterwards, so the context continues exactly as after
+// swe_step; nothing is allocated.
+int run_batch(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last_dt, bool na)
 {
-    if (!c) return SWE_E_INVAL;
     if (nsteps < 0 || !(cfl > 0.0 && cfl <= 1.0)) {
         c->err = "nsteps must be >= 0 and cfl in (0, 1]";
+        return SWE_E_INVAL;
+    }
+    if (na && nsteps > SWE_NOALLOC_MAX_STEPS) {
+        c->err = "swe_step_noalloc takes at most " + std::to_string(SWE_NOALLOC_MAX_STEPS) + " steps per call";
         return SWE_E_INVAL;
     }
     if (!c->has_state) {
@@ -548,8 +612,11 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
     c->hist_count = 0;
     if (nsteps == 0) return SWE_OK;
     unsigned flags = 0;
+    const StepBook own_book = c->book;
+    double *const own_part = c->cart_part;
+    const bool fused = c->path != SWE_PATH_EDGE;
     try {
-        if (nsteps > c->hist_cap) {
+        if (!na && nsteps > c->hist_cap) {
             int64_t cap = c->hist_cap;
             while (cap < nsteps) cap *= 2;
             HIPTRY(hipStreamSynchronize(c->stream));
@@ -564,7 +631,13 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
                 }
             c->hist_cap = cap;
         }
-        if (c->path != SWE_PATH_EDGE) { // fused (or its recomputation variant)
+        if (na) {
+            double *sp = c->na_scratch, *sb = sp + NA_PART;
+            if (fused) HIPTRY(copy_doubles(c->stream, own_part, sp, NA_PART));
+            c->book = StepBook{sb, sb + 3, reinterpret_cast<unsigned *>(sb + 4), sb + 5, sb + NA_BOOK};
+            if (fused) c->cart_part = sp;
+        }
+        if (fused) { // fused (or its recomputation variant)
             if (c->kind == SWE_MESH_CART) HIPTRY(launch_cart_batch(c, nsteps, cfl));
             else HIPTRY(launch_tri_batch(c, nsteps, cfl));
             c->cur ^= (nsteps & 1); // ping-pong: the last launch wrote the other buffer
@@ -577,17 +650,27 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
             HIPTRY(launch_batch_init(c));
             for (int64_t s = 0; s < nsteps; ++s) HIPTRY(launch_edge_step(c, s, cfl));
         }
+        if (na) { // the banks and the history back into the context
+            if (fused) HIPTRY(copy_doubles(c->stream, c->cart_part, own_part, NA_PART));
+            HIPTRY(copy_doubles(c->stream, c->book.hist, own_book.hist, nsteps));
+        }
         // slots, t, flags and the last dt in one copy
         HIPTRY(hipMemcpyAsync(c->h_pinned, c->book.slots, 8 * sizeof(double), hipMemcpyDeviceToHost, c->stream));
         HIPTRY(hipStreamSynchronize(c->stream));
         std::memcpy(&flags, c->h_pinned + 4, sizeof(unsigned));
     } catch (const Fail &f) {
+        c->book = own_book;
+        c->cart_part = own_part;
         c->dt_ready = false;
         return f.code;
     } catch (const std::bad_alloc &) {
+        c->book = own_book;
+        c->cart_part = own_part;
         c->err = "out of host memory";
         return SWE_E_NOMEM;
     }
+    c->book = own_book;
+    c->cart_part = own_part;
     c->hist_count = nsteps;
     if (t_adv) *t_adv = c->h_pinned[3];
     if (last_dt) *last_dt = c->h_pinned[5];
@@ -597,6 +680,22 @@ int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last
         c->dt_ready = false;
     }
     return st;
+}
+
+} // namespace
+
+extern "C" {
+
+int swe_step(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last_dt)
+{
+    if (!c) return SWE_E_INVAL;
+    return run_batch(c, nsteps, cfl, t_adv, last_dt, false);
+}
+
+int swe_step_noalloc(swe_ctx *c, int32_t nsteps, double cfl, double *t_adv, double *last_dt)
+{
+    if (!c) return SWE_E_INVAL;
+    return run_batch(c, nsteps, cfl, t_adv, last_dt, true);
 }
 
 int swe_get_state(swe_ctx *c, double *const *out)

@@ -138,6 +138,7 @@ struct swe_ctx {
     swe::StepBook book{nullptr, nullptr, nullptr, nullptr, nullptr};
     int64_t hist_cap = 0, hist_count = 0;
     double *h_pinned = nullptr; // t, last dt, flags
+    double *na_scratch = nullptr; // device address of swe_step_noalloc's scratch on this device
 
     std::vector<void *> allocs; // every device allocation, freed on destroy
 };

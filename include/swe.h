@@ -184,6 +184,22 @@ int swe_set_state_device(swe_ctx *ctx, const void *z_bed, const void *const *con
 int swe_step(swe_ctx *ctx, int32_t nsteps, double cfl, double *t_advanced,
              double *last_dt);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): swe_step without
+ * any allocation.  Same arguments, results and errors as swe_step (the
+ * same kernels, bit for bit, and the context continues exactly as after
+ * swe_step: swe_get_dt_history, a following swe_step or swe_step_noalloc).
+ * The batch's bookkeeping (partial dt minima, time, error flags, dt history)
+ * lives in one static device array per GPU (about 9.6 KB, held until the
+ * process ends) instead of buffers of the context, and the call makes no
+ * hipMalloc / hipFree or other allocating call.  nsteps must not exceed
+ * SWE_NOALLOC_MAX_STEPS (else SWE_E_INVAL, nothing run).  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * threads, or contexts on streams that run concurrently) race and must be
+ * serialised by the caller. */
+#define SWE_NOALLOC_MAX_STEPS 1024
+int swe_step_noalloc(swe_ctx *ctx, int32_t nsteps, double cfl, double *t_advanced, double *last_dt);
+
 /* Download the conserved state W of [IR] Eq. (1) (after the steps taken so
  * far, W^n of Eq. (4)) into caller-allocated host arrays of ncells doubles
  * (layout as in swe_set_state).  Synchronous.

@@ -114,10 +114,15 @@ template <typename T> __device__ __forceinline__ PC<T> prep(T h, T qx, T qy, T c
     return p;
 }
 
-// Fluctuations of one edge for its two cells, in the edge frame:
-// mass, normal momentum, transverse momentum, pollutant.
+// One edge, in the edge frame.  Mass and normal momentum as fluctuations
+// of its two cells (a: the cell on the normal's tail, b: its head), so that
+// float32 keeps the differences exactly that the large hydrostatic terms
+// would swamp; the transverse momentum and the pollutant as the flux through
+// the edge (ft, fc), which both cells share (a cell's own-state terms cancel
+// over its two edges of a direction, and these rows carry no hydrostatic
+// term).
 template <typename T> struct EF {
-    T am, an, at, ac, bm, bn, bt, bc;
+    T am, an, bm, bn, ft, fc;
 };
 
 // Interior edge, states given in the edge frame (qn, un normal; ut
@@ -154,44 +159,36 @@ __device__ __forceinline__ EF<T> flux(T hL, T sL, T qL, T uL, T tL, T cL, T zL, 
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
     if (flux_classical(FX)) {
+        // the contact waves: F_t(W_a) + (P^- X)_t
         const T wu = wminus(ubar);
         const T vbar = (sL * tL + sR * tR) * isum;
-        const T Xt = qR * tR - qL * tL;
-        o.at = vbar * pm0 + wu * (Xt - vbar * X0);
-        o.bt = Xt - o.at;
+        const T Ft = qL * tL;
+        o.ft = Ft + (vbar * pm0 + wu * ((qR * tR - Ft) - vbar * X0));
         if (TR) {
             const T cbar = (sL * cL + sR * cR) * isum;
-            const T Xc = qR * cR - qL * cL;
-            o.ac = cbar * pm0 + wu * (Xc - cbar * X0);
-            o.bc = Xc - o.ac;
+            const T Fc = qL * cL;
+            o.fc = Fc + (cbar * pm0 + wu * ((qR * cR - Fc) - cbar * X0));
         } else {
-            o.ac = o.bc = T(0);
+            o.fc = T(0);
         }
         return o;
     }
+    // carried by the mass flux phi0, upwinded by its sign
     const T phi0 = qL + pm0;
     const bool up = phi0 > T(0);
-    o.at = up ? pm0 * tL : phi0 * tR - qL * tL;
-    o.bt = up ? qR * tR - phi0 * tL : o.bm * tR;
-    if (TR) {
-        o.ac = up ? pm0 * cL : phi0 * cR - qL * cL;
-        o.bc = up ? qR * cR - phi0 * cL : o.bm * cR;
-    } else {
-        o.ac = o.bc = T(0);
-    }
+    o.ft = phi0 * (up ? tL : tR);
+    o.fc = TR ? phi0 * (up ? cL : cR) : T(0);
     return o;
 }
 
-// Reflective wall seen from the cell (edge frame, outward normal): mass,
-// transverse and pollutant fluxes are zero, the normal momentum gets the
-// mirror-problem term sqrt(g h) qn.
-template <typename T>
-__device__ __forceinline__ void wall(T h, T qn, T ut, T cc, T g, T &m, T &n, T &t, T &c)
+// Reflective wall seen from the cell (edge frame, outward normal): the mass,
+// transverse and pollutant fluxes are zero (the mass fluctuation is -qn and
+// ft = fc = 0 at the wall), the normal momentum gets the mirror-problem term
+// sqrt(g h) qn.
+template <typename T> __device__ __forceinline__ void wall(T h, T qn, T g, T &m, T &n)
 {
     m = -qn;
     n = FM<T>::sqrt(g * h) * qn;
-    t = -qn * ut;
-    c = -qn * cc;
 }
 
 // Eq. (5) speed |u_Roe| + c of an edge from per-cell s = sqrt(h) and
@@ -335,7 +332,7 @@ template <typename T> struct Carry {
     PC<T> prev;                  // W^n of row r-1
     bool prevrow;                // row r-1 inside the domain (uniform)
     T ax_m, ax_x, ax_y, ax_c;    // x-edge fluctuation sums of row r-1
-    T yb_m, yb_n, yb_t, yb_c;    // its bottom y-edge part (edge frame)
+    T yb_m, yb_n, yb_t, yb_c;    // its bottom y-edge: mass, normal parts; transverse, pollutant fluxes
     T np_h, np_s, np_b;          // W^{n+1} of row r-2: h, sqrt(h), qy / sqrt(h)
     bool nprow;                  // row r-2 inside the domain
     T sx_prev, sybot_prev;       // Eq. (5) speed sums of row r-2 (x-edges, bottom edge)
@@ -383,7 +380,7 @@ constexpr int PREFETCH = 2;
 template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC>
 __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
-                                         bool &bad_depth, bool &bad_val)
+                                         uint64_t &bad_depth, uint64_t &bad_val)
 {
     // the row PREFETCH ahead is requested before anything waits on row r
     if (r + PREFETCH <= K.rlast)
@@ -399,18 +396,17 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
             Rz = nxt(cur.z), Rq = nxt(cur.qx);
     EF<T> ex = flux<T, TR, FX>(cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, Rh, Rs, Rq, Ru, Rv, Rc, Rz, g);
     if (XW && K.xwall_lane) {
+        ex.ft = ex.fc = T(0);
         if (K.colok) { // wall on the right of this lane's cell
-            wall(cur.h, cur.qx, cur.v, cur.cc, g, ex.am, ex.an, ex.at, ex.ac);
-            ex.bm = ex.bn = ex.bt = ex.bc = T(0);
-        } else { // wall on the left of the next lane's cell: qn = -qx, ut = -v;
-                 // back-rotation (m, n, t, c) -> (m, -n, -t, c)
-            T m, n, t, c;
-            wall(Rh, -Rq, -Rv, Rc, g, m, n, t, c);
-            ex.am = ex.an = ex.at = ex.ac = T(0);
+            wall(cur.h, cur.qx, g, ex.am, ex.an);
+            ex.bm = ex.bn = T(0);
+        } else { // wall on the left of the next lane's cell: qn = -qx;
+                 // back-rotation of the normal momentum n -> -n
+            T m, n;
+            wall(Rh, -Rq, g, m, n);
+            ex.am = ex.an = T(0);
             ex.bm = m;
             ex.bn = -n;
-            ex.bt = -t;
-            ex.bc = c;
         }
     }
     if constexpr (RC) {
@@ -419,25 +415,23 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
                 Lz = prv(cur.z), Lq = prv(cur.qx);
         EF<T> el = flux<T, TR, FX>(Lh, Ls, Lq, Lu, Lv, Lc, Lz, cur.h, cur.s, cur.qx, cur.u, cur.v, cur.cc, cur.z, g);
         if (XW && K.lwall_lane) {
-            el.bm = el.bn = el.bt = el.bc = T(0);
+            el.bm = el.bn = el.ft = el.fc = T(0);
             if (K.colok) { // wall on the left of this lane's cell (as seen by the lane on the left)
-                T m, n, t, c;
-                wall(cur.h, -cur.qx, -cur.v, cur.cc, g, m, n, t, c);
+                T m, n;
+                wall(cur.h, -cur.qx, g, m, n);
                 el.bm = m;
                 el.bn = -n;
-                el.bt = -t;
-                el.bc = c;
             }
         }
         O.ax_m = ex.am + el.bm;
         O.ax_x = ex.an + el.bn;
-        O.ax_y = ex.at + el.bt;
-        O.ax_c = TR ? ex.ac + el.bc : T(0);
+        O.ax_y = ex.ft - el.ft;
+        O.ax_c = TR ? ex.fc - el.fc : T(0);
     } else {
         O.ax_m = ex.am + prv(ex.bm);
         O.ax_x = ex.an + prv(ex.bn);
-        O.ax_y = ex.at + prv(ex.bt);
-        O.ax_c = TR ? ex.ac + prv(ex.bc) : T(0);
+        O.ax_y = ex.ft - prv(ex.ft);
+        O.ax_c = TR ? ex.fc - prv(ex.fc) : T(0);
     }
 
     // ---- y-edge (row r-1, row r): normal (0, 1), qn = qy, ut = -u;
@@ -445,19 +439,17 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     EF<T> ey = flux<T, TR, FX>(prev.h, prev.s, prev.qy, prev.v, -prev.u, prev.cc, prev.z, cur.h, cur.s, cur.qy, cur.v,
                            -cur.u, cur.cc, cur.z, g);
     if (YW && I.prevrow != currow) {
+        ey.ft = ey.fc = T(0);
         if (I.prevrow) { // wall above row r-1
-            wall(prev.h, prev.qy, -prev.u, prev.cc, g, ey.am, ey.an, ey.at, ey.ac);
-            ey.bm = ey.bn = ey.bt = ey.bc = T(0);
-        } else { // wall below row r: normal (0, -1), qn = -qy, ut = u,
-                 // back-rotation (m, n, t, c) -> (m, t, -n, c), stored so
-                 // that the common map (m, -t, n, c) below yields it
-            T m, n, t, c;
-            wall(cur.h, -cur.qy, cur.u, cur.cc, g, m, n, t, c);
-            ey.am = ey.an = ey.at = ey.ac = T(0);
+            wall(prev.h, prev.qy, g, ey.am, ey.an);
+            ey.bm = ey.bn = T(0);
+        } else { // wall below row r: normal (0, -1), qn = -qy; the normal
+                 // momentum maps back as n -> -n
+            T m, n;
+            wall(cur.h, -cur.qy, g, m, n);
+            ey.am = ey.an = T(0);
             ey.bm = m;
-            ey.bt = -t;
             ey.bn = -n;
-            ey.bc = c;
         }
     }
 
@@ -476,32 +468,32 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     if (r >= K.j0) {
         // ---- complete row r-1: W^{n+1} = W^n - dt/|V| sum |G| fluct, the
         // x- and y-edge sums scaled by dt |G_x| / |V| and dt |G_y| / |V|;
-        // y-edge fluctuations map back as (m, n, t, c) -> (m, -t, n, c)
+        // y-edge parts map back as (m, n, t, c) -> (m, -t, n, c) (the edge
+        // frame's transverse axis is -x); the transverse and pollutant rows
+        // are flux differences (top minus bottom, right minus left)
         T ybm = I.yb_m, ybt = I.yb_t, ybn = I.yb_n, ybc = I.yb_c;
         if constexpr (RC) { // the bottom y-edge (r-2, r-1), evaluated again
             const PC<T> &p2 = I.prev2;
             EF<T> eb = flux<T, TR, FX>(p2.h, p2.s, p2.qy, p2.v, -p2.u, p2.cc, p2.z, prev.h, prev.s, prev.qy, prev.v,
                                        -prev.u, prev.cc, prev.z, g);
             if (YW && I.prev2row != I.prevrow) {
-                eb.bm = eb.bn = eb.bt = eb.bc = T(0);
+                eb.bm = eb.bn = eb.ft = eb.fc = T(0);
                 if (I.prevrow) { // wall below row r-1
-                    T m, n, t, c;
-                    wall(prev.h, -prev.qy, prev.u, prev.cc, g, m, n, t, c);
+                    T m, n;
+                    wall(prev.h, -prev.qy, g, m, n);
                     eb.bm = m;
-                    eb.bt = -t;
                     eb.bn = -n;
-                    eb.bc = c;
                 }
             }
             ybm = eb.bm;
-            ybt = eb.bt;
+            ybt = eb.ft;
             ybn = eb.bn;
-            ybc = eb.bc;
+            ybc = eb.fc;
         }
         const T ym = ybm + ey.am;
-        const T yt = ybt + ey.at;
+        const T yt = ey.ft - ybt;
         const T yn = ybn + ey.an;
-        const T yc = ybc + ey.ac;
+        const T yc = ey.fc - ybc;
         const T fx = K.fx, fy = K.fy;
         const T h1 = prev.h - fx * I.ax_m - fy * ym;
         const T qx1 = prev.qx - fx * I.ax_x + fy * yt;
@@ -543,8 +535,9 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         if (wr >= K.rs0 && wr < K.rs1 && K.wlane) {
             const uint32_t k = (uint32_t)(DN ? K.rbase - wr : wr) * (uint32_t)A.nx + (uint32_t)K.i;
             st_rec<T, TR ? 4 : 3>(A.out0, A.out1, k, h1, qx1, DN ? -qy1 : qy1, c1, A.nt);
-            bad_depth |= !(h1 > T(0));
-            bad_val |= !isfinite(h1 + qx1 + qy1 + c1);
+            // lane masks of the wavefront (scalar registers, no per-lane select)
+            bad_depth |= __ballot(!(h1 > T(0)));
+            bad_val |= __ballot(!isfinite(h1 + qx1 + qy1 + c1));
         }
         if constexpr (RC) {
             O.np2_h = I.np_h;
@@ -560,9 +553,9 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
     }
     // bottom part of the y-edge for row r (edge frame)
     O.yb_m = ey.bm;
-    O.yb_t = ey.bt;
+    O.yb_t = ey.ft;
     O.yb_n = ey.bn;
-    O.yb_c = ey.bc;
+    O.yb_c = ey.fc;
     if constexpr (RC) {
         O.prev2 = I.prev;
         O.prev2row = I.prevrow;
@@ -611,7 +604,7 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     K.ly = A.dx; // length of a y-edge
 
     T smax = T(0);
-    bool bad_depth = false, bad_val = false;
+    uint64_t bad_depth = 0, bad_val = 0;
     Carry<T> c0, c1;
     Ld<T> l0, l1, l2, l3;
     {

@@ -34,8 +34,8 @@ constexpr int TRI_XCD = 8;
 constexpr int TRI_NPART = 64;
 
 template <typename T> struct TriArgs {
-    const T *in[6];
-    T *out[6];
+    const T *in;  // W^n: one record of the NV conserved variables per cell
+    T *out;       // W^{n+1}, records as `in`
     const T *z;
     int64_t N;
     int B, nblocks, per_xcd, lc_max, e_max;
@@ -344,7 +344,7 @@ k_tri_fused(TriArgs<T> A)
     // below, which would otherwise pull them into a branch and wait on each)
 #pragma unroll
     for (int m = 0; m < RD; ++m) asm volatile("" ::"v"(hid[m]));
-    uint32_t gidx[RD]; // a valid cell for every lane; only l < LC are local cells
+    uint32_t gidx[RD]; // a valid cell for every lane; only l < LC are local cells (record offsets NV * cell)
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
         const int l = tid + m * NT;
@@ -357,7 +357,7 @@ k_tri_fused(TriArgs<T> A)
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) st[m][v] = ld32(A.in[v], gidx[m]);
+        for (int v = 0; v < NV; ++v) st[m][v] = ld32(A.in, gidx[m] * NV + v);
         st[m][NV] = ld32(A.z, gidx[m]);
     }
 #pragma unroll
@@ -551,7 +551,7 @@ k_tri_fused(TriArgs<T> A)
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                     const T x = c[v];
-                    st32(A.out[v], ubase + (uint32_t)l) = x;
+                    st32(A.out, (ubase + (uint32_t)l) * NV + v) = x;
                     badv |= !isfinite(x);
                 }
                 if (!(c[0] > T(0)) || (NL == 2 && !(c[3] > T(0)))) bad |= FLAG_DEPTH;
@@ -627,7 +627,7 @@ __device__ __forceinline__ void tri_state(const TriArgs<T> &A, const TriBlk &b, 
 {
     const uint32_t gi = tid < b.B0 ? (uint32_t)(b.base + tid) : (uint32_t)p.hid;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) st[v] = ld32(A.in[v], gi);
+    for (int v = 0; v < NV; ++v) st[v] = ld32(A.in, gi * NV + v);
     st[NV] = ld32(A.z, gi);
 }
 
@@ -755,7 +755,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const T x = c[v];
-                st32(A.out[v], (uint32_t)(cb.base + tid)) = x;
+                st32(A.out, (uint32_t)(cb.base + tid) * NV + v) = x;
                 badv |= !isfinite(x);
             }
             if (!(c[0] > T(0)) || (NL == 2 && !(c[3] > T(0)))) bad |= FLAG_DEPTH;
@@ -814,14 +814,42 @@ hipError_t launch_permute(swe_ctx *c, const void *src, void *dst, int to_interna
     return hipGetLastError();
 }
 
+// The caller's separate arrays, in the caller's cell order <-> the records
+// of the fused triangle path, in internal (Morton) order: record i holds the
+// nv variables of caller cell perm[i].
+template <typename T>
+__global__ void k_tri_pack(const int32_t *__restrict__ perm, StatePtrs<T> soa, T *__restrict__ rec, int64_t n, int nv,
+                           int pack)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t k = perm[i];
+    for (int v = 0; v < nv; ++v) {
+        if (pack) rec[i * nv + v] = soa.v[v][k];
+        else soa.v[v][k] = rec[i * nv + v];
+    }
+}
+
+template <typename T> static hipError_t tri_pack_t(swe_ctx *c, const void *const *soa, void *rec, int pack)
+{
+    StatePtrs<T> p;
+    for (int v = 0; v < 6; ++v) p.v[v] = v < c->nv ? (T *)soa[v] : nullptr;
+    const unsigned nb = (unsigned)((c->N + 255) / 256);
+    hipLaunchKernelGGL(k_tri_pack<T>, dim3(nb), dim3(256), 0, c->stream, c->perm, p, (T *)rec, c->N, c->nv, pack);
+    return hipGetLastError();
+}
+
+hipError_t launch_tri_pack(swe_ctx *c, const void *const *soa, void *rec, int pack)
+{
+    return c->prec == SWE_F32 ? tri_pack_t<float>(c, soa, rec, pack) : tri_pack_t<double>(c, soa, rec, pack);
+}
+
 template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, double cfl)
 {
     TriArgs<T> A;
     const int in = c->cur ^ (int)(step & 1), out = in ^ 1;
-    for (int v = 0; v < 6; ++v) {
-        A.in[v] = v < c->nv ? (const T *)c->state[in] + (int64_t)v * c->N : nullptr;
-        A.out[v] = v < c->nv ? (T *)c->state[out] + (int64_t)v * c->N : nullptr;
-    }
+    A.in = (const T *)c->state[in];
+    A.out = (T *)c->state[out];
     A.z = (const T *)c->zbed;
     A.N = c->N;
     A.B = c->tb.B;

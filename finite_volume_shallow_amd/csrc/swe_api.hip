@@ -335,7 +335,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             c->err = "grid too large";
             throw Fail{SWE_E_INVAL};
         }
-        c->interleaved = d->mesh_kind == SWE_MESH_CART && c->path != SWE_PATH_EDGE;
+        c->interleaved = c->path != SWE_PATH_EDGE; // the fused paths keep per-cell records
         c->N = d->mesh_kind == SWE_MESH_CART ? d->nx * d->ny : d->ncells;
 
         // host-side mesh work first: mesh errors are reported without
@@ -415,7 +415,8 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             // the fused triangle kernels address these arrays with 32-bit byte offsets
             const uint64_t lim = (uint64_t)1 << 32;
             if (hb.e_ab.size() * 4 > lim || hb.halo_ids.size() * 4 > lim || hb.slots.size() * 2 > lim ||
-                hb.e_gx.size() * c->rs > lim || hb.iarea.size() * c->rs > lim) {
+                hb.e_gx.size() * c->rs > lim || hb.iarea.size() * c->rs > lim ||
+                (uint64_t)c->N * c->nv * c->rs > lim) {
                 c->err = "triangle mesh too large for the fused path; use SWE_PATH_EDGE";
                 throw Fail{SWE_E_INVAL};
             }
@@ -522,10 +523,12 @@ int swe_set_state(swe_ctx *c, const double *z, const double *const *cons)
             return tmp.data();
         };
         upload_real(c, c->zbed, ordered(z), c->N);
-        if (c->interleaved) { // record planes (cart_plane_offset)
+        if (c->interleaved) { // per-cell records (state_offset), internal order
             std::vector<double> rec((size_t)c->nv * c->N);
-            for (int64_t i = 0; i < c->N; ++i)
-                for (int v = 0; v < c->nv; ++v) rec[cart_plane_offset(c, v, i)] = cons[v][i];
+            for (int64_t i = 0; i < c->N; ++i) {
+                const int64_t k = c->perm ? c->perm_host[i] : i;
+                for (int v = 0; v < c->nv; ++v) rec[state_offset(c, v, i)] = cons[v][k];
+            }
             upload_real(c, c->state[0], rec.data(), (int64_t)c->nv * c->N);
         } else {
             for (int v = 0; v < c->nv; ++v)
@@ -558,10 +561,9 @@ int swe_set_state_device(swe_ctx *c, const void *z, const void *const *cons)
     try {
         c->cur = 0;
         const size_t bytes = (size_t)c->N * c->rs;
-        if (c->perm) {
+        if (c->perm) { // fused triangle path: records in internal order
             HIPTRY(launch_permute(c, z, c->zbed, 1));
-            for (int v = 0; v < c->nv; ++v)
-                HIPTRY(launch_permute(c, cons[v], (char *)c->state[0] + v * bytes, 1));
+            HIPTRY(launch_tri_pack(c, cons, c->state[0], 1));
         } else {
             HIPTRY(hipMemcpyAsync(c->zbed, z, bytes, hipMemcpyDeviceToDevice, c->stream));
             if (c->interleaved) {
@@ -718,7 +720,7 @@ int swe_get_state(swe_ctx *c, double *const *out)
         const char *base = (const char *)c->state[c->cur];
         std::vector<double> d64;
         std::vector<float> f32;
-        if (c->interleaved) { // record planes (cart_plane_offset)
+        if (c->interleaved) { // per-cell records (state_offset), internal order
             const size_t n = (size_t)c->nv * c->N;
             d64.resize(n);
             if (c->prec == SWE_F64) {
@@ -730,8 +732,10 @@ int swe_get_state(swe_ctx *c, double *const *out)
                 HIPTRY(hipStreamSynchronize(c->stream));
                 for (size_t i = 0; i < n; ++i) d64[i] = f32[i];
             }
-            for (int64_t i = 0; i < c->N; ++i)
-                for (int v = 0; v < c->nv; ++v) out[v][i] = d64[cart_plane_offset(c, v, i)];
+            for (int64_t i = 0; i < c->N; ++i) {
+                const int64_t k = c->perm ? c->perm_host[i] : i;
+                for (int v = 0; v < c->nv; ++v) out[v][k] = d64[state_offset(c, v, i)];
+            }
             return SWE_OK;
         }
         for (int v = 0; v < c->nv; ++v) {
@@ -784,7 +788,8 @@ int swe_get_state_device(swe_ctx *c, void *const *out)
     try {
         const size_t bytes = (size_t)c->N * c->rs;
         if (c->interleaved) {
-            HIPTRY(launch_cart_pack(c, (const void *const *)out, c->state[c->cur], 0));
+            if (c->perm) HIPTRY(launch_tri_pack(c, (const void *const *)out, c->state[c->cur], 0));
+            else HIPTRY(launch_cart_pack(c, (const void *const *)out, c->state[c->cur], 0));
             return SWE_OK;
         }
         for (int v = 0; v < c->nv; ++v) {

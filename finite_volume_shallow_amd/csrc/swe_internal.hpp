@@ -93,8 +93,9 @@ struct swe_ctx {
     bool has_state = false;
 
     // state: two copies (ping-pong) of nv * N reals each: nv arrays of N
-    // reals (edge and triangle paths), or N interleaved records of nv reals
-    // (fused structured path, `interleaved`)
+    // reals (edge path), or interleaved per cell (`interleaved`: record
+    // planes on the fused structured path, records of nv reals on the fused
+    // triangle path); state_offset addresses all three
     void *state[2] = {nullptr, nullptr};
     bool interleaved = false;
     int cur = 0;
@@ -155,12 +156,21 @@ hipError_t launch_permute(swe_ctx *c, const void *src, void *dst, int to_interna
 // the record planes at rec (cart_plane); pack = 0 splits them.
 hipError_t launch_cart_pack(swe_ctx *c, const void *const *soa, void *rec, int pack);
 
+// Fused triangle path: pack = 1 moves the nv device arrays soa[] (caller
+// cell order) into the per-cell records at rec (internal order); pack = 0
+// moves them back.
+hipError_t launch_tri_pack(swe_ctx *c, const void *const *soa, void *rec, int pack);
+
 // Record planes of the structured fused path: float32, one plane of nv
 // reals per cell; float64, plane 0 holds (h, qx) and plane 1 the remaining
 // nv - 2 reals per cell.  Offset, in reals from the state's start, of
 // variable v of cell k, and the start of plane 1.
 inline int64_t cart_plane1(const swe_ctx *c);
 inline int64_t cart_plane_offset(const swe_ctx *c, int v, int64_t k);
+// Offset, in reals from the state's start, of variable v of (internal) cell
+// k in any path's layout: record planes (structured fused path), records of
+// nv reals (fused triangle path) or one array per variable (edge path).
+inline int64_t state_offset(const swe_ctx *c, int v, int64_t k);
 size_t tri_lds_bytes(int nv, size_t rs, int lc_max, int e_max);
 int tri_edge_rec(int nv);
 
@@ -171,4 +181,10 @@ inline int64_t swe::cart_plane_offset(const swe_ctx *c, int v, int64_t k)
 {
     if (c->rs == 4) return k * c->nv + v;
     return v < 2 ? 2 * k + v : 2 * c->N + k * (c->nv - 2) + (v - 2);
+}
+inline int64_t swe::state_offset(const swe_ctx *c, int v, int64_t k)
+{
+    if (!c->interleaved) return v * c->N + k;
+    if (c->kind == SWE_MESH_CART) return cart_plane_offset(c, v, k);
+    return k * c->nv + v;
 }

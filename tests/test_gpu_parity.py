@@ -216,8 +216,11 @@ def test_classical_and_ir_differ_on_gpu():
 # of its edges itself): against the oracle, and against the shared-edge
 # kernels (on Cartesian grids in every tiling and march direction).  A
 # recomputed edge has the same inputs as the shared one, but the compiler
-# may contract its multiply-adds differently, so the two agree to rounding.
-RC_TOL = {"f64": 1e-12, "f32": 2e-5}
+# may contract its multiply-adds differently, so the two agree to rounding:
+# in float32 that rounding accumulates over 100 steps to the size of the
+# float32-vs-float64 error itself (2.6e-5 on the 96^2 hump), so the bar is
+# half of the 1e-4 float32 tolerance.
+RC_TOL = {"f64": 1e-12, "f32": 5e-5}
 
 
 @pytest.mark.parametrize("name", list(CASES))

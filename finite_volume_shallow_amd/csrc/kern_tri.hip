@@ -77,25 +77,23 @@ __device__ __forceinline__ T roe2_speed(const T *L, const T *pL, const T *R, con
 // consecutive records of an odd number of 8-byte reals touches every bank
 // once, so every record stride here is odd (in reals) and field offsets are
 // constants (neighbouring fields load and store as one instruction).
-//   cell state: the NV conserved variables (two layers: and z), SA reals;
-//   cell aux (one layer): z, sqrt(h), 1/h, 3 reals, after all state records;
+//   cell: the NV conserved variables, z and (one layer) sqrt(h) and 1/h in
+//   one record of SA reals, so that an edge's gather of a cell takes the
+//   fewest LDS instructions;
 //   edge fluctuations: side a of every edge, then side b, ER reals each.
 template <int NL, int NV> struct TriRec {
-    static constexpr int SA = NL == 1 ? (NV | 1) : ((NV + 1) | 1);
-    static constexpr int AX = NL == 1 ? 3 : 0;
+    static constexpr int SA = NL == 1 ? ((NV + 3) | 1) : ((NV + 1) | 1);
+    static constexpr int AX = 0; // no separate per-cell record
     static constexpr int ER = NV | 1;
 };
 
-// View of local cell l: its state record and (one layer) its aux record.
+// View of local cell l: its record (state, z and, one layer, sqrt(h), 1/h).
 template <typename T, int NL, int NV> struct TriCell {
-    T *s, *x;
-    __device__ __forceinline__ TriCell(T *sm, int lcm, int l)
-        : s(sm + l * TriRec<NL, NV>::SA), x(sm + lcm * TriRec<NL, NV>::SA + l * TriRec<NL, NV>::AX)
-    {
-    }
-    __device__ __forceinline__ T &z() const { return NL == 1 ? x[0] : s[NV]; }
-    __device__ __forceinline__ T &sq() const { return x[1]; } // sqrt(h), one layer
-    __device__ __forceinline__ T &ih() const { return x[2]; } // 1/h, one layer
+    T *s;
+    __device__ __forceinline__ TriCell(T *sm, int lcm, int l) : s(sm + l * TriRec<NL, NV>::SA) {}
+    __device__ __forceinline__ T &z() const { return s[NV]; }
+    __device__ __forceinline__ T &sq() const { return s[NV + 1]; } // sqrt(h), one layer
+    __device__ __forceinline__ T &ih() const { return s[NV + 2]; } // 1/h, one layer
 };
 
 // sqrt(h) and 1/h of a one-layer cell (the two-layer path keeps its LDS for

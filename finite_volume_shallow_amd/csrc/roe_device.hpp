@@ -120,6 +120,20 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     const T uL = qnL * ihL, uR = qnR * ihR;
     const T isum = rcp(sL + sR);
     const T ubar = (sL * uL + sR * uR) * isum;
+    // classical flux: the contact waves' Roe averages and jumps are formed
+    // here, so that their inputs (the transverse velocities and sqrt(h)
+    // weights) are no longer needed during the 2x2 part
+    T vbar = T(0), Xt = T(0), cbar = T(0), Xc = T(0);
+    if (flux_classical(FX)) {
+        const T utL = qtL * ihL, utR = qtR * ihR;
+        vbar = (sL * utL + sR * utR) * isum;
+        Xt = qnR * utR - qnL * utL;
+        if (TRACER) {
+            const T ccL = cL * ihL, ccR = cR * ihR;
+            cbar = (sL * ccL + sR * ccR) * isum;
+            Xc = qnR * ccR - qnL * ccL;
+        }
+    }
     const T hbar = T(0.5) * (hL + hR);
     const T c2 = g * hbar;
     const T irc = FM<T>::rsq(c2);
@@ -139,17 +153,11 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
     o.an = pm1;
     o.bm = X0 - pm0;
     o.bn = X1 - pm1;
-    const T utL = qtL * ihL, utR = qtR * ihR;
     if (flux_classical(FX)) {
         const T wu = wminus(ubar);
-        const T vbar = (sL * utL + sR * utR) * isum;
-        const T Xt = qnR * utR - qnL * utL;
         o.at = vbar * pm0 + wu * (Xt - vbar * X0);
         o.bt = Xt - o.at;
         if (TRACER) {
-            const T ccL = cL * ihL, ccR = cR * ihR;
-            const T cbar = (sL * ccL + sR * ccR) * isum;
-            const T Xc = qnR * ccR - qnL * ccL;
             o.ac = cbar * pm0 + wu * (Xc - cbar * X0);
             o.bc = Xc - o.ac;
         } else {
@@ -159,6 +167,7 @@ __device__ __forceinline__ Flux1<T, TRACER> roe1_pre(T hL, T sL, T ihL, T qnL, T
         o.speed = fabs(ubar) + c;
         return o;
     }
+    const T utL = qtL * ihL, utR = qtR * ihR;
     const T phi0 = qnL + pm0; // mass flux through the edge
     if (phi0 > T(0)) {
         o.at = pm0 * utL;                    // phi0 utL - qnL utL

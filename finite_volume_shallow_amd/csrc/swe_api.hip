@@ -390,6 +390,14 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 if (pipe && !std::getenv("SWE_TRI_B")) B = 288; // the per-block kernel's first choice
                 pipe = false;
             }
+            // Two layers, one workgroup per block: a block whose local
+            // cells, edges or updated cells exceed one round of threads
+            // makes every block run two rounds (heavier on registers; the
+            // classical flux then spills), so the size first shrinks in
+            // steps of 8 cells, down to 192, while one block does not fit
+            // one round (the 1M two-layer mesh: one of 4,463 blocks of 224
+            // cells has 513 local edges, none at 216).
+            const bool fit_one_round = c->nv == 6 && !std::getenv("SWE_TRI_B");
             for (;;) {
                 st = build_tri_blocks(he, c->N, B, hb, c->err);
                 if (st != SWE_OK) throw Fail{st};
@@ -398,6 +406,10 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 const int need = std::max(std::max(hb.lc_max, hb.e_max), upd);
                 const bool lds_ok = tri_lds_bytes(c->nv, c->rs, hb.lc_max, hb.e_max) <= lds_cap &&
                                     2 * tri_edge_rec(c->nv) * hb.e_max <= 0xFFFF;
+                if (fit_one_round && !pipe && lds_ok && need > c->tb.nt && B > 192 && B <= 224) {
+                    B -= 8;
+                    continue;
+                }
                 if (pipe) {
                     if (lds_ok && need <= c->tb.nt) break;
                     pipe = false; // this mesh: one workgroup per block

@@ -17,7 +17,10 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libswe.so")
 ARCH = os.environ.get("SWE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["swe_api.hip", "mesh_host.cpp", "kern_edge.hip", "kern_cart.hip", "kern_tri.hip"]
+# (source, preprocessor symbol): kern_cart.hip is compiled twice, the second
+# time for the streaming-mode kernels of the structured path only
+SOURCES = [("swe_api.hip", None), ("mesh_host.cpp", None), ("kern_edge.hip", None), ("kern_cart.hip", None),
+           ("kern_cart.hip", "SWE_CART_STREAM_TU"), ("kern_tri.hip", None)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -27,13 +30,15 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(spec, verbose: bool) -> str:
+    src, define = spec
+    obj = os.path.join(BUILD, os.path.basename(src) + (f".{define}" if define else "") + ".o")
     path = os.path.join(CSRC, src)
+    extra = [f"-D{define}"] if define else []
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *extra, "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *extra, "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,7 +55,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: a symbol that no object defines fails the link, not the load
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -58,7 +58,7 @@ template <typename T, bool TR> struct CartArgs {
     T dx, dy, g, cfl;
     int ty;        // rows per tile
     int alt;       // odd row blocks march downward
-    int nt;        // non-temporal state stores (st_w)
+    int rev;       // tiles in reverse order (streaming mode, every other step)
     int nstrips;   // tiles across x
     int ntiles;    // tiles in total
     int per_xcd;   // tiles per XCD band
@@ -226,57 +226,68 @@ template <typename T, int W> struct CVec {
 
 // Element k of plane `base` with W reals per record (W = 1, 2 or 4 load as
 // one instruction; W = 3 as three adjacent reals), 32-bit byte offsets.
-template <typename T, int W> __device__ __forceinline__ void ld_w(const T *base, uint32_t k, T (&o)[W])
+// NTL: a non-temporal load (compile-time, so that no optimisation can merge
+// it with a plain load of the same address and drop the hint).
+template <typename T, int W, bool NTL = false>
+__device__ __forceinline__ void ld_w(const T *base, uint32_t k, T (&o)[W])
 {
     const char *p = reinterpret_cast<const char *>(base) + (uint32_t)(k * (uint32_t)(W * sizeof(T)));
     if constexpr (W == 2 || W == 4) {
-        const typename CVec<T, W>::V v = *reinterpret_cast<const typename CVec<T, W>::V *>(p);
+        typedef typename CVec<T, W>::V V;
+        V v;
+        if constexpr (NTL) v = __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+        else v = *reinterpret_cast<const V *>(p);
 #pragma unroll
         for (int i = 0; i < W; ++i) o[i] = v[i];
     } else {
 #pragma unroll
-        for (int i = 0; i < W; ++i) o[i] = reinterpret_cast<const T *>(p)[i];
-    }
-}
-// NT: a non-temporal store.  W^{n+1} is not read again in the launch that
-// writes it; on grids whose state exceeds the last-level cache, streaming it
-// past the caches pays (a memory-only copy of the 4096^2 march: 108 instead
-// of 121-127 us), while a grid whose two state copies stay cached reads it
-// back faster from the cache in the next launch.
-template <typename T, int W>
-__device__ __forceinline__ void st_w(T *base, uint32_t k, const T (&x)[W], bool nt)
-{
-    char *p = reinterpret_cast<char *>(base) + (uint32_t)(k * (uint32_t)(W * sizeof(T)));
-    if constexpr (W == 2 || W == 4) {
-        typename CVec<T, W>::V v;
-#pragma unroll
-        for (int i = 0; i < W; ++i) v[i] = x[i];
-        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<typename CVec<T, W>::V *>(p));
-        else *reinterpret_cast<typename CVec<T, W>::V *>(p) = v;
-    } else {
-#pragma unroll
         for (int i = 0; i < W; ++i) {
-            if (nt) __builtin_nontemporal_store(x[i], reinterpret_cast<T *>(p) + i);
-            else reinterpret_cast<T *>(p)[i] = x[i];
+            if constexpr (NTL) o[i] = __builtin_nontemporal_load(reinterpret_cast<const T *>(p) + i);
+            else o[i] = reinterpret_cast<const T *>(p)[i];
         }
     }
 }
 
+// Streaming mode, for grids whose two state copies and bed exceed the
+// last-level cache: W^n is loaded non-temporally (beyond the halo rows that
+// a neighbouring tile reads at about the same time, the launch does not read
+// it again), W^{n+1} is stored normally, and every other step runs its
+// tiles in reverse order, so that a step starts with the state its
+// predecessor wrote last, the part most likely still in the cache, and the
+// bed stays there.  Non-temporal stores as well cost about 1 us more on the
+// 4096^2 grid: the state they write is the next step's first read.  A grid
+// that fits the cache keeps plain loads and the forward order, since it
+// reads its state back from the cache in the next launch anyway.
+template <typename T, int W> __device__ __forceinline__ void st_w(T *base, uint32_t k, const T (&x)[W])
+{
+    char *p = reinterpret_cast<char *>(base) + (uint32_t)(k * (uint32_t)(W * sizeof(T)));
+    if constexpr (W == 2 || W == 4) {
+        typedef typename CVec<T, W>::V V;
+        V v;
+#pragma unroll
+        for (int i = 0; i < W; ++i) v[i] = x[i];
+        *reinterpret_cast<V *>(p) = v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < W; ++i) reinterpret_cast<T *>(p)[i] = x[i];
+    }
+}
+
 // Cell k of the state (NR = 3 or 4 variables) from / to its planes.
-template <typename T, int NR>
+template <typename T, int NR, bool NTL = false>
 __device__ __forceinline__ void ld_rec(const T *p0, const T *p1, uint32_t k, T &h, T &qx, T &qy, T &c)
 {
     if constexpr (sizeof(T) == 4) {
         T a[NR];
-        ld_w<T, NR>(p0, k, a);
+        ld_w<T, NR, NTL>(p0, k, a);
         h = a[0];
         qx = a[1];
         qy = a[2];
         c = NR == 4 ? a[NR - 1] : T(0);
     } else {
         T a[2], b[NR - 2];
-        ld_w<T, 2>(p0, k, a);
-        ld_w<T, NR - 2>(p1, k, b);
+        ld_w<T, 2, NTL>(p0, k, a);
+        ld_w<T, NR - 2, NTL>(p1, k, b);
         h = a[0];
         qx = a[1];
         qy = b[0];
@@ -284,7 +295,7 @@ __device__ __forceinline__ void ld_rec(const T *p0, const T *p1, uint32_t k, T &
     }
 }
 template <typename T, int NR>
-__device__ __forceinline__ void st_rec(T *p0, T *p1, uint32_t k, T h, T qx, T qy, T c, bool nt = false)
+__device__ __forceinline__ void st_rec(T *p0, T *p1, uint32_t k, T h, T qx, T qy, T c)
 {
     if constexpr (sizeof(T) == 4) {
         T a[NR];
@@ -292,14 +303,14 @@ __device__ __forceinline__ void st_rec(T *p0, T *p1, uint32_t k, T h, T qx, T qy
         a[1] = qx;
         a[2] = qy;
         if constexpr (NR == 4) a[3] = c;
-        st_w<T, NR>(p0, k, a, nt);
+        st_w<T, NR>(p0, k, a);
     } else {
         const T a[2] = {h, qx};
         T b[NR - 2];
         b[0] = qy;
         if constexpr (NR == 4) b[1] = c;
-        st_w<T, 2>(p0, k, a, nt);
-        st_w<T, NR - 2>(p1, k, b, nt);
+        st_w<T, 2>(p0, k, a);
+        st_w<T, NR - 2>(p1, k, b);
     }
 }
 
@@ -307,8 +318,8 @@ __device__ __forceinline__ void st_rec(T *p0, T *p1, uint32_t k, T h, T qx, T qy
 // outside the domain (walls); such cells get benign placeholder values.
 // `row` is the grid row.  The values are raw: a downward-marching tile
 // negates qy where it uses them, not here, so that nothing waits on a load
-// before its row is needed.
-template <bool CHECK, typename T, bool TR>
+// before its row is needed.  SM: streaming mode (non-temporal loads).
+template <bool CHECK, bool SM, typename T, bool TR>
 __device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int col, bool colok, T &h,
                                          T &qx, T &qy, T &c, T &z, bool &rowok)
 {
@@ -319,7 +330,7 @@ __device__ __forceinline__ void load_row(const CartArgs<T, TR> &A, int row, int 
     }
     if (!CHECK || (rowok && colok)) {
         const uint32_t k = (uint32_t)row * (uint32_t)A.nx + (uint32_t)col;
-        ld_rec<T, TR ? 4 : 3>(A.in0, A.in1, k, h, qx, qy, c);
+        ld_rec<T, TR ? 4 : 3, SM>(A.in0, A.in1, k, h, qx, qy, c);
         z = at(A.z, k);
     } else {
         h = T(1);
@@ -377,14 +388,14 @@ constexpr int PREFETCH = 2;
 // recomputed edge are bit-identical to the shared one's; the results agree
 // to rounding (the compiler may contract the two evaluations' multiply-adds
 // differently).
-template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC>
+template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC, bool SM>
 __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T> &K, int r, const Carry<T> &I,
                                          Carry<T> &O, const Ld<T> &cur_ld, Ld<T> &nxt_ld, T &smax,
                                          uint64_t &bad_depth, uint64_t &bad_val)
 {
     // the row PREFETCH ahead is requested before anything waits on row r
     if (r + PREFETCH <= K.rlast)
-        load_row<XW || YW>(A, DN ? K.rbase - (r + PREFETCH) : r + PREFETCH, K.col, K.colok, nxt_ld.h, nxt_ld.qx,
+        load_row<XW || YW, SM>(A, DN ? K.rbase - (r + PREFETCH) : r + PREFETCH, K.col, K.colok, nxt_ld.h, nxt_ld.qx,
                            nxt_ld.qy, nxt_ld.c, nxt_ld.z, nxt_ld.rowok);
     const PC<T> cur = prep(cur_ld.h, cur_ld.qx, DN ? -cur_ld.qy : cur_ld.qy, cur_ld.c, cur_ld.z);
     const bool currow = cur_ld.rowok; // uniform across the wavefront
@@ -534,7 +545,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
         const int wr = r - 1;
         if (wr >= K.rs0 && wr < K.rs1 && K.wlane) {
             const uint32_t k = (uint32_t)(DN ? K.rbase - wr : wr) * (uint32_t)A.nx + (uint32_t)K.i;
-            st_rec<T, TR ? 4 : 3>(A.out0, A.out1, k, h1, qx1, DN ? -qy1 : qy1, c1, A.nt);
+            st_rec<T, TR ? 4 : 3>(A.out0, A.out1, k, h1, qx1, DN ? -qy1 : qy1, c1);
             // lane masks of the wavefront (scalar registers, no per-lane select)
             bad_depth |= __ballot(!(h1 > T(0)));
             bad_val |= __ballot(!isfinite(h1 + qx1 + qy1 + c1));
@@ -568,7 +579,7 @@ __device__ __forceinline__ void row_step(const CartArgs<T, TR> &A, const TileC<T
 // tile's rows reach a wall in y.  Tiles with neither (almost all of them)
 // run without any wall code.  Returns the tile's largest Eq. (5) speed sum
 // sum |G| ||D|| (the smallest dt candidate is 2 gamma |V| over it).
-template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC>
+template <typename T, bool TR, bool XW, bool YW, bool DN, int FX, bool RC, bool SM>
 __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, int lane, double dtd, T &smax_out,
                                           unsigned &bad_out)
 {
@@ -609,7 +620,7 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     Ld<T> l0, l1, l2, l3;
     {
         Ld<T> p;
-        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 2) : K.j0 - 2, K.col, K.colok, p.h, p.qx, p.qy, p.c, p.z, p.rowok);
+        load_row<XW || YW, SM>(A, DN ? K.rbase - (K.j0 - 2) : K.j0 - 2, K.col, K.colok, p.h, p.qx, p.qy, p.c, p.z, p.rowok);
         c0.prevrow = p.rowok;
         c0.ax_m = c0.ax_x = c0.ax_y = c0.ax_c = T(0);
         c0.yb_m = c0.yb_n = c0.yb_t = c0.yb_c = T(0);
@@ -623,8 +634,8 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
         c0.np2_s = T(1);
         c0.np2_b = T(0);
         c0.np2row = false;
-        load_row<XW || YW>(A, DN ? K.rbase - (K.j0 - 1) : K.j0 - 1, K.col, K.colok, l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
-        load_row<XW || YW>(A, DN ? K.rbase - K.j0 : K.j0, K.col, K.colok, l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
+        load_row<XW || YW, SM>(A, DN ? K.rbase - (K.j0 - 1) : K.j0 - 1, K.col, K.colok, l0.h, l0.qx, l0.qy, l0.c, l0.z, l0.rowok);
+        load_row<XW || YW, SM>(A, DN ? K.rbase - K.j0 : K.j0, K.col, K.colok, l1.h, l1.qx, l1.qy, l1.c, l1.z, l1.rowok);
         c0.prev = prep(p.h, p.qx, DN ? -p.qy : p.qy, p.c, p.z);
         c0.prev2 = c0.prev;
     }
@@ -633,36 +644,38 @@ __device__ __forceinline__ void cart_tile(const CartArgs<T, TR> &A, int tile, in
     // another), so no register is copied between rows.
     int r = K.j0 - 1;
     for (; r + 3 <= K.rlast; r += 4) {
-        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
-        row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+        row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r + 3, c1, c0, l3, l1, smax, bad_depth, bad_val);
     }
-    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
-    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
-    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
+    if (r <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r, c0, c1, l0, l2, smax, bad_depth, bad_val);
+    if (r + 1 <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r + 1, c1, c0, l1, l3, smax, bad_depth, bad_val);
+    if (r + 2 <= K.rlast) row_step<T, TR, XW, YW, DN, FX, RC, SM>(A, K, r + 2, c0, c1, l2, l0, smax, bad_depth, bad_val);
     smax_out = smax;
     bad_out = (bad_depth ? FLAG_DEPTH : 0u) | (bad_val ? FLAG_NONFINITE : 0u);
 }
 
 // The tile variant for its walls (x, y) and march direction.
-template <typename T, bool TR, bool DN, int FX, bool RC>
+template <typename T, bool TR, bool DN, int FX, bool RC, bool SM>
 __device__ __forceinline__ void cart_tile_dispatch(const CartArgs<T, TR> &A, int tile, int lane, double dtd, bool xw,
                                                    bool yw, T &smax, unsigned &bad)
 {
-    if (!xw && !yw) cart_tile<T, TR, false, false, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
-    else if (!yw) cart_tile<T, TR, true, false, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
-    else if (!xw) cart_tile<T, TR, false, true, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
-    else cart_tile<T, TR, true, true, DN, FX, RC>(A, tile, lane, dtd, smax, bad);
+    if (!xw && !yw) cart_tile<T, TR, false, false, DN, FX, RC, SM>(A, tile, lane, dtd, smax, bad);
+    else if (!yw) cart_tile<T, TR, true, false, DN, FX, RC, SM>(A, tile, lane, dtd, smax, bad);
+    else if (!xw) cart_tile<T, TR, false, true, DN, FX, RC, SM>(A, tile, lane, dtd, smax, bad);
+    else cart_tile<T, TR, true, true, DN, FX, RC, SM>(A, tile, lane, dtd, smax, bad);
 }
 
-template <typename T, bool TR, int FX = FLUX_IR, bool RC = false>
+template <typename T, bool TR, int FX = FLUX_IR, bool RC = false, bool SM = false>
 __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
 {
     const int lane = threadIdx.x;
-    // XCD-aware tile index: workgroup w runs on XCD w % 8
+    // XCD-aware tile index: workgroup w runs on XCD w % 8.  A reversed step
+    // starts with the tiles that the step before it wrote last.
     const int w = blockIdx.x;
-    const int tile = (w % NUM_XCD) * A.per_xcd + w / NUM_XCD;
+    const int tile0 = (w % NUM_XCD) * A.per_xcd + w / NUM_XCD;
+    const int tile = A.rev ? A.per_xcd * NUM_XCD - 1 - tile0 : tile0;
 
     // dt^n from the partial minima of the previous launch
     const int bank = (int)((A.step + A.bank0) % 3);
@@ -687,8 +700,8 @@ __global__ __launch_bounds__(64) void k_cart_fused(CartArgs<T, TR> A)
     // on large grids odd row blocks march downward: neighbouring blocks then
     // reach the rows they share (each other's halo) at about the same time,
     // while those rows are still in L2
-    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, FX, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
-    else cart_tile_dispatch<T, TR, false, FX, RC>(A, tile, lane, dtd, xw, yw, smax, bad);
+    if (A.alt && (rb & 1)) cart_tile_dispatch<T, TR, true, FX, RC, SM>(A, tile, lane, dtd, xw, yw, smax, bad);
+    else cart_tile_dispatch<T, TR, false, FX, RC, SM>(A, tile, lane, dtd, xw, yw, smax, bad);
 
     // the tile's dt candidate 2 gamma |V| / max sum |G| ||D|| (Eq. (5))
     const double dmin = wave_min(smax > T(0) ? (double)(T(2) * A.cfl * A.dx * A.dy / smax) : __builtin_inf());
@@ -822,6 +835,35 @@ template <typename T, int NR> __global__ __launch_bounds__(64 * DT0_WAVES) void 
     block_min_to_slot(cand, A.part + (blockIdx.x % NPART));
 }
 
+// Launch of the streaming-mode kernel for one step.  Its instantiations are
+// compiled in a translation unit of their own (this file built a second time
+// with SWE_CART_STREAM_TU defined), in parallel with the rest of the file.
+template <typename T, bool TR, int FX, bool RC>
+void launch_cart_stream(unsigned grid, hipStream_t s, const CartArgs<T, TR> &A);
+
+#ifdef SWE_CART_STREAM_TU
+
+template <typename T, bool TR, int FX, bool RC>
+void launch_cart_stream(unsigned grid, hipStream_t s, const CartArgs<T, TR> &A)
+{
+    hipLaunchKernelGGL((k_cart_fused<T, TR, FX, RC, true>), dim3(grid), dim3(CART_LANES), 0, s, A);
+}
+
+// every flux and path that launch_cart_batch dispatches
+#define SWE_CART_STREAM_INST(T, TR)                                                                          \
+    template void launch_cart_stream<T, TR, FLUX_IR, false>(unsigned, hipStream_t, const CartArgs<T, TR> &);   \
+    template void launch_cart_stream<T, TR, FLUX_IR_HH, false>(unsigned, hipStream_t, const CartArgs<T, TR> &); \
+    template void launch_cart_stream<T, TR, FLUX_ROE, false>(unsigned, hipStream_t, const CartArgs<T, TR> &);  \
+    template void launch_cart_stream<T, TR, FLUX_ROE_HH, false>(unsigned, hipStream_t, const CartArgs<T, TR> &); \
+    template void launch_cart_stream<T, TR, FLUX_IR, true>(unsigned, hipStream_t, const CartArgs<T, TR> &);
+SWE_CART_STREAM_INST(float, false)
+SWE_CART_STREAM_INST(float, true)
+SWE_CART_STREAM_INST(double, false)
+SWE_CART_STREAM_INST(double, true)
+#undef SWE_CART_STREAM_INST
+
+#else // the rest of the path
+
 // Batch start: elapsed time and error flags to zero; the partial minima
 // too when the batch starts from a fresh state (else the previous batch's
 // last launch left dt of the current state in bank bank0).
@@ -855,7 +897,7 @@ template <typename T, bool TR> static CartArgs<T, TR> cart_args(swe_ctx *c, int6
     A.cfl = (T)cfl;
     A.ty = c->cart_ty;
     A.alt = c->cart_alt;
-    A.nt = c->cart_nt;
+    A.rev = c->cart_stream ? in : 0;
     A.nstrips = (int)((c->nx + CART_COLS - 1) / CART_COLS);
     const int nrb = (int)((c->ny + A.ty - 1) / A.ty);
     A.ntiles = A.nstrips * nrb;
@@ -896,7 +938,10 @@ static hipError_t cart_batch_t(swe_ctx *c, int32_t nsteps, double cfl)
     for (int64_t s = 0; s < nsteps; ++s) {
         const CartArgs<T, TR> A = cart_args<T, TR>(c, s, cfl);
         const unsigned grid = (unsigned)(A.per_xcd * NUM_XCD);
-        hipLaunchKernelGGL((k_cart_fused<T, TR, FX, RC>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
+        if (c->cart_stream)
+            launch_cart_stream<T, TR, FX, RC>(grid, c->stream, A);
+        else
+            hipLaunchKernelGGL((k_cart_fused<T, TR, FX, RC>), dim3(grid), dim3(CART_LANES), 0, c->stream, A);
     }
     return hipGetLastError();
 }
@@ -962,5 +1007,7 @@ hipError_t launch_cart_batch(swe_ctx *c, int32_t nsteps, double cfl)
     if (c->hh) return cart_batch_fx<FLUX_IR_HH, false>(c, nsteps, cfl);
     return cart_batch_fx<FLUX_IR, false>(c, nsteps, cfl);
 }
+
+#endif // SWE_CART_STREAM_TU
 
 } // namespace swe

@@ -463,12 +463,14 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
         } else if (d->mesh_kind == SWE_MESH_CART) {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             cart_tiling(d->nx, d->ny, d->bc_y == SWE_BC_PERIODIC, c->cart_ty, c->cart_alt);
-            // non-temporal state stores where the two state copies and the
-            // bed exceed the 256 MB last-level cache (measured: 4096^2 float32,
-            // 604 MB, 133.2 -> 131.0 us per step; 1024^2 float64, 75 MB,
-            // 24.1 -> 25.7 us)
-            c->cart_nt = (double)c->N * c->rs * (2 * c->nv + 1) > 256.0 * (1 << 20);
-            if (const char *e = std::getenv("SWE_CART_NT")) c->cart_nt = std::atoi(e) != 0;
+            // streaming mode (non-temporal state loads, tile order reversed
+            // every other step) where the two state copies and the bed exceed
+            // the 256 MB last-level cache.  Measured on one box: 4096^2 with
+            // a pollutant, float32 (604 MB) 130.6 -> 124.6 us per step,
+            // float64 256 -> 247 us; 1024^2 float64 (75 MB) 23.1 -> 24.5 us,
+            // so it stays off there.  SWE_CART_STREAM=0/1 overrides the choice.
+            c->cart_stream = (double)c->N * c->rs * (2 * c->nv + 1) > 256.0 * (1 << 20);
+            if (const char *e = std::getenv("SWE_CART_STREAM")) c->cart_stream = std::atoi(e) != 0;
         } else {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             if (c->prec == SWE_F32) upload_blocks<float>(c, hb);

@@ -117,7 +117,7 @@ struct swe_ctx {
     double dt_cfl = 0.0;
     int cart_ty = 64;            // rows per tile
     int cart_alt = 0;            // odd row blocks of tiles march downward
-    int cart_nt = 0;             // non-temporal state stores
+    int cart_stream = 0;         // streaming mode: non-temporal state loads, alternating tile order
     double *cart_part = nullptr; // [3][64] partial dt minima (both fused paths)
 
     // fused triangle path: cells in internal (Morton) order

@@ -89,6 +89,85 @@ def test_parity_cart_tilings(tiling, monkeypatch):
     assert np.abs(dts - rdts).max() <= dtol * rdts.max()
 
 
+# Streaming mode (non-temporal state loads, tile order reversed every other
+# step) switches on by itself only where the grid's two state copies and bed
+# exceed the last-level cache; here it is forced on small grids.  Tile order
+# does not enter the arithmetic and the dt minimum is exact, so the result
+# must equal the default run bit for bit, which also shows that the reversed
+# order reaches every tile; and it must match the oracle.
+STREAMING = {
+    "flow-160x96-f32": lambda: CASES["flow-160x96-f32"][0](),
+    "flow-ragged-67x33-f64": lambda: CASES["flow-ragged-67x33-f64"][0](),
+    "dam-break-ragged-131x5": lambda: CASES["dam-break-ragged-131x5"][0](),
+    "flow-periodic-xy-67x40-f64": lambda: CASES["flow-periodic-xy-67x40-f64"][0](),
+    "hump-96-f64": lambda: CASES["hump-96-f64"][0](),
+    "classical-flow-160x96-f32": lambda: _classical(CASES["flow-160x96-f32"][0]),
+    "hh-dam-break-131x5-f32": lambda: HH["hh-dam-break-131x5-f32"][0](),
+    "hh-classical-dam-break-200x6-f64": lambda: HH["hh-classical-dam-break-200x6-f64"][0](),
+}
+STREAM_STEPS = {"hh-dam-break-131x5-f32": (100, "f32"), "hh-classical-dam-break-200x6-f64": (150, "f64"),
+                "classical-flow-160x96-f32": (100, "f32")}
+
+
+def _stream_case(name):
+    if name in STREAM_STEPS:
+        return STREAMING[name](), *STREAM_STEPS[name]
+    _, nsteps, prec = CASES[name]
+    return STREAMING[name](), nsteps, prec
+
+
+STREAM_RUNS = [f"{n}@default" for n in STREAMING] + [
+    f"{n}@{v}" for n in ("flow-160x96-f32", "flow-periodic-xy-67x40-f64") for v in ("recompute", "ty8alt1")]
+
+
+@pytest.mark.parametrize("run", STREAM_RUNS)
+def test_parity_cart_streaming(run, monkeypatch):
+    name, variant = run.split("@")
+    if variant == "ty8alt1":
+        monkeypatch.setenv("SWE_CART_TY", "8")
+        monkeypatch.setenv("SWE_CART_ALT", "1")
+    path = 3 if variant == "recompute" else 0
+    w, nsteps, prec = _stream_case(name)
+    say(f"[streaming] {name} {variant} steps={nsteps} prec={prec}")
+    monkeypatch.setenv("SWE_CART_STREAM", "0")
+    base, bdts, bt = gpu_run(w, nsteps=nsteps, path=path, precision=prec)
+    monkeypatch.setenv("SWE_CART_STREAM", "1")
+    got, dts, t = gpu_run(w, nsteps=nsteps, path=path, precision=prec)
+    assert np.array_equal(dts, bdts) and t == bt
+    for a, b in zip(got, base):
+        assert np.array_equal(a, b)
+    if variant == "default":
+        ref, rdts = oracle_reference(w, nsteps=nsteps, precision=prec)
+        tol = FP64_TOL if prec == "f64" else FP32_TOL
+        errs = field_errors(got, ref, w.g)
+        assert max(errs) <= tol, errs
+        dtol = 1e-12 if prec == "f64" else 1e-5
+        assert np.abs(dts - rdts).max() <= dtol * rdts.max()
+
+
+def test_streaming_across_batches(monkeypatch):
+    """The order alternates with the state buffer a step reads, so a run
+    split into batches of odd lengths equals one batch bit for bit."""
+    import finite_volume_shallow_amd as swe
+    w = inputs.smooth_flow(nx=160, ny=96)
+    say("[streaming] 7 + 6 + 5 steps == 18 steps")
+    monkeypatch.setenv("SWE_CART_STREAM", "0")
+    a, da, _ = gpu_run(w, nsteps=18)
+    monkeypatch.setenv("SWE_CART_STREAM", "1")
+    desc, keep = swe.desc_from_workload(w)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        swe.swe_set_state(ctx, w.z, w.state)
+        for n in (7, 6, 5):
+            swe.swe_step(ctx, n, w.cfl)
+        b = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    del keep
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 # One-layer triangle meshes run the software-pipelined persistent kernel by
 # default; these force the one-workgroup-per-block kernel (and its larger
 # blocks) on them, and the pipelined kernel with a small persistent grid.

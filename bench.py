@@ -291,6 +291,7 @@ def main():
     del keep
     used_path = {swe.SWE_PATH_FUSED: "fused", swe.SWE_PATH_EDGE: "edge",
                  swe.SWE_PATH_RECOMPUTE: "recompute"}[swe.swe_path(ctx)]
+    launch_shape = swe.swe_describe(ctx)
 
     times, one = [], []
     for _ in range(max(1, args.repeats)):
@@ -380,7 +381,8 @@ def main():
                                + (" (classical Roe flux)" if args.scheme == "classical" else "")
                                + (" (Harten-Hyman entropy fix)" if args.entropy_fix else ""), "cells": N,
                    "scheme": args.scheme, "entropy_fix": bool(args.entropy_fix),
-                   "precision": prec, "path": used_path, "simulated_seconds": t_adv},
+                   "precision": prec, "path": used_path, "kernel": launch_shape,
+                   "simulated_seconds": t_adv},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -51,7 +51,8 @@ SWE_NOALLOC_MAX_STEPS = 1024
 
 EXPORTS = ["swe_create_mesh", "swe_set_state", "swe_set_state_device", "swe_step", "swe_step_noalloc",
            "swe_get_state", "swe_get_state_device", "swe_get_dt_history", "swe_destroy",
-           "swe_strerror", "swe_last_error", "swe_nvars", "swe_ncells", "swe_path"]
+           "swe_strerror", "swe_last_error", "swe_nvars", "swe_ncells", "swe_path",
+           "swe_describe"]
 
 
 def _load():
@@ -82,6 +83,8 @@ def _load():
     L.swe_ncells.argtypes = [P]
     L.swe_ncells.restype = ctypes.c_int64
     L.swe_path.argtypes = [P]
+    L.swe_describe.argtypes = [P]
+    L.swe_describe.restype = ctypes.c_char_p
     return L
 
 
@@ -215,6 +218,10 @@ def swe_ncells(ctx):
 
 def swe_path(ctx):
     return _lib.swe_path(ctx)
+
+
+def swe_describe(ctx):
+    return _lib.swe_describe(ctx).decode()
 
 
 # ------------------------------------------------------------------ helpers

@@ -1,5 +1,6 @@
 // C ABI of the shallow-water step library (see include/swe.h).
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
@@ -280,6 +281,8 @@ int swe_nvars(const swe_ctx *c) { return c ? c->nv : -1; }
 int64_t swe_ncells(const swe_ctx *c) { return c ? c->N : -1; }
 int swe_path(const swe_ctx *c) { return c ? c->path : -1; }
 
+const char *swe_describe(const swe_ctx *c) { return c ? c->desc.c_str() : ""; }
+
 int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
 {
     if (!out) return SWE_E_INVAL;
@@ -364,9 +367,12 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             if (st != SWE_OK) throw Fail{st};
             // 512 threads per workgroup.  One layer: blocks of 224 cells,
             // which one round of the threads covers (local cells and edges
-            // <= 512), run by the software-pipelined persistent kernel;
-            // failing that (irregular meshes) 288, 192 or 128 cells with one
-            // workgroup per block.  Two layers (twice the LDS per cell and
+            // <= 512), run by the software-pipelined persistent kernel; where
+            // a block of the mesh does not fit one round, the size shrinks in
+            // steps of 8 cells, down to 192 (the jittered meshes of 1M, 1.28M
+            // and 1.5M triangles fit at 216 cells, where the per-block kernel
+            // at 288 cells ran 35 % slower per cell); failing that (irregular
+            // meshes) 288, 192 or 128 cells with one workgroup per block.  Two layers (twice the LDS per cell and
             // edge): 224 cells with one workgroup per block, else 192 or 128.
             // Blocks keep their LDS within 64 KiB (one layer) or 96 KiB (two
             // layers: 224-cell blocks, 79 KiB on the 1M two-layer mesh,
@@ -412,6 +418,10 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 }
                 if (pipe) {
                     if (lds_ok && need <= c->tb.nt) break;
+                    if (B > 192 && !std::getenv("SWE_TRI_B")) {
+                        B -= 8;
+                        continue;
+                    }
                     pipe = false; // this mesh: one workgroup per block
                     B = 288;
                     continue;
@@ -433,6 +443,14 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 throw Fail{SWE_E_INVAL};
             }
             c->tb.pipe_wgs = pipe ? -1 : 0; // -1: size the persistent grid at the first launch
+            char buf[256];
+            std::snprintf(buf, sizeof buf,
+                          "triangle mesh, %s: %s, blocks of %d cells (%d blocks; local cells <= %d, local edges "
+                          "<= %d), %d threads per workgroup",
+                          c->nv == 6 ? "two layers" : "one layer",
+                          pipe ? "software-pipelined persistent kernel" : "one workgroup per block", B, hb.nblocks,
+                          hb.lc_max, hb.e_max, c->tb.nt);
+            c->desc = buf;
         }
 
         HIPTRY(hipGetDevice(&c->device));
@@ -460,6 +478,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             if (c->prec == SWE_F32) upload_geometry<float>(c, he);
             else upload_geometry<double>(c, he);
             c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
+            c->desc = "edge-list path: an edge pass and a cell pass per step, dt by a separate reduction";
         } else if (d->mesh_kind == SWE_MESH_CART) {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             cart_tiling(d->nx, d->ny, d->bc_y == SWE_BC_PERIODIC, c->cart_ty, c->cart_alt);
@@ -471,6 +490,14 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             // so it stays off there.  SWE_CART_STREAM=0/1 overrides the choice.
             c->cart_stream = (double)c->N * c->rs * (2 * c->nv + 1) > 256.0 * (1 << 20);
             if (const char *e = std::getenv("SWE_CART_STREAM")) c->cart_stream = std::atoi(e) != 0;
+            char buf[256];
+            std::snprintf(buf, sizeof buf,
+                          "structured grid %lld x %lld: one fused launch per step, tiles of 60 columns x %d rows%s%s",
+                          (long long)d->nx, (long long)d->ny, c->cart_ty,
+                          c->cart_alt ? ", odd row blocks marching downward" : "",
+                          c->cart_stream ? ", streaming mode (non-temporal state loads, tile order reversed every "
+                                           "other step)" : "");
+            c->desc = buf;
         } else {
             c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
             if (c->prec == SWE_F32) upload_blocks<float>(c, hb);
@@ -478,6 +505,10 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             c->perm = (int32_t *)dev_alloc(c, c->N * sizeof(int32_t));
             upload_raw(c, c->perm, c->perm_host.data(), c->N * sizeof(int32_t));
         }
+
+        c->desc = std::string(c->classical ? "classical Roe flux" : "IR-Roe flux") +
+                  (c->hh ? " with the Harten-Hyman fix" : "") + (c->prec == SWE_F32 ? ", float32" : ", float64") +
+                  (c->path == SWE_PATH_RECOMPUTE ? ", every cell evaluating all of its edges" : "") + "; " + c->desc;
 
         c->state[0] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);
         c->state[1] = dev_alloc(c, (size_t)c->nv * c->N * c->rs);

@@ -90,6 +90,7 @@ struct swe_ctx {
     hipStream_t stream = nullptr;
     bool own_stream = false;
     std::string err;
+    std::string desc; // what swe_describe returns
     bool has_state = false;
 
     // state: two copies (ping-pong) of nv * N reals each: nv arrays of N

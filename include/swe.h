@@ -245,6 +245,12 @@ int64_t swe_ncells(const swe_ctx *ctx);
  * SWE_PATH_RECOMPUTE); -1 for NULL. */
 int swe_path(const swe_ctx *ctx);
 
+/* What the context runs, as one line of text for logs: the kernel and its
+ * launch shape (structured tiles and march order, triangle block size and
+ * kernel, or the edge-list path).  Owned by the context and valid until
+ * swe_destroy; "" for NULL.  Informational only: its wording may change. */
+const char *swe_describe(const swe_ctx *ctx);
+
 #ifdef __cplusplus
 }
 #endif

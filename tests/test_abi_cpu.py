@@ -182,6 +182,7 @@ def test_null_handles_are_safe():
     assert swe.swe_nvars(None) == -1
     assert swe.swe_ncells(None) == -1
     assert swe.swe_path(None) == -1
+    assert swe.swe_describe(None) == ""
     swe.swe_destroy(None)
     assert swe._lib.swe_step(None, 1, 0.5, None, None) == swe.SWE_E_INVAL
     assert swe._lib.swe_create_mesh(None, None) == swe.SWE_E_INVAL

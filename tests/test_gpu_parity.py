@@ -572,6 +572,44 @@ def test_device_state_roundtrip_triangles():
         assert (h == g).all()
 
 
+def _describe(w, **kw):
+    import finite_volume_shallow_amd as swe
+    desc, keep = swe.desc_from_workload(w, **kw)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        return swe.swe_describe(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+
+
+def test_describe_names_the_kernel():
+    say("[describe] structured, triangles, two layers, edge path")
+    d = _describe(inputs.smooth_flow(nx=160, ny=96))
+    assert d.startswith("IR-Roe flux, float32") and "structured grid 160 x 96" in d, d
+    assert "tiles of 60 columns" in d and "streaming" not in d, d
+    d = _describe(_classical(lambda: inputs.circular_dam_break(nq=36)))
+    assert d.startswith("classical Roe flux, float64"), d
+    assert "one layer: software-pipelined persistent kernel, blocks of 224 cells" in d, d
+    d = _describe(inputs.two_layer_dam_break(nq=30))
+    assert "two layers: one workgroup per block" in d, d
+    d = _describe(inputs.dam_break(), path=PATHS["edge"])
+    assert "edge-list path" in d, d
+
+
+def test_pipelined_kernel_shrinks_its_blocks():
+    """On the jittered 1M-triangle mesh a few blocks of 224 cells have more
+    than 512 local edges; the pipelined kernel is kept, at 216 cells."""
+    w = inputs.circular_dam_break(nq=707)
+    d = _describe(w)
+    say(f"[shrink] {d}")
+    assert "software-pipelined persistent kernel, blocks of 216 cells" in d, d
+    got, dts, _ = gpu_run(w, nsteps=6)
+    ref, rdts = oracle_reference(w, nsteps=6)
+    errs = field_errors(got, ref, w.g)
+    assert max(errs) <= FP64_TOL, errs
+    assert np.abs(dts - rdts).max() <= 1e-12 * rdts.max()
+
+
 def test_error_paths():
     import finite_volume_shallow_amd as swe
     say("[err] depth, non-hyperbolic, bad arguments, zero steps")

@@ -32,6 +32,8 @@ namespace swe {
 
 constexpr int TRI_XCD = 8;
 constexpr int TRI_NPART = 64;
+constexpr int TRI_CTR_STRIDE = 64; // 32-bit words from one block counter to the next: 256 bytes
+static_assert(3 * TRI_NPART + 3 * TRI_XCD * TRI_CTR_STRIDE / 2 <= PART_DOUBLES, "partial minima and block counters");
 
 template <typename T> struct TriArgs {
     const T *in;  // W^n: one record of the NV conserved variables per cell
@@ -46,6 +48,9 @@ template <typename T> struct TriArgs {
     const T *iarea;
     T g, r, cfl;
     double *part;
+    unsigned *ctr; // [3][TRI_XCD] block counters of the pipelined kernel (bank of the launch, per XCD band),
+                   // TRI_CTR_STRIDE words apart
+    int rev;       // the pipelined kernel walks its bands backwards (every other step)
     StepBook book;
     int64_t step;  // index of the step within the batch (dt history)
     int bank0;     // partial-minimum bank of the batch's first step
@@ -239,12 +244,14 @@ template <typename T> __device__ __forceinline__ T &st32(T *base, uint32_t i)
     return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + (uint32_t)(i * (uint32_t)sizeof(T)));
 }
 
-// Per-step bookkeeping by workgroup 0: clear the partial-minimum bank the
-// launch after next will fill, record dt^n and advance the time.
+// Per-step bookkeeping by workgroup 0: clear the partial-minimum bank and
+// the block counters the launch after next will use, record dt^n and
+// advance the time.
 template <typename T> __device__ __forceinline__ void tri_book(const TriArgs<T> &A, int bank, int tid, double dtd)
 {
     if (tid < 64) {
         A.part[((bank + 2) % 3) * TRI_NPART + tid] = __builtin_inf();
+        if (tid < TRI_XCD) A.ctr[(((bank + 2) % 3) * TRI_XCD + tid) * TRI_CTR_STRIDE] = 0u;
         if (tid == 0) {
             A.book.hist[A.step] = dtd;
             A.book.last[0] = dtd;
@@ -643,12 +650,21 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = blockIdx.x;
-    // XCD-aware: the workgroups of XCD w % 8 share its band of consecutive
-    // (Morton-neighbouring) blocks, dealt round-robin
-    const int xcd = w % TRI_XCD, G = (int)gridDim.x / TRI_XCD;
-    const int bend = min((xcd + 1) * A.per_xcd, A.nblocks);
-    int blk = xcd * A.per_xcd + w / TRI_XCD;
     const int bank = (int)((A.step + A.bank0) % 3);
+    // XCD-aware: the G workgroups of XCD w % 8 share its band of consecutive
+    // (Morton-neighbouring) blocks.  Each takes the band positions w / 8 and
+    // w / 8 + G, then further positions from 2 G on, one at a time, from the
+    // band's counter: the resident workgroups of a CU do not progress at the
+    // same rate (on the 2M mesh a CU's first workgroup spent 3.4 us per block,
+    // its third 5.9), and a fixed deal of the band left the slowest finishing
+    // last.  Every other step walks the band backwards, so that it begins with
+    // the blocks its predecessor wrote last.
+    const int xcd = w % TRI_XCD, G = (int)gridDim.x / TRI_XCD;
+    const int bstart = xcd * A.per_xcd;
+    const int nband = min(A.per_xcd, A.nblocks - bstart);
+    unsigned *const ctr = A.ctr + (bank * TRI_XCD + xcd) * TRI_CTR_STRIDE;
+    __shared__ int s_next; // the position after next, published by thread 0
+    int pos = w / TRI_XCD, npos = pos + G;
     const double dpart = A.part[bank * TRI_NPART + lane];
     const T g = A.g, rr = A.r;
     unsigned bad = 0;
@@ -659,17 +675,16 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
     T cst[NV + 1];
 #pragma unroll
     for (int v = 0; v <= NV; ++v) cst[v] = T(1);
-    if (blk < bend) {
-        cb = tri_blk(A, blk);
+    if (pos < nband) {
+        cb = tri_blk(A, A.rev ? bstart + nband - 1 - pos : bstart + pos);
         cp = tri_pre(A, cb, tid);
         asm volatile("" ::"v"(cp.hid));
         tri_state<T, NV>(A, cb, cp, tid, cst);
     }
     const double dtd = wave_min(dpart);
 
-    while (blk < bend) { // uniform over the workgroup
-        const int nblk = blk + G;
-        const bool more = nblk < bend;
+    while (pos < nband) { // uniform over the workgroup
+        const bool more = npos < nband;
         const int LC = cb.B0 + cb.nh, nc = cb.B0 + cb.n1;
 
         // ---- 1. W^n and z into LDS; this thread's edge geometry
@@ -691,7 +706,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         TriBlk nb{};
         TriPre<T> np{};
         if (more) {
-            nb = tri_blk(A, nblk);
+            nb = tri_blk(A, A.rev ? bstart + nband - 1 - npos : bstart + npos);
             np = tri_pre(A, nb, tid);
         }
 
@@ -708,6 +723,13 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
             }
         }
         __syncthreads();
+
+        // the position after next, from the band's counter, by the last wave:
+        // the compiler waits for the returned value right away, and with 224-
+        // cell blocks on 512 threads that wave has no cell or edge in phases
+        // 3 to 5 (its state loads below are placeholders)
+        unsigned taken = 0;
+        if (more && tid == NT - 64) taken = atomicAdd(ctr, 1u);
 
         // next block's cell states (its halo ids have arrived)
         T nst[NV + 1];
@@ -759,13 +781,16 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
             if (!(c[0] > T(0)) || (NL == 2 && !(c[3] > T(0)))) bad |= FLAG_DEPTH;
             if (badv) bad |= FLAG_NONFINITE;
         }
+        if (tid == NT - 64) s_next = more ? 2 * G + (int)taken : nband; // read after the barrier
         __syncthreads(); // the LDS is the next block's
+        const int nnpos = s_next; // rewritten only after the next iteration's first barriers
 
         cb = nb;
         cp = np;
 #pragma unroll
         for (int v = 0; v <= NV; ++v) cst[v] = nst[v];
-        blk = nblk;
+        pos = npos;
+        npos = nnpos;
     }
 
     // dt candidate of everything this workgroup updated: 2 gamma over the
@@ -776,13 +801,15 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
     if (w == 0) tri_book(A, bank, tid, dtd);
 }
 
-// Batch start: elapsed time and error flags to zero; the partial minima
-// too when the batch starts from a fresh state (as k_cart_init).
+// Batch start: elapsed time, error flags and every block counter to zero;
+// the partial minima too when the batch starts from a fresh state (as
+// k_cart_init).
 __global__ void k_tri_init(double *part, StepBook book, int reset_part)
 {
     const int t = threadIdx.x;
     if (reset_part)
         for (int k = t; k < 3 * TRI_NPART; k += blockDim.x) part[k] = __builtin_inf();
+    if (t < 3 * TRI_XCD) reinterpret_cast<unsigned *>(part + 3 * TRI_NPART)[t * TRI_CTR_STRIDE] = 0u;
     if (t == 0) {
         book.t[0] = 0.0;
         book.flags[0] = 0u;
@@ -870,6 +897,8 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     A.r = (T)c->r;
     A.cfl = (T)cfl;
     A.part = c->cart_part;
+    A.ctr = reinterpret_cast<unsigned *>(c->cart_part + 3 * TRI_NPART);
+    A.rev = in; // the step that reads the second state buffer walks backwards
     A.book = c->book;
     A.step = step;
     A.bank0 = c->bank0;

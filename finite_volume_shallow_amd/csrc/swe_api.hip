@@ -205,14 +205,15 @@ void free_all(swe_ctx *c)
 
 // ---- scratch of swe_step_noalloc
 // The per-batch bookkeeping of a batch that swe_step_noalloc runs: three
-// banks of 64 partial dt minima, the 8-double step record (dt slots, time,
-// flags, last dt) and the dt history of up to SWE_NOALLOC_MAX_STEPS steps,
-// in a file-scope device array (about 9.6 KB per GPU, held until the
-// process ends).  Host code never passes `scratch` itself to a kernel or a
-// copy: its name is a host-side stand-in.  The device address comes from
+// banks of 64 partial dt minima and the triangle path's block counters
+// (PART_DOUBLES), the 8-double step record (dt slots, time, flags, last dt)
+// and the dt history of up to SWE_NOALLOC_MAX_STEPS steps, in a file-scope
+// device array (about 15.9 KB per GPU, held until the process ends).  Host
+// code never passes `scratch` itself to a kernel or a copy: its name is a
+// host-side stand-in.  The device address comes from
 // hipGetSymbolAddress, taken once per device (with that device current) and
 // kept in g_scratch_dev.
-constexpr int NA_PART = 3 * 64;
+constexpr int NA_PART = PART_DOUBLES;
 constexpr int NA_BOOK = 8;
 constexpr int NA_DOUBLES = NA_PART + NA_BOOK + SWE_NOALLOC_MAX_STEPS;
 static __device__ __align__(256) double scratch[NA_DOUBLES];
@@ -443,6 +444,10 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                 throw Fail{SWE_E_INVAL};
             }
             c->tb.pipe_wgs = pipe ? -1 : 0; // -1: size the persistent grid at the first launch
+            if (const char *e = std::getenv("SWE_TRI_WGS")) { // tuning override: persistent workgroups
+                const int v = std::atoi(e);
+                if (pipe && v >= 8) c->tb.pipe_wgs = v; // at least one per XCD
+            }
             char buf[256];
             std::snprintf(buf, sizeof buf,
                           "triangle mesh, %s: %s, blocks of %d cells (%d blocks; local cells <= %d, local edges "
@@ -480,7 +485,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             c->e_out = dev_alloc(c, (size_t)(2 * c->nv + 1) * c->E * c->rs);
             c->desc = "edge-list path: an edge pass and a cell pass per step, dt by a separate reduction";
         } else if (d->mesh_kind == SWE_MESH_CART) {
-            c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
+            c->cart_part = (double *)dev_alloc(c, PART_DOUBLES * sizeof(double));
             cart_tiling(d->nx, d->ny, d->bc_y == SWE_BC_PERIODIC, c->cart_ty, c->cart_alt);
             // streaming mode (non-temporal state loads, tile order reversed
             // every other step) where the two state copies and the bed exceed
@@ -499,7 +504,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
                                            "other step)" : "");
             c->desc = buf;
         } else {
-            c->cart_part = (double *)dev_alloc(c, 3 * 64 * sizeof(double));
+            c->cart_part = (double *)dev_alloc(c, PART_DOUBLES * sizeof(double));
             if (c->prec == SWE_F32) upload_blocks<float>(c, hb);
             else upload_blocks<double>(c, hb);
             c->perm = (int32_t *)dev_alloc(c, c->N * sizeof(int32_t));

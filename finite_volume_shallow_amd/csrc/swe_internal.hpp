@@ -11,6 +11,13 @@
 
 namespace swe {
 
+// The fused paths' per-batch device bookkeeping, in doubles: three banks of
+// 64 partial dt minima, then three banks of eight 32-bit block counters (the
+// pipelined triangle kernel's dynamic block schedule, one per XCD band), each
+// counter on a 256-byte line of its own: atomics of all eight bands on one
+// line serialised and made the triangle step 75 % slower.
+constexpr int PART_DOUBLES = 3 * 64 + 3 * 8 * 32;
+
 // Device error flags, OR-ed by the kernels and read once per batch.
 enum : unsigned { FLAG_DEPTH = 1u, FLAG_NONFINITE = 2u, FLAG_NONHYPERBOLIC = 4u };
 
@@ -119,7 +126,8 @@ struct swe_ctx {
     int cart_ty = 64;            // rows per tile
     int cart_alt = 0;            // odd row blocks of tiles march downward
     int cart_stream = 0;         // streaming mode: non-temporal state loads, alternating tile order
-    double *cart_part = nullptr; // [3][64] partial dt minima (both fused paths)
+    double *cart_part = nullptr; // PART_DOUBLES: [3][64] partial dt minima (both fused paths), then the
+                                 // triangle path's [3][8] 32-bit block counters
 
     // fused triangle path: cells in internal (Morton) order
     int32_t *perm = nullptr;          // device: internal index -> caller index

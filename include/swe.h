@@ -189,14 +189,14 @@ int swe_step(swe_ctx *ctx, int32_t nsteps, double cfl, double *t_advanced,
  * any allocation.  Same arguments, results and errors as swe_step (the
  * same kernels, bit for bit, and the context continues exactly as after
  * swe_step: swe_get_dt_history, a following swe_step or swe_step_noalloc).
- * The batch's bookkeeping (partial dt minima, time, error flags, dt history)
- * lives in one static device array per GPU (about 9.6 KB, held until the
- * process ends) instead of buffers of the context, and the call makes no
- * hipMalloc / hipFree or other allocating call.  nsteps must not exceed
- * SWE_NOALLOC_MAX_STEPS (else SWE_E_INVAL, nothing run).  Every call on a
- * GPU shares that GPU's array: calls that overlap in time on one GPU (other
- * threads, or contexts on streams that run concurrently) race and must be
- * serialised by the caller. */
+ * The batch's bookkeeping (partial dt minima, block counters, time, error
+ * flags, dt history) lives in one static device array per GPU (about 15.9
+ * KB, held until the process ends) instead of buffers of the context, and
+ * the call makes no hipMalloc / hipFree or other allocating call.  nsteps
+ * must not exceed SWE_NOALLOC_MAX_STEPS (else SWE_E_INVAL, nothing run).
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (other threads, or contexts on streams that run concurrently) race
+ * and must be serialised by the caller. */
 #define SWE_NOALLOC_MAX_STEPS 1024
 int swe_step_noalloc(swe_ctx *ctx, int32_t nsteps, double cfl, double *t_advanced, double *last_dt);
 

@@ -170,10 +170,16 @@ def test_streaming_across_batches(monkeypatch):
 
 # One-layer triangle meshes run the software-pipelined persistent kernel by
 # default; these force the one-workgroup-per-block kernel (and its larger
-# blocks) on them, and the pipelined kernel with a small persistent grid.
+# blocks) on them, and the pipelined kernel with smaller blocks and small
+# persistent grids: with one or three workgroups per XCD band most blocks
+# of these meshes are taken from the band's counter (positions from twice
+# the workgroups per band on), which the default grid reaches only on
+# meshes of several hundred thousand cells.
 TRI_KERNELS = {"per-block-288": {"SWE_TRI_PIPE": "0", "SWE_TRI_B": "288"},
                "per-block-128": {"SWE_TRI_PIPE": "0", "SWE_TRI_B": "128"},
-               "pipelined-128": {"SWE_TRI_B": "128"}}
+               "pipelined-128": {"SWE_TRI_B": "128"},
+               "pipelined-64-1wg": {"SWE_TRI_B": "64", "SWE_TRI_WGS": "8"},
+               "pipelined-64-3wg": {"SWE_TRI_B": "64", "SWE_TRI_WGS": "24"}}
 
 
 @pytest.mark.parametrize("kernel", list(TRI_KERNELS))
@@ -594,6 +600,35 @@ def test_describe_names_the_kernel():
     assert "two layers: one workgroup per block" in d, d
     d = _describe(inputs.dam_break(), path=PATHS["edge"])
     assert "edge-list path" in d, d
+
+
+def test_pipelined_kernel_mid_size_mesh():
+    """405,000 triangles: 1,809 blocks, so each XCD band has more than twice
+    the default persistent workgroups per band and the later blocks come from
+    the band counters.  Two batches, so the counters are reset between them."""
+    import finite_volume_shallow_amd as swe
+    w = inputs.circular_dam_break(nq=450)
+    say(f"[mid] {_describe(w)}")
+    ref, rdts = oracle_reference(w, nsteps=12)
+    desc, keep = swe.desc_from_workload(w)
+    ctx = swe.swe_create_mesh(desc)
+    try:
+        swe.swe_set_state(ctx, w.z, w.state)
+        swe.swe_step(ctx, 5, w.cfl)
+        d1 = swe.swe_get_dt_history(ctx)
+        swe.swe_step(ctx, 7, w.cfl)
+        d2 = swe.swe_get_dt_history(ctx)
+        got = swe.swe_get_state(ctx)
+    finally:
+        swe.swe_destroy(ctx)
+    del keep
+    errs = field_errors(got, ref, w.g)
+    assert max(errs) <= FP64_TOL, errs
+    dts = np.concatenate([d1, d2])
+    assert np.abs(dts - rdts).max() <= 1e-12 * rdts.max()
+    again, _, _ = gpu_run(w, nsteps=12)
+    for a, b in zip(got, again):
+        assert np.array_equal(a, b)
 
 
 def test_pipelined_kernel_shrinks_its_blocks():

@@ -125,12 +125,18 @@ typedef struct swe_mesh_desc {
  * normal use -- results do not depend on them beyond rounding):
  *   SWE_CART_TY=n, SWE_CART_ALT=0|1  rows per tile (4..4096) and alternating
  *                                    march of the fused Cartesian kernel;
+ *   SWE_CART_STREAM=0|1              its streaming mode (non-temporal state
+ *                                    loads, tile order reversed every other
+ *                                    step), by default on where the two state
+ *                                    copies and the bed exceed 256 MiB;
  *   SWE_TRI_B=n                      cells per triangle block (64..512, a
  *                                    multiple of 32), before the size checks;
  *   SWE_TRI_LDS=bytes                LDS cap per triangle block;
  *   SWE_TRI_NT=256                   256-thread triangle workgroups;
  *   SWE_TRI_PIPE=0|1                 the pipelined persistent triangle kernel
- *                                    (one layer) on or off. */
+ *                                    (one layer) on or off;
+ *   SWE_TRI_WGS=n                    its number of persistent workgroups
+ *                                    (>= 8; by default as many as fit). */
 
 /* Create a context for a mesh and upload its geometry ([IR] Sec. 2.2: cells
  * V_i with area |V_i|, edges G_ij with length |G_ij| and unit normal eta_ij

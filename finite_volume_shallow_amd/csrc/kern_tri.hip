@@ -663,8 +663,9 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
     const int bstart = xcd * A.per_xcd;
     const int nband = min(A.per_xcd, A.nblocks - bstart);
     unsigned *const ctr = A.ctr + (bank * TRI_XCD + xcd) * TRI_CTR_STRIDE;
-    __shared__ int s_next; // the position after next, published by thread 0
+    __shared__ int s_next; // the next position, published in the previous block's phase 5
     int pos = w / TRI_XCD, npos = pos + G;
+    bool first = true;
     const double dpart = A.part[bank * TRI_NPART + lane];
     const T g = A.g, rr = A.r;
     unsigned bad = 0;
@@ -684,7 +685,6 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
     const double dtd = wave_min(dpart);
 
     while (pos < nband) { // uniform over the workgroup
-        const bool more = npos < nband;
         const int LC = cb.B0 + cb.nh, nc = cb.B0 + cb.n1;
 
         // ---- 1. W^n and z into LDS; this thread's edge geometry
@@ -701,6 +701,9 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         const unsigned la = cp.eab & 0xFFFFu, lb = cp.eab >> 16;
         const bool wall = lb == 0xFFFFu;
         __syncthreads();
+        if (!first) npos = s_next; // rewritten only in this block's phase 5
+        first = false;
+        const bool more = npos < nband;
 
         // next block's scalars and mesh data
         TriBlk nb{};
@@ -737,7 +740,10 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         for (int v = 0; v <= NV; ++v) nst[v] = T(1);
         if (more) tri_state<T, NV>(A, nb, np, tid, nst);
 
-        // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order
+        // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order;
+        // the block's own cells go out to HBM from registers right away, so
+        // that phase 5 reads no cell record and the next block may refill
+        // them without another barrier
         if (tid < nc) {
             T acc[NV];
 #pragma unroll
@@ -750,9 +756,23 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
             }
             const T fct = (T)dtd * cp.cia;
             const Cell c(sm, LCM, tid);
+            T nw[NV];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) c.s[v] -= fct * acc[v];
+            for (int v = 0; v < NV; ++v) {
+                nw[v] = c.s[v] - fct * acc[v];
+                c.s[v] = nw[v];
+            }
             tri_cellpre<T, NL, NV>(c);
+            if (tid < cb.B0) {
+                bool badv = false;
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    st32(A.out, (uint32_t)(cb.base + tid) * NV + v) = nw[v];
+                    badv |= !isfinite(nw[v]);
+                }
+                if (!(nw[0] > T(0)) || (NL == 2 && !(nw[3] > T(0)))) bad |= FLAG_DEPTH;
+                if (badv) bad |= FLAG_NONFINITE;
+            }
         }
         __syncthreads();
 
@@ -765,32 +785,22 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         }
         __syncthreads();
 
-        // ---- 5. the block cells' S_i / |V_i| and W^{n+1} out
+        // ---- 5. the block cells' S_i / |V_i|.  No barrier follows: this
+        // phase reads only the speed slots, which the next block writes after
+        // its first barrier, and the next block's phase 1 fills only the cell
+        // records
         if (tid < cb.B0) {
             const T S = fl[(unsigned)cp.csl4 & 0xFFFFu] + fl[(unsigned)(cp.csl4 >> 16) & 0xFFFFu] +
                         fl[(unsigned)(cp.csl4 >> 32) & 0xFFFFu];
             rate = fmax(rate, cp.cia * S);
-            const T *c = sm + tid * Rec::SA;
-            bool badv = false;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const T x = c[v];
-                st32(A.out, (uint32_t)(cb.base + tid) * NV + v) = x;
-                badv |= !isfinite(x);
-            }
-            if (!(c[0] > T(0)) || (NL == 2 && !(c[3] > T(0)))) bad |= FLAG_DEPTH;
-            if (badv) bad |= FLAG_NONFINITE;
         }
-        if (tid == NT - 64) s_next = more ? 2 * G + (int)taken : nband; // read after the barrier
-        __syncthreads(); // the LDS is the next block's
-        const int nnpos = s_next; // rewritten only after the next iteration's first barriers
+        if (tid == NT - 64) s_next = more ? 2 * G + (int)taken : nband; // read after the next first barrier
 
         cb = nb;
         cp = np;
 #pragma unroll
         for (int v = 0; v <= NV; ++v) cst[v] = nst[v];
         pos = npos;
-        npos = nnpos;
     }
 
     // dt candidate of everything this workgroup updated: 2 gamma over the

@@ -373,8 +373,9 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             // steps of 8 cells, down to 192 (the jittered meshes of 1M, 1.28M
             // and 1.5M triangles fit at 216 cells, where the per-block kernel
             // at 288 cells ran 35 % slower per cell); failing that (irregular
-            // meshes) 288, 192 or 128 cells with one workgroup per block.  Two layers (twice the LDS per cell and
-            // edge): 224 cells with one workgroup per block, else 192 or 128.
+            // meshes) 288, 192 or 128 cells with one workgroup per block.
+            // Two layers (twice the LDS per cell and edge): 224 cells with one
+            // workgroup per block, else 192 or 128.
             // Blocks keep their LDS within 64 KiB (one layer) or 96 KiB (two
             // layers: 224-cell blocks, 79 KiB on the 1M two-layer mesh,
             // measured 2-3 % faster there than 192-cell blocks; 256 cells and

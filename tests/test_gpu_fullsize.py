@@ -1,9 +1,10 @@
 """GPU runs at the workloads' full sizes.
 
 * Parity with the oracle, every cell, at full size: configs 1, 2 (fp64, all
-  1000 steps), 2 and 3 in fp32 (100 steps, the fp32 parity point), 4 (all
-  200 steps) and 5 (all 200 steps; the two-layer oracle takes about a
-  second per step there, so it runs in pieces with a progress line each).
+  1000 steps), 2 and 3 in fp32 (100 steps, the fp32 parity point), 3 in
+  fp64 (20 steps), 4 (all 200 steps) and 5 (all 200 steps; the two-layer
+  oracle takes about a second per step there, so it runs in pieces with a
+  progress line each).
 * Full step counts on the GPU with properties that hold at any size: all
   values finite, depths positive, water, pollutant and layer masses
   conserved.
@@ -24,6 +25,9 @@ FULL = {
     "hump-1024-f64": (lambda: inputs.gaussian_hump(), "f64", 1000),
     "hump-1024-f32": (lambda: inputs.gaussian_hump(), "f32", 100),
     "flow-4096-f32": (lambda: inputs.smooth_flow(), "f32", 100),
+    # the float64 instance of the grid's streaming mode at its full size (20
+    # steps: 3.4e8 oracle cell-updates)
+    "flow-4096-f64": (lambda: inputs.smooth_flow(), "f64", 20),
     "tri-2M-f64": (lambda: inputs.circular_dam_break(), "f64", 200),
     "two-layer-1M-f64": (lambda: inputs.two_layer_dam_break(), "f64", 200),
 }

@@ -602,6 +602,31 @@ def test_describe_names_the_kernel():
     assert "edge-list path" in d, d
 
 
+def test_pipelined_schedules_agree_bit_for_bit(monkeypatch):
+    """The same blocks run by one, three or as many persistent workgroups per
+    XCD band as fit (block order and the band counters differ) give the same
+    bits: no block's arithmetic depends on which workgroup runs it, and the
+    dt minimum is exact."""
+    w = inputs.circular_dam_break(nq=60)
+    monkeypatch.setenv("SWE_TRI_B", "64")
+    runs = []
+    for wgs in ("8", "24", None):
+        if wgs is None:
+            monkeypatch.delenv("SWE_TRI_WGS", raising=False)
+        else:
+            monkeypatch.setenv("SWE_TRI_WGS", wgs)
+        say(f"[schedules] {_describe(w)}; workgroups {wgs or 'as many as fit'}")
+        runs.append(gpu_run(w, nsteps=30))
+    (a, da, ta) = runs[0]
+    for b, db, tb in runs[1:]:
+        assert np.array_equal(da, db) and ta == tb
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    ref, rdts = oracle_reference(w, nsteps=30)
+    assert max(field_errors(a, ref, w.g)) <= FP64_TOL
+    assert np.abs(da - rdts).max() <= 1e-12 * rdts.max()
+
+
 def test_pipelined_kernel_mid_size_mesh():
     """405,000 triangles: 1,809 blocks, so each XCD band has more than twice
     the default persistent workgroups per band and the later blocks come from

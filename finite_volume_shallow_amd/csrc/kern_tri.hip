@@ -45,6 +45,7 @@ template <typename T> struct TriArgs {
     const uint32_t *e_ab;
     const T *e_gx, *e_gy; // |G| eta of the local edges
     const uint16_t *slots;
+    const uint32_t *slots32; // the pipelined kernel's 4-byte rows (three 10-bit record indices)
     const T *iarea;
     T g, r, cfl;
     double *part;
@@ -606,7 +607,7 @@ template <typename T> struct TriPre {
     int32_t hid;
     uint32_t eab;
     T gx, gy;
-    uint64_t csl4;
+    uint32_t csl; // three 10-bit fluctuation-record indices
     T cia;
 };
 
@@ -619,7 +620,7 @@ template <typename T> __device__ __forceinline__ TriPre<T> tri_pre(const TriArgs
     p.gx = ld32(A.e_gx, k);
     p.gy = ld32(A.e_gy, k);
     const uint32_t r = (uint32_t)(b.s0 + min(tid, b.B0 + b.n1 - 1));
-    p.csl4 = ld32(reinterpret_cast<const uint64_t *>(A.slots), r);
+    p.csl = ld32(A.slots32, r);
     p.cia = ld32(A.iarea, r);
     return p;
 }
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
             for (int v = 0; v < NV; ++v) acc[v] = T(0);
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
-                const T *f = fl + ((unsigned)(cp.csl4 >> (16 * j)) & 0xFFFFu);
+                const T *f = fl + ER * ((cp.csl >> (10 * j)) & 0x3FFu);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) acc[v] += f[v];
             }
@@ -790,8 +791,8 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         // its first barrier, and the next block's phase 1 fills only the cell
         // records
         if (tid < cb.B0) {
-            const T S = fl[(unsigned)cp.csl4 & 0xFFFFu] + fl[(unsigned)(cp.csl4 >> 16) & 0xFFFFu] +
-                        fl[(unsigned)(cp.csl4 >> 32) & 0xFFFFu];
+            const T S = fl[ER * (cp.csl & 0x3FFu)] + fl[ER * ((cp.csl >> 10) & 0x3FFu)] +
+                        fl[ER * ((cp.csl >> 20) & 0x3FFu)];
             rate = fmax(rate, cp.cia * S);
         }
         if (tid == NT - 64) s_next = more ? 2 * G + (int)taken : nband; // read after the next first barrier
@@ -902,6 +903,7 @@ template <typename T> static TriArgs<T> tri_args(swe_ctx *c, int64_t step, doubl
     A.e_gx = (const T *)c->tb.e_gx;
     A.e_gy = (const T *)c->tb.e_gy;
     A.slots = c->tb.slots;
+    A.slots32 = c->tb.slots32;
     A.iarea = (const T *)c->tb.iarea;
     A.g = (T)c->g;
     A.r = (T)c->r;

@@ -191,6 +191,25 @@ template <typename T> void upload_blocks(swe_ctx *c, const HostBlocks &hb)
             enc[i] = (uint16_t)(((hb.slots[i] & 1u) * (unsigned)hb.e_max + (hb.slots[i] >> 1)) * er);
     c->tb.slots = (uint16_t *)dev_alloc(c, enc.size() * sizeof(uint16_t));
     upload_raw(c, c->tb.slots, enc.data(), enc.size() * sizeof(uint16_t));
+    // the pipelined kernel's rows in 4 bytes: three 10-bit record indices
+    // side e_max + edge (below 1024: its blocks have at most 512 local
+    // edges), which the kernel scales by er itself
+    if (c->tb.pipe_wgs != 0) {
+        const size_t rows = hb.slots.size() / 4;
+        std::vector<uint32_t> enc32(rows, 0u);
+        for (size_t r = 0; r < rows; ++r)
+            for (int j = 0; j < 3; ++j) {
+                const unsigned sl = hb.slots[4 * r + j];
+                const unsigned idx = (sl & 1u) * (unsigned)hb.e_max + (sl >> 1);
+                if (idx >= 1024u) { // excluded by the one-round check
+                    c->err = "triangle block too large for the pipelined kernel's slot rows";
+                    throw Fail{SWE_E_INVAL};
+                }
+                enc32[r] |= idx << (10 * j);
+            }
+        c->tb.slots32 = (uint32_t *)dev_alloc(c, rows * sizeof(uint32_t));
+        upload_raw(c, c->tb.slots32, enc32.data(), rows * sizeof(uint32_t));
+    }
 }
 
 void free_all(swe_ctx *c)

@@ -142,6 +142,7 @@ struct swe_ctx {
         uint32_t *e_ab = nullptr;
         void *e_gx = nullptr, *e_gy = nullptr, *iarea = nullptr;
         uint16_t *slots = nullptr;
+        uint32_t *slots32 = nullptr; // pipelined kernel: three 10-bit record indices per cell
     } tb;
 
     // step bookkeeping

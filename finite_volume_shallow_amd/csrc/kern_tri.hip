@@ -706,13 +706,13 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
         first = false;
         const bool more = npos < nband;
 
-        // next block's scalars and mesh data
-        TriBlk nb{};
-        TriPre<T> np{};
-        if (more) {
-            nb = tri_blk(A, A.rev ? bstart + nband - 1 - npos : bstart + npos);
-            np = tri_pre(A, nb, tid);
-        }
+        // next block's scalars and mesh data.  Issued on every pass (the
+        // current block again once the band is done): with a branch around
+        // them, the compiler's wait counters merged the path without loads
+        // into the flux phase and made it wait for these loads to return
+        const int lpos = more ? npos : pos;
+        const TriBlk nb = tri_blk(A, A.rev ? bstart + nband - 1 - lpos : bstart + lpos);
+        const TriPre<T> np = tri_pre(A, nb, tid);
 
         // ---- 2. every edge touching the block or ring 1, once
         if (tid < cb.ne) {
@@ -737,9 +737,7 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
 
         // next block's cell states (its halo ids have arrived)
         T nst[NV + 1];
-#pragma unroll
-        for (int v = 0; v <= NV; ++v) nst[v] = T(1);
-        if (more) tri_state<T, NV>(A, nb, np, tid, nst);
+        tri_state<T, NV>(A, nb, np, tid, nst);
 
         // ---- 3. W^{n+1} of the block and ring 1, gathered in a fixed order;
         // the block's own cells go out to HBM from registers right away, so

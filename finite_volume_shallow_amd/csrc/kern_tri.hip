@@ -947,8 +947,9 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
                                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
                 if (e != hipSuccess) return e;
             }
+            int per_cu = 0;
             if (c->tb.pipe_wgs < 0) { // as many workgroups as can be resident at once
-                int per_cu = 0, cus = 0;
+                int cus = 0;
                 if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tri_pipe<T, NL, TR, NT, FX>, NT, lds) !=
                         hipSuccess ||
                     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess)
@@ -956,6 +957,9 @@ static hipError_t tri_batch_rd(swe_ctx *c, int32_t nsteps, double cfl)
                 c->tb.pipe_wgs = std::max(1, per_cu) * std::max(1, cus);
             }
             const dim3 pgrid((unsigned)(TRI_XCD * std::max(1, std::min(c->tb.pipe_wgs / TRI_XCD, per_xcd))));
+            if (per_cu > 0) // sized just now: the description names the grid
+                c->desc += ", " + std::to_string(pgrid.x) + " persistent workgroups (" + std::to_string(per_cu) +
+                           " resident per CU)";
             for (int64_t s = 0; s < nsteps; ++s)
                 hipLaunchKernelGGL((k_tri_pipe<T, NL, TR, NT, FX>), pgrid, block, lds, c->stream, tri_args<T>(c, s, cfl));
             return hipGetLastError();

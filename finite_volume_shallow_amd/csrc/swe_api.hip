@@ -406,7 +406,7 @@ int swe_create_mesh(const swe_mesh_desc *d, swe_ctx **out)
             size_t lds_cap = c->nv == 6 ? 98304 : 65536;
             if (const char *e = std::getenv("SWE_TRI_B")) { // tuning overrides
                 const int v = std::atoi(e);
-                if (v >= 64 && v <= 512 && v % 32 == 0) B = v;
+                if (v >= 64 && v <= 512 && v % 8 == 0) B = v;
             }
             if (const char *e = std::getenv("SWE_TRI_LDS")) lds_cap = (size_t)std::atol(e);
             if (const char *e = std::getenv("SWE_TRI_NT"))

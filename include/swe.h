@@ -130,7 +130,7 @@ typedef struct swe_mesh_desc {
  *                                    step), by default on where the two state
  *                                    copies and the bed exceed 256 MiB;
  *   SWE_TRI_B=n                      cells per triangle block (64..512, a
- *                                    multiple of 32), before the size checks;
+ *                                    multiple of 8), before the size checks;
  *   SWE_TRI_LDS=bytes                LDS cap per triangle block;
  *   SWE_TRI_NT=256                   256-thread triangle workgroups;
  *   SWE_TRI_PIPE=0|1                 the pipelined persistent triangle kernel

@@ -102,6 +102,18 @@ template <typename T, int NL, int NV> struct TriCell {
     __device__ __forceinline__ T &ih() const { return s[NV + 2]; } // 1/h, one layer
 };
 
+// One 8-byte LDS read kept as a single instruction.  On gfx950 the paired
+// form the compiler otherwise makes of neighbouring fields (ds_read2_b64, two
+// 8-byte values per lane) takes about 8 cycles per wavefront for consecutive
+// records where a single read takes 2, and 22-30 against 7 for gathered ones:
+// two single reads are about twice as fast.  A volatile read is not paired;
+// it is made through an LDS pointer, since a volatile access through a
+// generic one would stay a flat load.
+template <typename T> __device__ __forceinline__ T lds(const T *p)
+{
+    return *(const volatile __attribute__((address_space(3))) T *)p;
+}
+
 // sqrt(h) and 1/h of a one-layer cell (the two-layer path keeps its LDS for
 // occupancy and forms them per edge)
 template <typename T, int NL, int NV> __device__ __forceinline__ void tri_cellpre(const TriCell<T, NL, NV> &c)
@@ -123,16 +135,16 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
 {
     const T *A = CA.s, *B = CB.s;
     if constexpr (NL == 1) {
-        const T ha = A[0], qxa = A[1], qya = A[2];
-        const T ca = TR ? A[3] : T(0);
+        const T ha = lds(A), qxa = lds(A + 1), qya = lds(A + 2);
+        const T ca = TR ? lds(A + 3) : T(0);
         const T qna = qxa * nx + qya * ny, qta = -qxa * ny + qya * nx;
         Flux1<T, TR> f;
         if (!wall) {
-            const T hb = B[0], qxb = B[1], qyb = B[2];
-            const T cb = TR ? B[3] : T(0);
+            const T hb = lds(B), qxb = lds(B + 1), qyb = lds(B + 2);
+            const T cb = TR ? lds(B + 3) : T(0);
             const T qnb = qxb * nx + qyb * ny, qtb = -qxb * ny + qyb * nx;
-            f = roe1_pre<T, TR, FX>(ha, CA.sq(), CA.ih(), qna, qta, ca, CA.z(), hb, CB.sq(), CB.ih(), qnb, qtb, cb,
-                                CB.z(), g);
+            f = roe1_pre<T, TR, FX>(ha, lds(&CA.sq()), lds(&CA.ih()), qna, qta, ca, lds(&CA.z()), hb, lds(&CB.sq()),
+                                lds(&CB.ih()), qnb, qtb, cb, lds(&CB.z()), g);
         } else {
             f = roe1_wall<T, TR>(ha, qna, qta, ca, g);
         }
@@ -150,8 +162,8 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
         T L[6], Rs[6];
 #pragma unroll
         for (int l2 = 0; l2 < 2; ++l2) {
-            const T qx = A[3 * l2 + 1], qy = A[3 * l2 + 2];
-            L[3 * l2] = A[3 * l2];
+            const T qx = lds(A + 3 * l2 + 1), qy = lds(A + 3 * l2 + 2);
+            L[3 * l2] = lds(A + 3 * l2);
             L[3 * l2 + 1] = qx * nx + qy * ny;
             L[3 * l2 + 2] = -qx * ny + qy * nx;
         }
@@ -159,14 +171,14 @@ __device__ __forceinline__ void tri_edge_flux(const TriCell<T, NL, NV> &CA, cons
         if (!wall) {
 #pragma unroll
             for (int l2 = 0; l2 < 2; ++l2) {
-                const T qx = B[3 * l2 + 1], qy = B[3 * l2 + 2];
-                Rs[3 * l2] = B[3 * l2];
+                const T qx = lds(B + 3 * l2 + 1), qy = lds(B + 3 * l2 + 2);
+                Rs[3 * l2] = lds(B + 3 * l2);
                 Rs[3 * l2 + 1] = qx * nx + qy * ny;
                 Rs[3 * l2 + 2] = -qx * ny + qy * nx;
             }
-            f = roe2_interior<T, flux_classical(FX)>(L, CA.z(), Rs, CB.z(), g, rr);
+            f = roe2_interior<T, flux_classical(FX)>(L, lds(&CA.z()), Rs, lds(&CB.z()), g, rr);
         } else {
-            f = roe2_wall<T>(L, CA.z(), g, rr);
+            f = roe2_wall<T>(L, lds(&CA.z()), g, rr);
         }
         if (f.nonhyp) bad |= FLAG_NONHYPERBOLIC;
 #pragma unroll
@@ -189,12 +201,12 @@ __device__ __forceinline__ T tri_edge_speed(const TriCell<T, NL, NV> &CA, const 
     const T *A = CA.s, *B = CB.s;
     T sp;
     if constexpr (NL == 1) {
-        const T ha = A[0], qna = A[1] * nx + A[2] * ny;
+        const T ha = lds(A), qna = lds(A + 1) * nx + lds(A + 2) * ny;
         if (!wall) {
-            const T hb = B[0], qnb = B[1] * nx + B[2] * ny;
-            const T sa = CA.sq(), sb = CB.sq();
+            const T hb = lds(B), qnb = lds(B + 1) * nx + lds(B + 2) * ny;
+            const T sa = lds(&CA.sq()), sb = lds(&CB.sq());
             // u_Roe = (sa ua + sb ub) / (sa + sb), s u = qn sqrt(h) / h
-            const T ubar = (qna * sa * CA.ih() + qnb * sb * CB.ih()) * FM<T>::rcp(sa + sb);
+            const T ubar = (qna * sa * lds(&CA.ih()) + qnb * sb * lds(&CB.ih())) * FM<T>::rcp(sa + sb);
             sp = fabs(ubar) + FM<T>::sqrt(g * T(0.5) * (ha + hb));
         } else {
             sp = FM<T>::sqrt(g * ha);
@@ -203,8 +215,8 @@ __device__ __forceinline__ T tri_edge_speed(const TriCell<T, NL, NV> &CA, const 
         T L[6], Rs[6];
 #pragma unroll
         for (int l2 = 0; l2 < 2; ++l2) {
-            L[3 * l2] = A[3 * l2];
-            L[3 * l2 + 1] = A[3 * l2 + 1] * nx + A[3 * l2 + 2] * ny;
+            L[3 * l2] = lds(A + 3 * l2);
+            L[3 * l2 + 1] = lds(A + 3 * l2 + 1) * nx + lds(A + 3 * l2 + 2) * ny;
             L[3 * l2 + 2] = T(0);
         }
         T pa[4], pb[4];
@@ -212,8 +224,8 @@ __device__ __forceinline__ T tri_edge_speed(const TriCell<T, NL, NV> &CA, const 
         if (!wall) {
 #pragma unroll
             for (int l2 = 0; l2 < 2; ++l2) {
-                Rs[3 * l2] = B[3 * l2];
-                Rs[3 * l2 + 1] = B[3 * l2 + 1] * nx + B[3 * l2 + 2] * ny;
+                Rs[3 * l2] = lds(B + 3 * l2);
+                Rs[3 * l2 + 1] = lds(B + 3 * l2 + 1) * nx + lds(B + 3 * l2 + 2) * ny;
                 Rs[3 * l2 + 2] = T(0);
             }
             roe2_cellpre(Rs, pb);
@@ -445,7 +457,7 @@ k_tri_fused(TriArgs<T> A)
                 const T fct = (T)dtd * cia[m];
                 const Cell c(sm, LCM, l);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) nw[m][v] = c.s[v] - fct * acc[v];
+                for (int v = 0; v < NV; ++v) nw[m][v] = lds(c.s + v) - fct * acc[v];
             }
         }
         __syncthreads();
@@ -495,7 +507,7 @@ k_tri_fused(TriArgs<T> A)
                 for (int j = 0; j < 3; ++j) {
                     const T *f = fl + ((unsigned)(csl4[m] >> (16 * j)) & 0xFFFFu);
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) acc[v] += f[v];
+                    for (int v = 0; v < NV; ++v) acc[v] += lds(f + v);
                 }
                 const T fct = (T)dtd * cia[m];
                 const Cell c(sm, LCM, l);
@@ -751,14 +763,14 @@ __global__ __launch_bounds__(NT) void k_tri_pipe(TriArgs<T> A)
             for (int j = 0; j < 3; ++j) {
                 const T *f = fl + ER * ((cp.csl >> (10 * j)) & 0x3FFu);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) acc[v] += f[v];
+                for (int v = 0; v < NV; ++v) acc[v] += lds(f + v);
             }
             const T fct = (T)dtd * cp.cia;
             const Cell c(sm, LCM, tid);
             T nw[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                nw[v] = c.s[v] - fct * acc[v];
+                nw[v] = lds(c.s + v) - fct * acc[v];
                 c.s[v] = nw[v];
             }
             tri_cellpre<T, NL, NV>(c);

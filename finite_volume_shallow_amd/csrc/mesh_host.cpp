@@ -210,6 +210,126 @@ void morton_perm(int64_t nnodes, const double *xy, int64_t ncells, const int32_t
 // Blocks of the fused triangle path
 // ---------------------------------------------------------------------------
 
+// LDS banks (gfx950, measured): an 8-byte LDS read by a wavefront is served
+// in two halves of 32 lanes, and a half takes as many cycles as the largest
+// number of distinct addresses sharing one 8-byte bank slot, (address / 8)
+// mod 32.  The kernels gather cell records of 7 reals by the cell's local id
+// and fluctuation records of an odd number of reals by the record index, so
+// two gathers share a slot exactly when their indices agree mod 32.  Two
+// greedy passes spread them: the local edges are placed 32 at a time (the
+// lanes of one half) so that the cells on each side of a half's edges differ
+// mod 32 unless they are the same cell (one address, read once), and each
+// updated cell's three slots are permuted within its half of cells so that
+// each of the three gathers meets few shared slots.  Neither pass changes
+// what is computed; the slot order only fixes the order of a cell's
+// three-term sums.
+struct BankSet {
+    int32_t cell[32];
+    void clear() { std::fill(cell, cell + 32, -1); }
+    bool free_for(int32_t c) const { return c < 0 || cell[c & 31] < 0 || cell[c & 31] == c; }
+    void put(int32_t c)
+    {
+        if (c >= 0 && cell[c & 31] < 0) cell[c & 31] = c;
+    }
+};
+
+// Take n edges of rem into out for the current half (ua, ub: the cells on
+// either side already in it): those that meet no shared slot, in order, then
+// the leftovers that meet the fewest (among the first 64).
+static void bank_take(std::vector<int32_t> &rem, int n, BankSet &ua, BankSet &ub, const std::vector<int32_t> &la,
+                      const std::vector<int32_t> &lb, std::vector<int32_t> &out, std::vector<int32_t> &rest)
+{
+    rest.clear();
+    int got = 0;
+    for (int32_t k : rem) {
+        if (got < n && ua.free_for(la[k]) && ub.free_for(lb[k])) {
+            out.push_back(k);
+            ua.put(la[k]);
+            ub.put(lb[k]);
+            ++got;
+        } else {
+            rest.push_back(k);
+        }
+    }
+    while (got < n && !rest.empty()) {
+        size_t best = 0;
+        int bp = 3;
+        for (size_t i = 0; i < rest.size() && i < 64; ++i) {
+            const int p = !ua.free_for(la[rest[i]]) + !ub.free_for(lb[rest[i]]);
+            if (p < bp) {
+                bp = p;
+                best = i;
+            }
+        }
+        const int32_t k = rest[best];
+        out.push_back(k);
+        ua.put(la[k]);
+        ub.put(lb[k]);
+        rest.erase(rest.begin() + (ptrdiff_t)best);
+        ++got;
+    }
+    rem.swap(rest);
+}
+
+// New order of a block's local edges (positions 0..ne-1 index la, lb: the
+// local cells on either side, -1 for a wall); the first es0 stay first.
+static void bank_order_edges(int es0, const std::vector<int32_t> &la, const std::vector<int32_t> &lb,
+                             std::vector<int32_t> &order)
+{
+    const int ne = (int)la.size();
+    std::vector<int32_t> ra, rb, rest;
+    for (int k = 0; k < es0; ++k) ra.push_back(k);
+    for (int k = es0; k < ne; ++k) rb.push_back(k);
+    order.clear();
+    BankSet ua, ub;
+    while ((int)order.size() < ne) {
+        ua.clear();
+        ub.clear();
+        int space = 32;
+        const int na = std::min(space, (int)ra.size());
+        bank_take(ra, na, ua, ub, la, lb, order, rest);
+        space -= na;
+        if (ra.empty() && space > 0) bank_take(rb, std::min(space, (int)rb.size()), ua, ub, la, lb, order, rest);
+    }
+}
+
+// Permute each updated cell's three slots within its half of 32 cells.
+static void bank_order_slots(HostBlocks &out)
+{
+    static const int P[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 0, 2}, {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
+    std::vector<int32_t> used[3][32];
+    for (int b = 0; b < out.nblocks; ++b) {
+        const int s0 = out.slot_off[b], nc = out.slot_off[b + 1] - s0;
+        for (int h0 = 0; h0 < nc; h0 += 32) {
+            for (auto &u : used)
+                for (auto &v : u) v.clear();
+            for (int l = h0; l < std::min(nc, h0 + 32); ++l) {
+                uint16_t *sl = &out.slots[4 * (size_t)(s0 + l)];
+                int32_t r[3];
+                for (int j = 0; j < 3; ++j) r[j] = (int32_t)((sl[j] & 1u) * (unsigned)out.e_max + (sl[j] >> 1));
+                int best = 0, bp = 1 << 30;
+                for (int q = 0; q < 6; ++q) {
+                    int pen = 0;
+                    for (int j = 0; j < 3; ++j) {
+                        const std::vector<int32_t> &u = used[j][r[P[q][j]] & 31];
+                        if (std::find(u.begin(), u.end(), r[P[q][j]]) == u.end()) pen += (int)u.size();
+                    }
+                    if (pen < bp) {
+                        bp = pen;
+                        best = q;
+                    }
+                }
+                const uint16_t old[3] = {sl[0], sl[1], sl[2]};
+                for (int j = 0; j < 3; ++j) {
+                    sl[j] = old[P[best][j]];
+                    std::vector<int32_t> &u = used[j][r[P[best][j]] & 31];
+                    if (std::find(u.begin(), u.end(), r[P[best][j]]) == u.end()) u.push_back(r[P[best][j]]);
+                }
+            }
+        }
+    }
+}
+
 int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std::string &err)
 {
     out = HostBlocks();
@@ -274,6 +394,18 @@ int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std
             err = "triangle block too large for 16-bit local indices";
             return SWE_E_INVAL;
         }
+        {
+            std::vector<int32_t> la(ne), lb(ne), order, tmp(ledges);
+            for (int k = 0; k < ne; ++k) {
+                la[k] = cloc[he.a[ledges[k]]];
+                lb[k] = he.b[ledges[k]] >= 0 ? cloc[he.b[ledges[k]]] : -1;
+            }
+            bank_order_edges(es0, la, lb, order);
+            for (int k = 0; k < ne; ++k) {
+                ledges[k] = tmp[order[k]];
+                eloc[ledges[k]] = k;
+            }
+        }
         for (int32_t e : ledges) {
             const uint32_t la = (uint32_t)cloc[he.a[e]];
             const uint32_t lb = he.b[e] >= 0 ? (uint32_t)cloc[he.b[e]] : 0xFFFFu;
@@ -306,6 +438,7 @@ int build_tri_blocks(const HostEdges &he, int64_t N, int B, HostBlocks &out, std
         out.lc_max = std::max(out.lc_max, lc);
         out.e_max = std::max(out.e_max, ne);
     }
+    bank_order_slots(out); // needs the final e_max (a record's index is side e_max + edge)
     return SWE_OK;
 }
 

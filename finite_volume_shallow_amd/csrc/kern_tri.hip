@@ -79,10 +79,11 @@ __device__ __forceinline__ T roe2_speed(const T *L, const T *pL, const T *R, con
     return fmax(fabs(hi + m), fabs(lo + m));
 }
 
-// LDS records.  LDS has 32 four-byte banks: a wave whose lanes read
-// consecutive records of an odd number of 8-byte reals touches every bank
-// once, so every record stride here is odd (in reals) and field offsets are
-// constants (neighbouring fields load and store as one instruction).
+// LDS records.  A wavefront's 8-byte LDS read is served in two halves of
+// 32 lanes, each taking as many cycles as the largest number of distinct
+// addresses in one 8-byte bank slot ((address / 8) mod 32): lanes reading
+// consecutive records of an odd number of 8-byte reals meet no conflict, so
+// every record stride here is odd (in reals); field offsets are constants.
 //   cell: the NV conserved variables, z and (one layer) sqrt(h) and 1/h in
 //   one record of SA reals, so that an edge's gather of a cell takes the
 //   fewest LDS instructions;

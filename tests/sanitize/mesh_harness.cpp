@@ -59,6 +59,10 @@ static int check_blocks(const swe::HostBlocks &hb, int64_t ncells)
         for (int k = 0; k < ne; ++k) {
             const uint32_t ab = hb.e_ab[e0 + k], la = ab & 0xFFFFu, lb = ab >> 16;
             CHECK((int)la < lc && (lb == 0xFFFFu || (int)lb < lc), "block %d edge %d cells %u %u", b, k, la, lb);
+            // the edges touching the block come first (the kernels' speed phase takes those)
+            const bool touches = (int)la < B0 || (lb != 0xFFFFu && (int)lb < B0);
+            CHECK(touches == (k < hb.e_s0[b]), "block %d edge %d of %d touches the block: %d", b, k, hb.e_s0[b],
+                  (int)touches);
         }
         const int s0 = hb.slot_off[b], nc = hb.slot_off[b + 1] - s0;
         CHECK(nc == B0 + n1, "block %d updated cells", b);
@@ -72,6 +76,8 @@ static int check_blocks(const swe::HostBlocks &hb, int64_t ncells)
                 const uint32_t mine = side ? (ab >> 16) : (ab & 0xFFFFu);
                 CHECK((int)mine == l, "block %d cell %d slot %d names cell %u", b, l, j, mine);
             }
+            const uint16_t *sl = &hb.slots[4 * (size_t)(s0 + l)];
+            CHECK(sl[0] != sl[1] && sl[0] != sl[2] && sl[1] != sl[2], "block %d cell %d repeats a slot", b, l);
         }
     }
     return 0;
